@@ -1,0 +1,305 @@
+"""CPU oracle for the per-rank ZeRO sharded-optimizer step.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  It never imports the
+HIP library and the HIP library never imports it.
+
+The arithmetic lives in ``zero_oracle.c`` (plain scalar C, single thread);
+this module only marshals numpy arrays into it and strings the primitives
+together in the order the pages describe one optimizer step:
+
+  * each rank owns one of N equal parts of the flat parameter space
+    ("ZeRO技术解析：大模型分布式训练的革命性突破" §2.1, §4.1);
+  * gradients are reduce-scattered, so a rank sums the replicas' values of
+    its own slice only (same page §2.1; "ZeRO 和分片优化器", technical
+    insight);
+  * fp16 loss scaling with a dynamic scaler, or bf16 (first page §3.3, §5.1);
+  * global-norm clipping at 1.0 (first page §6 configuration);
+  * AdamW with lr 6e-5 and weight decay 0.01 (first page §3.1) on fp32
+    master weights and moments ("ZeRO 和分片优化器" FAQ);
+  * the updated part is all-gathered in the working precision (first page
+    §2.1 and the §1.2.1 configuration).
+
+Parity of the loss-scaler rule is unpinned by the pages (they give only the
+knobs); every other function is pinned by the CPU tests.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+from dataclasses import dataclass, field
+
+import numpy as np
+
+FP16 = 1
+BF16 = 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "zero_oracle.c")
+# ZERO_ORACLE_LIB lets the mutation test load a deliberately broken copy.
+_LIB_PATH = os.environ.get("ZERO_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def compile_oracle(src: str, out: str, strict: bool = True) -> None:
+    """gcc -O2 with no contraction and no fast-math: every fp operation in
+    the source is one IEEE-754 operation in the order written."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math",
+           "-fexcess-precision=standard", "-fPIC", "-shared", "-Wall"]
+    cmd += ["-Werror"] if strict else ["-w"]
+    cmd += ["-I", _HERE, src, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle library in place (always, when force is set)."""
+    if force or not os.path.exists(_LIB_PATH):
+        compile_oracle(_SRC, _LIB_PATH)
+    return _LIB_PATH
+
+
+class _Scaler(ctypes.Structure):
+    _fields_ = [("scale", ctypes.c_double), ("good", ctypes.c_int32),
+                ("hyst", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("hysteresis", ctypes.c_int32), ("min_scale", ctypes.c_double)]
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        L = ctypes.CDLL(_LIB_PATH)
+        i64, i32, f32, f64 = (ctypes.c_int64, ctypes.c_int32, ctypes.c_float,
+                              ctypes.c_double)
+        vp = ctypes.c_void_p
+        L.oracle_partition.argtypes = [i64, i32, i32, vp, vp, vp]
+        L.oracle_partition.restype = ctypes.c_int
+        L.oracle_bucket_plan.argtypes = [vp, i32, i64, vp, vp]
+        L.oracle_bucket_plan.restype = i32
+        L.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
+        L.oracle_f16_to_f32.restype = f32
+        L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_to_f32.restype = f32
+        L.oracle_f32_to_f16.argtypes = [f32]
+        L.oracle_f32_to_f16.restype = ctypes.c_uint16
+        L.oracle_f32_to_bf16.argtypes = [f32]
+        L.oracle_f32_to_bf16.restype = ctypes.c_uint16
+        for name in ("oracle_f32_to_f16_array", "oracle_f32_to_bf16_array",
+                     "oracle_f16_to_f32_array", "oracle_bf16_to_f32_array"):
+            getattr(L, name).argtypes = [i64, vp, vp]
+            getattr(L, name).restype = None
+        L.oracle_reduce.argtypes = [i32, vp, i32, i64, f32, vp, vp, vp]
+        L.oracle_reduce.restype = None
+        L.oracle_clip.argtypes = [f64, f64, vp, vp]
+        L.oracle_clip.restype = i32
+        L.oracle_adamw.argtypes = [i64, vp, vp, vp, vp, f64, f64, f64, f64,
+                                   f64, f64, i64]
+        L.oracle_adamw.restype = None
+        L.oracle_scaler_init.argtypes = [ctypes.POINTER(_Scaler), i32, i32,
+                                         i32, f64]
+        L.oracle_scaler_init.restype = None
+        L.oracle_scaler_update.argtypes = [ctypes.POINTER(_Scaler), i32]
+        L.oracle_scaler_update.restype = i32
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be contiguous"
+    return a.ctypes.data
+
+
+# ---------------------------------------------------------------- partition
+def partition(numel: int, world_size: int, alignment: int):
+    """Return (shard_numel, padded_numel, valid_per_rank) or raise."""
+    s = ctypes.c_int64()
+    padded = ctypes.c_int64()
+    valid = np.zeros(max(world_size, 1), dtype=np.int64)
+    rc = lib().oracle_partition(numel, world_size, alignment,
+                                ctypes.addressof(s), ctypes.addressof(padded),
+                                _ptr(valid))
+    if rc != 0:
+        raise ValueError("invalid partition arguments")
+    return s.value, padded.value, [int(x) for x in valid[:world_size]]
+
+
+def bucket_plan(sizes, bucket_size: int):
+    """Return (offsets, bucket_of, n_buckets) for tensors laid end to end."""
+    n = np.ascontiguousarray(np.asarray(sizes, dtype=np.int64))
+    off = np.zeros(max(len(n), 1), dtype=np.int64)
+    bof = np.zeros(max(len(n), 1), dtype=np.int32)
+    nb = lib().oracle_bucket_plan(_ptr(n) if len(n) else None, len(n),
+                                  bucket_size, _ptr(off), _ptr(bof))
+    if nb < 0:
+        raise ValueError("invalid bucket arguments")
+    return off[:len(n)].copy(), bof[:len(n)].copy(), nb
+
+
+# ------------------------------------------------------------ number formats
+def f32_to_f16(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().oracle_f32_to_f16_array(x.size, _ptr(x), _ptr(out))
+    return out
+
+
+def f32_to_bf16(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().oracle_f32_to_bf16_array(x.size, _ptr(x), _ptr(out))
+    return out
+
+
+def f16_to_f32(h: np.ndarray) -> np.ndarray:
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.shape, dtype=np.float32)
+    lib().oracle_f16_to_f32_array(h.size, _ptr(h), _ptr(out))
+    return out
+
+
+def bf16_to_f32(b: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    out = np.empty(b.shape, dtype=np.float32)
+    lib().oracle_bf16_to_f32_array(b.size, _ptr(b), _ptr(out))
+    return out
+
+
+def cast(p: np.ndarray, dtype: int) -> np.ndarray:
+    return f32_to_f16(p) if dtype == FP16 else f32_to_bf16(p)
+
+
+# ------------------------------------------------------------------ reduce
+def inv_scale(loss_scale: float, predivide: float = 1.0) -> np.float32:
+    """fp32 of 1 / (loss_scale * predivide), the unscale multiplier."""
+    return np.float32(1.0 / (float(loss_scale) * float(predivide)))
+
+
+def reduce(replicas, dtype: int, inv: float, sumsq: float = 0.0,
+           overflow: int = 0):
+    """Sum the replicas' slices; return (g, sumsq, overflow) accumulated."""
+    reps = [np.ascontiguousarray(r, dtype=np.uint16) for r in replicas]
+    n = reps[0].size
+    assert all(r.size == n for r in reps)
+    arr = (ctypes.c_void_p * len(reps))(*[_ptr(r) for r in reps])
+    g = np.empty(n, dtype=np.float32)
+    ss = ctypes.c_double(sumsq)
+    of = ctypes.c_int32(overflow)
+    lib().oracle_reduce(len(reps), ctypes.addressof(arr), dtype, n,
+                        np.float32(inv), _ptr(g), ctypes.addressof(ss),
+                        ctypes.addressof(of))
+    return g, ss.value, of.value
+
+
+def clip(sumsq: float, max_norm: float):
+    """Return (applies, norm, coef)."""
+    norm = ctypes.c_double()
+    coef = ctypes.c_double()
+    applies = lib().oracle_clip(sumsq, max_norm, ctypes.addressof(norm),
+                                ctypes.addressof(coef))
+    return bool(applies), norm.value, coef.value
+
+
+def adamw(g, p, m, v, coef, lr, beta1, beta2, eps, weight_decay, t):
+    """Update fp32 arrays p, m, v in place."""
+    for a in (g, p, m, v):
+        assert a.dtype == np.float32 and a.flags["C_CONTIGUOUS"]
+    n = g.size
+    assert p.size == n and m.size == n and v.size == n
+    lib().oracle_adamw(n, _ptr(g), _ptr(p), _ptr(m), _ptr(v), float(coef),
+                       float(lr), float(beta1), float(beta2), float(eps),
+                       float(weight_decay), int(t))
+
+
+# ------------------------------------------------------------------ scaler
+class LossScaler:
+    """Dynamic loss scaler (reading; parity unpinned by the pages)."""
+
+    def __init__(self, initial_scale_power=16, window=100, hysteresis=2,
+                 min_scale=1.0):
+        self._s = _Scaler()
+        lib().oracle_scaler_init(ctypes.byref(self._s), initial_scale_power,
+                                 window, hysteresis, min_scale)
+
+    @property
+    def scale(self) -> float:
+        return self._s.scale
+
+    @property
+    def good(self) -> int:
+        return self._s.good
+
+    @property
+    def hyst(self) -> int:
+        return self._s.hyst
+
+    def update(self, overflow: bool) -> bool:
+        """Record one step's overflow flag; return True when it is skipped."""
+        return bool(lib().oracle_scaler_update(ctypes.byref(self._s),
+                                               1 if overflow else 0))
+
+
+# ---------------------------------------------------------- one full step
+@dataclass
+class Hyper:
+    lr: float = 6e-5
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+    weight_decay: float = 0.01
+    max_grad_norm: float = 1.0
+    loss_scale: float = 1.0
+    predivide: float = 1.0
+
+
+@dataclass
+class StepInfo:
+    sumsq: float
+    norm: float
+    coef: float
+    clipped: bool
+    overflow: bool
+    skipped: bool
+    grads: list = field(default_factory=list)   # reduced fp32 grad per rank
+
+
+def step(replica_flats, dtype: int, numel: int, world_size: int,
+         alignment: int, masters, exp_avgs, exp_avg_sqs, full_params,
+         hp: Hyper, t: int, keep_grads: bool = False) -> StepInfo:
+    """One sharded step for every rank of the world, in rank order.
+
+    replica_flats: N flat uint16 gradient buffers (one per data-parallel
+        replica), each at least `numel` long (padding beyond is ignored).
+    masters, exp_avgs, exp_avg_sqs: world_size fp32 arrays of shard length,
+        updated in place (their padding tail is never touched).
+    full_params: uint16 array of the padded full length; each rank's real
+        elements are overwritten with its cast masters.
+    A step whose reduced gradient holds inf or nan anywhere is skipped: no
+    state changes, and the caller must not advance t.
+    """
+    s, padded, valid = partition(numel, world_size, alignment)
+    inv = inv_scale(hp.loss_scale, hp.predivide)
+    sumsq, overflow = 0.0, 0
+    grads = []
+    for r in range(world_size):
+        lo, n = r * s, valid[r]
+        g, sumsq, overflow = reduce([f[lo:lo + n] for f in replica_flats],
+                                    dtype, inv, sumsq, overflow)
+        grads.append(g)
+    overflow = overflow or not math.isfinite(sumsq)
+    applies, norm, coef = clip(sumsq, hp.max_grad_norm)
+    info = StepInfo(sumsq, norm, coef, applies, bool(overflow),
+                    bool(overflow), grads if keep_grads else [])
+    if overflow:
+        return info
+    for r in range(world_size):
+        lo, n = r * s, valid[r]
+        p, m, v = masters[r][:n], exp_avgs[r][:n], exp_avg_sqs[r][:n]
+        adamw(grads[r], p, m, v, coef, hp.lr, hp.beta1, hp.beta2, hp.eps,
+              hp.weight_decay, t)
+        full_params[lo:lo + n] = cast(p, dtype)
+    return info

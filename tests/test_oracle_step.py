@@ -1,0 +1,309 @@
+"""Pins for the oracle's reduce, clip, AdamW, scaler and full step (CPU only).
+
+Each arithmetic piece is pinned to something other than itself: special
+cases with exact answers (one replica, N equal replicas, constant
+gradients, the first Adam step), library routines on the CPU
+(torch.optim.AdamW and torch.nn.utils.clip_grad_norm_ in float64,
+numpy sums), and the invariants the pages fix: a rank updates only its own
+part, and the concatenated parts equal the unsharded step.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+
+def f32_bits_to_code(x, dtype):
+    return oracle.f32_to_f16(x) if dtype == oracle.FP16 else oracle.f32_to_bf16(x)
+
+
+def decode(c, dtype):
+    return oracle.f16_to_f32(c) if dtype == oracle.FP16 else oracle.bf16_to_f32(c)
+
+
+def rand_codes(rng, n, dtype, sigma=1.0):
+    return f32_bits_to_code((rng.standard_normal(n) * sigma).astype(np.float32), dtype)
+
+
+# ------------------------------------------------------------------ reduce
+@pytest.mark.parametrize("dtype", [oracle.FP16, oracle.BF16])
+def test_reduce_one_replica_is_identity(dtype):
+    rng = np.random.default_rng(0)
+    x = rand_codes(rng, 4097, dtype)
+    for scale in (1.0, 2.0**16, 2.0**-3):
+        g, ss, of = oracle.reduce([x], dtype, oracle.inv_scale(scale))
+        ref = decode(x, dtype).astype(np.float64) / scale
+        assert np.array_equal(g.astype(np.float64), ref)
+        assert of == 0
+        assert ss == pytest.approx(float(np.sum(ref * ref)), rel=1e-13)
+
+
+@pytest.mark.parametrize("dtype", [oracle.FP16, oracle.BF16])
+@pytest.mark.parametrize("N", [2, 4, 8])
+def test_reduce_equal_replicas_is_exact_multiple(dtype, N):
+    rng = np.random.default_rng(N)
+    x = rand_codes(rng, 1000, dtype)
+    g, _, of = oracle.reduce([x] * N, dtype, oracle.inv_scale(1.0))
+    assert np.array_equal(g, decode(x, dtype) * np.float32(N))
+    assert of == 0
+
+
+@pytest.mark.parametrize("dtype", [oracle.FP16, oracle.BF16])
+def test_reduce_matches_numpy_fp32_running_sum(dtype):
+    rng = np.random.default_rng(11)
+    N, n = 7, 3001
+    reps = [rand_codes(rng, n, dtype, sigma=10.0 ** rng.uniform(-3, 3)) for _ in range(N)]
+    acc = decode(reps[0], dtype).copy()
+    for r in reps[1:]:
+        acc = np.add(acc, decode(r, dtype), dtype=np.float32)
+    inv = oracle.inv_scale(8.0)
+    g, ss, of = oracle.reduce(reps, dtype, inv)
+    assert np.array_equal(g, np.multiply(acc, inv, dtype=np.float32))
+    assert of == 0
+    exact = math.fsum(float(v) * float(v) for v in g)
+    assert ss == pytest.approx(exact, rel=1e-12)
+
+
+def test_reduce_sum_of_squares_accumulates_across_calls():
+    rng = np.random.default_rng(2)
+    a = rand_codes(rng, 500, oracle.BF16)
+    b = rand_codes(rng, 700, oracle.BF16)
+    inv = oracle.inv_scale(1.0)
+    _, s1, _ = oracle.reduce([a], oracle.BF16, inv)
+    _, s2, _ = oracle.reduce([b], oracle.BF16, inv, s1, 0)
+    _, s12, _ = oracle.reduce([np.concatenate([a, b])], oracle.BF16, inv)
+    assert s2 == s12
+
+
+@pytest.mark.parametrize("dtype", [oracle.FP16, oracle.BF16])
+@pytest.mark.parametrize("poison", [np.inf, -np.inf, np.nan])
+def test_reduce_flags_any_nonfinite(dtype, poison):
+    rng = np.random.default_rng(5)
+    reps = [rand_codes(rng, 300, dtype) for _ in range(4)]
+    for r in range(4):
+        for i in (0, 150, 299):
+            bad = [x.copy() for x in reps]
+            bad[r][i] = f32_bits_to_code(np.array([poison], np.float32), dtype)[0]
+            g, _, of = oracle.reduce(bad, dtype, oracle.inv_scale(2.0**16))
+            assert of == 1 and not np.isfinite(g[i])
+            assert np.isfinite(np.delete(g, i)).all()
+
+
+def test_reduce_flags_fp32_overflow_of_the_sum():
+    big = oracle.f32_to_bf16(np.array([3.0e38], np.float32))
+    g, _, of = oracle.reduce([big, big], oracle.BF16, oracle.inv_scale(1.0))
+    assert of == 1 and np.isinf(g[0])
+    g, _, of = oracle.reduce([big], oracle.BF16, oracle.inv_scale(1.0))
+    assert of == 0
+
+
+# -------------------------------------------------------------------- clip
+def test_clip_constant_gradient_closed_form():
+    for n, c in ((100, 0.5), (10_000, 1e-3), (1, 3.0)):
+        g = np.full(n, c, np.float32)
+        _, ss, _ = oracle.reduce([oracle.f32_to_bf16(g)], oracle.BF16, 1.0)
+        cval = float(oracle.bf16_to_f32(oracle.f32_to_bf16(np.float32([c])))[0])
+        applies, norm, coef = oracle.clip(ss, 1.0)
+        assert norm == pytest.approx(abs(cval) * math.sqrt(n), rel=1e-15)
+        assert applies == (norm + 1e-6 > 1.0)
+        assert coef == (1.0 / (norm + 1e-6) if applies else 1.0)
+
+
+def test_clip_matches_torch_clip_grad_norm():
+    rng = np.random.default_rng(9)
+    for sigma in (1e-4, 1e-2, 1.0):
+        g = (rng.standard_normal(5000) * sigma).astype(np.float32)
+        t = torch.nn.Parameter(torch.zeros(5000, dtype=torch.float64))
+        t.grad = torch.from_numpy(g.astype(np.float64))
+        total = torch.nn.utils.clip_grad_norm_([t], 1.0)
+        ss = float(np.sum(g.astype(np.float64) ** 2))
+        applies, norm, coef = oracle.clip(ss, 1.0)
+        assert norm == pytest.approx(float(total), rel=1e-12)
+        assert np.allclose(g.astype(np.float64) * coef, t.grad.numpy(), rtol=1e-14, atol=0)
+    assert oracle.clip(4.0, 0.0) == (False, 2.0, 1.0)      # max_norm <= 0: off
+    assert oracle.clip(4.0, -1.0)[0] is False
+
+
+# ------------------------------------------------------------------- AdamW
+def test_adamw_first_step_closed_form():
+    # t = 1, m = v = 0: the bias-corrected ratio is g / (|g| + eps).
+    rng = np.random.default_rng(4)
+    g = (rng.standard_normal(2000) * 10.0 ** rng.uniform(-6, 1, 2000)).astype(np.float32)
+    p0 = (rng.standard_normal(2000) * 0.02).astype(np.float32)
+    p, m, v = p0.copy(), np.zeros_like(g), np.zeros_like(g)
+    lr, wd, eps = 6e-5, 0.01, 1e-8
+    oracle.adamw(g, p, m, v, 1.0, lr, 0.9, 0.999, eps, wd, 1)
+    gd, pd = g.astype(np.float64), p0.astype(np.float64)
+    assert np.array_equal(m, (0.1 * gd).astype(np.float32))
+    assert np.array_equal(v, (0.001 * gd * gd).astype(np.float32))
+    expect = pd * (1 - lr * wd) - lr * gd / (np.abs(gd) + eps)
+    assert np.max(np.abs(p - expect) / np.abs(expect)) < 2.0**-23
+
+
+def test_adamw_clip_coefficient_scales_gradient():
+    rng = np.random.default_rng(6)
+    g = rng.standard_normal(100).astype(np.float32)
+    p = rng.standard_normal(100).astype(np.float32)
+    a = [p.copy(), np.zeros(100, np.float32), np.zeros(100, np.float32)]
+    b = [p.copy(), np.zeros(100, np.float32), np.zeros(100, np.float32)]
+    oracle.adamw(g, *a, 0.25, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1)
+    oracle.adamw((g * np.float32(0.25)).astype(np.float32), *b, 1.0, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_adamw_matches_torch_adamw_float64():
+    rng = np.random.default_rng(8)
+    n = 4000
+    lr, b1, b2, eps, wd = 6e-5, 0.9, 0.999, 1e-8, 0.01
+    p = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    for t in range(1, 8):
+        g = (rng.standard_normal(n) * 10.0 ** rng.uniform(-4, 0)).astype(np.float32)
+        tp = torch.nn.Parameter(torch.from_numpy(p.astype(np.float64)))
+        opt = torch.optim.AdamW([tp], lr=lr, betas=(b1, b2), eps=eps, weight_decay=wd,
+                                foreach=False, fused=False)
+        opt.state[tp] = {"step": torch.tensor(float(t - 1), dtype=torch.float64),
+                         "exp_avg": torch.from_numpy(m.astype(np.float64)),
+                         "exp_avg_sq": torch.from_numpy(v.astype(np.float64))}
+        tp.grad = torch.from_numpy(g.astype(np.float64))
+        opt.step()
+        oracle.adamw(g, p, m, v, 1.0, lr, b1, b2, eps, wd, t)
+        st = opt.state[tp]
+        for mine, ref in ((p, tp.detach()), (m, st["exp_avg"]), (v, st["exp_avg_sq"])):
+            ref32 = ref.numpy().astype(np.float32)
+            ulps = np.abs(mine.view(np.int32).astype(np.int64) - ref32.view(np.int32).astype(np.int64))
+            assert ulps.max() <= 1, (t, ulps.max())
+
+
+# ------------------------------------------------------------------ scaler
+def run_scaler(flags, power=4, window=3, hysteresis=2, min_scale=1.0):
+    s = oracle.LossScaler(power, window, hysteresis, min_scale)
+    out = []
+    for f in flags:
+        skip = s.update(f)
+        out.append((skip, s.scale, s.good, s.hyst))
+    return out
+
+
+def test_scaler_grows_every_window_without_overflow():
+    out = run_scaler([False] * 10, power=16, window=3)
+    assert [o[1] for o in out] == [2.0 ** (16 + (k + 1) // 3) for k in range(10)]
+    assert not any(o[0] for o in out)
+
+
+def test_scaler_hand_traced_sequence():
+    F, T = False, True
+    # window 3, hysteresis 2, start 16:
+    flags = [F, T, F, F, F, T, T, T, F, F, F, F]
+    expect = [
+        (False, 16, 1, 2),   # good step
+        (True, 16, 0, 1),    # first overflow spends the hysteresis
+        (False, 16, 1, 1),
+        (False, 16, 2, 1),
+        (False, 32, 0, 2),   # third good step: grow, refill hysteresis
+        (True, 32, 0, 1),    # overflow: hysteresis 2 -> 1, scale kept
+        (True, 16, 0, 1),    # overflow with hysteresis 1: halve
+        (True, 8, 0, 1),     # and again
+        (False, 8, 1, 1),
+        (False, 8, 2, 1),
+        (False, 16, 0, 2),
+        (False, 16, 1, 2),
+    ]
+    assert run_scaler(flags) == expect
+
+
+def test_scaler_floor_at_min_scale():
+    out = run_scaler([True] * 10, power=3, window=5, hysteresis=1, min_scale=1.0)
+    assert [o[1] for o in out] == [4, 2, 1, 1, 1, 1, 1, 1, 1, 1]
+    assert all(o[0] for o in out)
+
+
+def test_scaler_page_defaults():
+    s = oracle.LossScaler(16, 100, 2, 1.0)
+    assert s.scale == 65536.0 and s.hyst == 2
+    for _ in range(99):
+        s.update(False)
+    assert s.scale == 65536.0
+    s.update(False)
+    assert s.scale == 131072.0
+
+
+# --------------------------------------------------------------- full step
+def make_world(rng, P, N, world, A, dtype, sigma, scale=1.0):
+    s, padded, valid = oracle.partition(P, world, A)
+    reps = []
+    for _ in range(N):
+        f = np.zeros(padded, np.uint16)
+        f[:P] = f32_bits_to_code((rng.standard_normal(P) * sigma * scale).astype(np.float32), dtype)
+        reps.append(f)
+    master = (rng.standard_normal(padded) * 0.02).astype(np.float32)
+    master[P:] = 0
+    return s, padded, valid, reps, master
+
+
+def split(arr, world, s):
+    return [arr[r * s:(r + 1) * s].copy() for r in range(world)]
+
+
+@pytest.mark.parametrize("dtype,sigma,clip", [(oracle.BF16, 1e-2, 1.0),
+                                              (oracle.FP16, 1e-3, 1e9),
+                                              (oracle.BF16, 1e-5, 1.0)])
+def test_sharded_concatenation_equals_unsharded_step(dtype, sigma, clip):
+    rng = np.random.default_rng(12)
+    P, N, A = 10_007, 8, 8
+    scale = 2.0**10 if dtype == oracle.FP16 else 1.0
+    s, padded, valid, reps, master = make_world(rng, P, N, N, A, dtype, sigma, scale)
+    hp = oracle.Hyper(max_grad_norm=clip, loss_scale=scale)
+    ms, ps_, vs = split(np.zeros(padded, np.float32), N, s), split(master, N, s), \
+        split(np.zeros(padded, np.float32), N, s)
+    full = np.zeros(padded, np.uint16)
+    info = oracle.step(reps, dtype, P, N, A, ps_, ms, vs, full, hp, t=1)
+    # unsharded: the same N replicas, a world of one rank
+    p1 = [master[:P].copy()]
+    m1 = [np.zeros(P, np.float32)]
+    v1 = [np.zeros(P, np.float32)]
+    full1 = np.zeros(P, np.uint16)
+    info1 = oracle.step(reps, dtype, P, 1, 1, p1, m1, v1, full1, hp, t=1)
+    assert info.sumsq == info1.sumsq and info.clipped == info1.clipped
+    assert np.array_equal(np.concatenate(ps_)[:P], p1[0])
+    assert np.array_equal(np.concatenate(ms)[:P], m1[0])
+    assert np.array_equal(np.concatenate(vs)[:P], v1[0])
+    assert np.array_equal(full[:P], full1)
+    # padding is never touched
+    assert not np.concatenate(ms)[P:].any() and not full[P:].any()
+
+
+def test_each_rank_updates_only_its_part():
+    rng = np.random.default_rng(13)
+    P, N, A = 5000, 4, 8
+    s, padded, valid, reps, master = make_world(rng, P, N, N, A, oracle.BF16, 1e-2)
+    ps_ = split(master, N, s)
+    ms = split(np.zeros(padded, np.float32), N, s)
+    vs = split(np.zeros(padded, np.float32), N, s)
+    full = np.full(padded, 0xABCD, np.uint16)
+    oracle.step(reps, oracle.BF16, P, N, A, ps_, ms, vs, full, oracle.Hyper(), t=1)
+    assert np.array_equal(full[:P], oracle.f32_to_bf16(np.concatenate(ps_)[:P]))
+    assert (full[P:] == 0xABCD).all()
+
+
+@pytest.mark.parametrize("where", [(0, 0), (3, 4999), (2, 2600)])
+def test_overflow_anywhere_skips_every_rank(where):
+    rng = np.random.default_rng(14)
+    P, N, A = 5000, 4, 8
+    s, padded, valid, reps, master = make_world(rng, P, N, N, A, oracle.FP16, 1e-3, 2.0**16)
+    reps[where[0]][where[1]] = 0x7C00                      # +inf
+    ps_ = split(master, N, s)
+    ms = split(np.full(padded, 0.5, np.float32), N, s)
+    vs = split(np.full(padded, 0.25, np.float32), N, s)
+    full = np.full(padded, 0x1234, np.uint16)
+    before = [x.copy() for x in ps_ + ms + vs] + [full.copy()]
+    info = oracle.step(reps, oracle.FP16, P, N, A, ps_, ms, vs, full,
+                       oracle.Hyper(loss_scale=2.0**16), t=3)
+    assert info.overflow and info.skipped
+    for a, b in zip(before, ps_ + ms + vs + [full]):
+        assert np.array_equal(a, b)
