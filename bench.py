@@ -1,0 +1,249 @@
+"""Benchmark of the ZeRO sharded-optimizer step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload shard13b]
+
+Default workload: a 13B-parameter flat model over 8 data-parallel ranks;
+this GPU is rank 0 and owns a 1,625,000,064-element shard.  Eight bf16
+replica gradient slices, fp32 master weights and Adam moments, and the
+13,000,000,512-element bf16 full parameter buffer sit in HBM before timing
+starts.  One step = replica reduce (+ unscale, inf/nan flag, partial norm),
+combine (norm, clip factor), AdamW + cast into the rank's slice of the full
+buffer: the three kernels zero_shard_step queues, here queued by the split
+calls so that HIP events between them time each kernel.
+
+Prints one JSON line.  `value` is params updated per second (the shard's
+real elements / step time); `roofline` is for the dominant kernel (the
+AdamW + cast pass) against the 8 TB/s HBM peak; `cpu_baseline` is the CPU
+oracle timed on a bounded sample of the same inputs on one host core.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "ZeRO shard step: params updated/s + achieved HBM GB/s (% of 8 TB/s peak)"
+KERNEL_SRC = os.path.join(ROOT, "zero_sharded_optimizer_step_amd", "csrc", "zero_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_shard13b.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="shard13b", choices=["shard13b"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 28,
+                    help="elements of the shard the CPU oracle is timed on")
+    ap.add_argument("--calibrate-copy", type=int, default=0,
+                    help="only run N torch copies of 4 GiB (counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed
+    counter runs, or None when absent or taken on other kernel sources."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_hash() or rec.get("workload") != workload:
+        return None
+    return rec.get("apply_bytes_per_launch")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ workloads
+def setup_shard13b(torch, Z, W):
+    w = W.SHARD_13B_OF_8
+    part = Z.zero_partition(w.numel, w.world_size, w.alignment)
+    s = part.shard_numel
+    valid = Z.zero_partition_valid_numel(part, 0)
+    dev = "cuda"
+    log("allocating: 8 x %d bf16 grads, 3 x fp32 state, %d bf16 full params" % (s, part.padded_numel))
+    grads = []
+    for i in range(w.world_size):
+        g = torch.empty(s, dtype=torch.bfloat16, device=dev)
+        W.flat_normal(g, 0, w.numel, w.grad_sigma, W.grad_key(w, 0, 0, i))
+        grads.append(g)
+        log("  replica %d generated" % i)
+    master = torch.empty(s, dtype=torch.float32, device=dev)
+    W.flat_normal(master, 0, w.numel, w.master_sigma, W.master_key(w, 0))
+    m = torch.zeros(s, dtype=torch.float32, device=dev)
+    v = torch.zeros(s, dtype=torch.float32, device=dev)
+    full = torch.zeros(part.padded_numel, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(Z.zero_shard_workspace_bytes(s), dtype=torch.uint8, device=dev)
+    partials = torch.zeros(Z.zero_partials_bytes(1), dtype=torch.uint8, device=dev)
+    glob = torch.zeros(256, dtype=torch.uint8, device=dev)
+    return dict(w=w, s=s, valid=valid, grads=grads, master=master, m=m, v=v, full=full, ws=ws,
+                partials=partials, glob=glob, nrep=w.world_size)
+
+
+def run_shard13b(args, torch, Z, W):
+    st = setup_shard13b(torch, Z, W)
+    w, s, valid = st["w"], st["s"], st["valid"]
+    torch.cuda.synchronize()
+
+    def step_args(t):
+        return Z.StepArgs(world_size=w.world_size, rank=0, shard_numel=s, valid_numel=valid,
+                          replica_grads=st["grads"], master=st["master"], exp_avg=st["m"],
+                          exp_avg_sq=st["v"], full_params=st["full"], workspace=st["ws"],
+                          lr=w.lr, weight_decay=w.weight_decay, step=t,
+                          max_grad_norm=w.max_grad_norm)
+
+    stream = torch.cuda.current_stream()
+    t = 1
+    for _ in range(args.warmup):
+        Z.zero_shard_step(step_args(t), stream=stream)
+        t += 1
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    wall0 = time.perf_counter()
+    for k in range(K):
+        a = step_args(t)
+        e = ev[k]
+        e[0].record(stream)
+        Z.zero_shard_reduce(a, 0, st["partials"], stream)
+        e[1].record(stream)
+        Z.zero_shard_combine(st["partials"], 1, w.max_grad_norm, st["glob"], stream)
+        e[2].record(stream)
+        Z.zero_shard_apply(a, st["glob"], stream)
+        e[3].record(stream)
+        t += 1
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = ev[0][0].elapsed_time(ev[-1][3])
+    red = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    comb = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    app = sum(e[2].elapsed_time(e[3]) for e in ev) / K
+    ms = total_ms / K
+    # the fused entry point over the same inputs, as a cross-check
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(K):
+        Z.zero_shard_step(step_args(t), stream=stream)
+        t += 1
+    e1.record(stream)
+    torch.cuda.synchronize()
+    fused_ms = e0.elapsed_time(e1) / K
+    info = Z.zero_shard_step(step_args(t), want_info=True)
+    nrep = st["nrep"]
+    bytes_reduce = valid * (2 * nrep + 4)
+    bytes_apply = valid * (16 + 14)
+    bytes_step = bytes_reduce + bytes_apply
+    res = dict(ms=ms, wall_ms=wall * 1e3 / K, fused_ms=fused_ms, reduce_ms=red, combine_ms=comb,
+               apply_ms=app, valid=valid, bytes_step=bytes_step, bytes_reduce=bytes_reduce,
+               bytes_apply=bytes_apply, norm=info.norm, clipped=info.clipped,
+               overflow=info.overflow, grads=st["grads"], master0=None, st=st)
+    return res
+
+
+def cpu_baseline_shard13b(args, torch, W, st):
+    """The oracle on the first `cpu_sample` elements of the same inputs: the
+    8-replica reduce, clip (norm of the sample), AdamW and bf16 cast."""
+    import numpy as np
+    import oracle
+    n = min(args.cpu_sample, st["valid"])
+    w = st["w"]
+    reps = [g[:n].view(torch.int16).cpu().numpy().view(np.uint16) for g in st["grads"]]
+    # regenerate the initial masters (the timed steps changed the device copy)
+    mdev = torch.empty(n, dtype=torch.float32, device="cuda")
+    W.flat_normal(mdev, 0, w.numel, w.master_sigma, W.master_key(w, 0))
+    p = [mdev.cpu().numpy()]
+    m = [np.zeros(n, np.float32)]
+    v = [np.zeros(n, np.float32)]
+    full = np.zeros(n, np.uint16)
+    hp = oracle.Hyper(lr=w.lr, weight_decay=w.weight_decay, max_grad_norm=w.max_grad_norm)
+    t0 = time.perf_counter()
+    oracle.step(reps, oracle.BF16, n, 1, 8, p, m, v, full, hp, 1)
+    dt = time.perf_counter() - t0
+    return dict(value=n / dt, unit="params/s", cores=1, kind="oracle",
+                sample="first %d elements of rank 0's shard (8 bf16 replicas): reduce, clip, "
+                       "AdamW, bf16 cast; one host thread, %.1f s" % (n, dt))
+
+
+def calibrate_copy(torch, n):
+    """Plain copies of a known size, for scaling the HBM byte counters."""
+    nbytes = 4 << 30
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for i in range(n):
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy %d of %d bytes done" % (i, nbytes))
+    print(json.dumps({"calibration_copy_bytes_read": nbytes, "bytes_written": nbytes}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(each rank's step is local; see the sharding notes). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import zero_sharded_optimizer_step_amd as Z
+    from zero_sharded_optimizer_step_amd import workloads as W
+    Z.lib()
+    if args.calibrate_copy:
+        calibrate_copy(torch, args.calibrate_copy)
+        return
+    r = run_shard13b(args, torch, Z, W)
+    app_gbps = r["bytes_apply"] / (r["apply_ms"] * 1e-3) / 1e9
+    step_gbps = r["bytes_step"] / (r["ms"] * 1e-3) / 1e9
+    traffic = measured_traffic("shard13b")
+    out = {
+        "metric": METRIC,
+        "value": r["valid"] / (r["ms"] * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": W.SHARD_13B_OF_8.name, "shard_numel": r["st"]["s"],
+                   "world_size": 8, "replicas": 8, "grad_dtype": "bf16", "param_dtype": "bf16",
+                   "lr": 6e-5, "weight_decay": 0.01, "max_grad_norm": 1.0},
+        "hbm_gbps": step_gbps,
+        "hbm_frac": step_gbps / HBM_PEAK_GBPS,
+        "bytes_per_step": r["bytes_step"],
+        "kernels_ms": {"reduce": r["reduce_ms"], "combine": r["combine_ms"], "apply": r["apply_ms"]},
+        "fused_call_ms_per_step": r["fused_ms"],
+        "wall_ms_per_step": r["wall_ms"],
+        "roofline": {"bound": "hbm", "kernel": "apply_kernel (AdamW + cast)",
+                     "achieved": app_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": app_gbps / HBM_PEAK_GBPS, "traffic": traffic},
+        "reduce_gbps": r["bytes_reduce"] / (r["reduce_ms"] * 1e-3) / 1e9,
+        "step_check": {"norm": r["norm"], "clipped": r["clipped"], "overflow": r["overflow"]},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        out["cpu_baseline"] = cpu_baseline_shard13b(args, torch, W, r["st"])
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

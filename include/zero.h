@@ -1,0 +1,288 @@
+/*
+ * zero.h -- C ABI of the MI355X (gfx950) ZeRO sharded-optimizer step.
+ *
+ * One data-parallel rank owns one equal part ("shard") of the flat parameter
+ * space and, in each optimizer step,
+ *   1. sums the replicas' gradients over its shard (the arithmetic of the
+ *      gradient reduce-scatter),
+ *   2. undoes the fp16/bf16 loss scale, flags inf/nan and takes its part of
+ *      the global L2 norm,
+ *   3. combines the norm and flag over the world and derives the clip factor,
+ *   4. applies AdamW to its fp32 master weights and Adam moments, skipping
+ *      the whole step when any gradient overflowed,
+ *   5. casts the new masters into its slice of the full low-precision
+ *      parameter buffer (the all-gather's contribution).
+ *
+ * Sources, cited by page title and section:
+ *   [P1] "ZeRO技术解析：大模型分布式训练的革命性突破" (intelliparadigm.com)
+ *   [P2] "大模型分片训练：ZeRO-3策略在PyTorch中的实现" (dn008.com.cn); this
+ *        page has no section numbers and is cited by passage topic
+ *   [P3] "ZeRO 和分片优化器" (aiunderstanding.org)
+ *
+ * Conventions for every call.
+ *   - Returns ZERO_OK (0) or a negative ZERO_E* code; zero_last_error()
+ *     then describes the failure (per calling thread).  Arguments are
+ *     checked before any work is queued: a call that fails has queued
+ *     nothing and touched no memory.
+ *   - The caller owns every buffer.  The library allocates no device
+ *     memory.  "device" pointers are HIP device addresses on the current
+ *     device; "host" pointers are ordinary process memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL: the null stream).
+ *     Device work is queued on it and the call returns without waiting,
+ *     unless a call says otherwise.
+ *   - Device pointers must be 16-byte aligned (ZERO_EALIGN otherwise).
+ *   - Element counts are 64-bit; shards beyond 2^32 elements are fine.
+ *   - Calls keep no state between them; concurrent calls on different
+ *     buffers are safe.  Calls that write the same buffers race.
+ */
+#ifndef ZERO_H
+#define ZERO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZERO_OK        0
+#define ZERO_EINVAL   (-1)   /* an argument is out of range or NULL        */
+#define ZERO_EALIGN   (-2)   /* a device pointer is not 16-byte aligned    */
+#define ZERO_ESIZE    (-3)   /* a caller buffer or table is too small      */
+#define ZERO_EDEVICE  (-4)   /* the HIP runtime reported an error          */
+
+/* Low-precision formats of gradients and working parameters: [P1] §3.3
+ * enables either fp16 or bf16 mixed precision, never both. */
+#define ZERO_FP16 1
+#define ZERO_BF16 2
+
+/* Largest number of data-parallel replicas one reduce can sum. */
+#define ZERO_MAX_REPLICAS 64
+
+/* Thread-local text of the last failure on this thread ("" if none). */
+const char* zero_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Partition.  [P1] §2.1 splits the parameters into N parts and lets each
+ * GPU update only the optimizer state of its own part; [P1] §4.1 says ZeRO
+ * cuts the flat parameter space rather than whole modules; [P3] (technical
+ * insight) has each GPU keep only the matching gradient slice.
+ *
+ * shard_numel is the smallest multiple of `alignment` with
+ * world_size * shard_numel >= numel; rank r owns flat elements
+ * [r*shard_numel, (r+1)*shard_numel), of which the first
+ * valid_numel(r) = clamp(numel - r*shard_numel, 0, shard_numel) are real and
+ * the rest is padding at the end of the flat space.
+ * Errors: numel < 0, world_size < 1, alignment < 1 or not a power of two,
+ * out == NULL -> ZERO_EINVAL.  Host only; touches no device.
+ */
+typedef struct {
+    int64_t numel;          /* real flat parameter count                  */
+    int64_t shard_numel;    /* elements per rank, padding included        */
+    int64_t padded_numel;   /* world_size * shard_numel                   */
+    int32_t world_size;
+    int32_t alignment;
+} zero_partition_t;
+
+int zero_partition(int64_t numel, int32_t world_size, int32_t alignment,
+                   zero_partition_t* out);
+
+/* Real (unpadded) element count of `rank`; -1 if rank is out of range. */
+int64_t zero_partition_valid_numel(const zero_partition_t* p, int32_t rank);
+
+/* ------------------------------------------------------------------------
+ * Bucket plan.  [P1] §2.2: gradients travel in buckets whose size
+ * (reduce_bucket_size) sets the communication granularity; [P1] §5.1 and §6
+ * suggest 2e8 elements; [P1] §5.2 lists contiguous_gradients for memory
+ * locality.
+ *
+ * Tensors are laid end to end in the given order with no gaps: tensor t
+ * occupies flat [slots[t].offset, slots[t].offset + tensor_numel[t]).
+ * Buckets are greedy runs of whole tensors holding at most
+ * reduce_bucket_size elements; a larger tensor is a bucket of its own.
+ * Host arrays: tensor_numel[n_tensors] (in), slots[n_tensors] (out),
+ * buckets[bucket_cap] (out).  *n_buckets receives the bucket count; when it
+ * exceeds bucket_cap the call fails with ZERO_ESIZE and *n_buckets holds the
+ * capacity needed.  Errors: n_tensors < 0, a negative size,
+ * reduce_bucket_size < 1, a NULL pointer -> ZERO_EINVAL.  Host only.
+ */
+typedef struct {
+    int64_t offset;         /* first flat element of the tensor           */
+    int64_t numel;
+    int32_t bucket;         /* index of the bucket that holds it          */
+    int32_t reserved;
+} zero_tensor_slot_t;
+
+typedef struct {
+    int64_t begin;          /* flat range [begin, end) of the bucket      */
+    int64_t end;
+    int32_t first_tensor;
+    int32_t n_tensors;
+} zero_bucket_t;
+
+int zero_bucket_plan(const int64_t* tensor_numel, int32_t n_tensors,
+                     int64_t reduce_bucket_size, zero_tensor_slot_t* slots,
+                     zero_bucket_t* buckets, int32_t bucket_cap,
+                     int32_t* n_buckets);
+
+/* ------------------------------------------------------------------------
+ * Flatten one replica's gradients into its contiguous flat buffer
+ * ([P1] §5.2 contiguous_gradients; buckets per [P1] §2.2).
+ *
+ * For each t < n_tensors, copies tensor_numel = slots[t].numel 16-bit
+ * values from src_dev[t] (device, 2-byte aligned, any offset) to flat
+ * elements [slots[t].offset, +numel) of flat_dev (device, 16-byte aligned),
+ * then writes zeros over [end of the last slot, flat_numel) -- the
+ * partition padding when flat_numel is the padded size.  slots (host) must
+ * have non-decreasing, non-overlapping ranges inside [0, flat_numel);
+ * src_dev is a host array of device pointers.  A bucket at a time may be
+ * flattened by passing its slots and flat_numel = bucket end (no padding
+ * is then written).  Bit copy: dtype (ZERO_FP16 / ZERO_BF16) is checked,
+ * the values are not interpreted.
+ * Errors: NULL pointers, bad dtype, slots out of order or out of range ->
+ * ZERO_EINVAL; flat_dev misaligned -> ZERO_EALIGN; launch -> ZERO_EDEVICE.
+ */
+int zero_bucket_flatten(const zero_tensor_slot_t* slots, int32_t n_tensors,
+                        const void* const* src_dev, int32_t dtype,
+                        void* flat_dev, int64_t flat_numel, void* stream);
+
+/* ------------------------------------------------------------------------
+ * The shard step.
+ *
+ * Arguments of one rank's step.  Hyper-parameters follow [P1] §3.1 (AdamW,
+ * lr 6e-5, weight_decay 0.01), [P1] §6 (gradient_clipping 1.0) and
+ * [P1] §3.3 / §5.1 (fp16 loss scale); the fp32 master weights and two Adam
+ * moments are the state [P3] (FAQ) and [P2] (memory arithmetic) describe.
+ */
+typedef struct {
+    int32_t world_size;       /* ranks in the data-parallel world          */
+    int32_t rank;             /* this rank, in [0, world_size)             */
+    int64_t shard_numel;      /* from zero_partition                       */
+    int64_t valid_numel;      /* real elements of this rank's shard        */
+    int32_t grad_dtype;       /* ZERO_FP16 or ZERO_BF16                    */
+    int32_t param_dtype;      /* ZERO_FP16 or ZERO_BF16                    */
+    int32_t n_replicas;       /* gradients summed, 1..ZERO_MAX_REPLICAS    */
+    int32_t reserved0;
+    /* host array of n_replicas device pointers; entry i points at this
+     * rank's slice (flat element rank*shard_numel) of replica i's flat
+     * gradient buffer.  valid_numel values are read from each.            */
+    const void* const* replica_grad;
+    float* master;            /* device fp32[shard_numel], updated in place */
+    float* exp_avg;           /* device fp32[shard_numel], Adam m           */
+    float* exp_avg_sq;        /* device fp32[shard_numel], Adam v           */
+    /* device buffer of world_size*shard_numel param_dtype values; this rank
+     * writes elements [rank*shard_numel, rank*shard_numel + valid_numel).  */
+    void* full_params;
+    void* workspace;          /* device, zero_shard_workspace_bytes() long  */
+    size_t workspace_bytes;
+    double lr, beta1, beta2, eps, weight_decay;
+    int64_t step;             /* t of this update, >= 1; advance it only
+                                 after a step that was not skipped         */
+    double loss_scale;        /* S > 0: gradients hold S * dL/dw           */
+    double grad_predivide;    /* D > 0: the sum is divided by S*D          */
+    double max_grad_norm;     /* <= 0 disables clipping                    */
+} zero_step_args;
+
+/* Result of the cross-rank combine, 32 bytes in device memory. */
+typedef struct {
+    double  sumsq;            /* sum of squares of the unscaled gradient    */
+    double  norm;             /* sqrt(sumsq)                                */
+    float   coef;             /* clip factor applied to the gradient (1: none) */
+    int32_t overflow;         /* 1: some gradient was inf/nan; step skipped */
+    int32_t clipped;          /* 1: coef < 1 was applied                    */
+    int32_t reserved;
+} zero_global_t;
+
+typedef zero_global_t zero_step_info;
+
+/* Bytes of workspace a rank needs: the fp32 reduced gradient of its shard
+ * (shard_numel * 4, rounded up to 256) followed by the per-block partial
+ * norms and flags and one zero_global_t.  Host only. */
+size_t zero_shard_workspace_bytes(int64_t shard_numel);
+
+/* Bytes of the partials table zero_shard_reduce / zero_shard_combine share
+ * for n_slots ranks.  Host only. */
+size_t zero_partials_bytes(int32_t n_slots);
+
+/* Pass 1 of a rank's step, for worlds simulated in one process.
+ * [P1] §2.1, [P3] technical insight: the reduce-scatter leaves each rank the
+ * sum over replicas of its own gradient slice.  For i < valid_numel:
+ *   acc  = g_0[i] + g_1[i] + ... + g_{R-1}[i]   (fp32, replica order)
+ *   g[i] = acc * fp32(1 / (loss_scale * grad_predivide))
+ * stored as fp32 at the start of a->workspace; then writes this rank's
+ * per-block sums of g^2 (fp64) and inf/nan flags into slot `slot` of
+ * partials_dev (device, zero_partials_bytes(n_slots) long).
+ * Errors: as zero_shard_step; slot < 0 -> ZERO_EINVAL. */
+int zero_shard_reduce(const zero_step_args* a, int32_t slot,
+                      void* partials_dev, void* stream);
+
+/* Combine slots [0, n_slots) of partials_dev in a fixed order into one
+ * zero_global_t at global_dev (device): the global sum of squares and norm,
+ * the overflow flag (any slot flagged, or a non-finite sum), and the clip
+ * factor max_grad_norm / (norm + 1e-6), applied only when below 1 and
+ * max_grad_norm > 0 ([P1] §6 gradient_clipping). */
+int zero_shard_combine(const void* partials_dev, int32_t n_slots,
+                       double max_grad_norm, void* global_dev, void* stream);
+
+/* Pass 2 of a rank's step.  Reads *global_dev; if its overflow flag is set
+ * nothing is written (the skipped step of [P1] §3.3 / §5.1 loss scaling).
+ * Otherwise for i < valid_numel, with g' = g * coef:
+ *   m'  = b1 m + (1 - b1) g'
+ *   v'  = b2 v + (1 - b2) g'^2
+ *   p'  = p (1 - lr wd) - lr/(1 - b1^t) * m' / (sqrt(v')/sqrt(1 - b2^t) + eps)
+ * (AdamW, [P1] §3.1; each GPU updates only its part, [P1] §2.1), all in
+ * fp32, then full_params[rank*shard_numel + i] = round-to-nearest-even of p'
+ * in param_dtype (the all-gather's contribution, [P1] §2.1). */
+int zero_shard_apply(const zero_step_args* a, const void* global_dev,
+                     void* stream);
+
+/* One rank's whole step: zero_shard_reduce into the workspace, a combine
+ * with the peers' contribution (peer_sumsq is the other ranks' total sum of
+ * squares and peer_overflow their OR'd flag; 0 and 0 when this rank holds
+ * the whole world or stands alone), then zero_shard_apply.
+ * If info is not NULL the call waits for the stream and copies the
+ * combine's result into *info (host); otherwise it does not wait.
+ * Errors: world_size < 1, rank outside [0, world_size), valid_numel outside
+ * [0, shard_numel], shard_numel not a multiple of 8, bad dtype, n_replicas
+ * outside [1, ZERO_MAX_REPLICAS], step < 1, loss_scale or grad_predivide
+ * <= 0, lr, betas or eps out of range, a NULL pointer -> ZERO_EINVAL; a
+ * misaligned device pointer -> ZERO_EALIGN; workspace_bytes too small ->
+ * ZERO_ESIZE; a HIP failure -> ZERO_EDEVICE.  When valid_numel is 0 the
+ * rank touches no element and only the workspace must be given. */
+int zero_shard_step(const zero_step_args* a, double peer_sumsq,
+                    int32_t peer_overflow, zero_step_info* info, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Dynamic loss scaler for fp16 ([P1] §3.3: loss_scale_window 100,
+ * hysteresis 2; [P1] §5.1: initial_scale_power 16, min_loss_scale 1).  The
+ * pages give only these knobs; the rule is this library's reading:
+ *   start:        scale = 2^initial_scale_power, good = 0, hyst = hysteresis
+ *   overflow:     skip the step; good = 0; if hyst > 1 then hyst -= 1,
+ *                 else scale = max(scale / 2, min_loss_scale)
+ *   no overflow:  good += 1; when good == loss_scale_window:
+ *                 scale *= 2, good = 0, hyst = hysteresis
+ * The new scale applies to the next step's loss.  Host only.
+ * Errors: NULL st, loss_scale_window < 1, hysteresis < 1,
+ * min_loss_scale <= 0, initial_scale_power outside [-126, 127]
+ * -> ZERO_EINVAL.
+ */
+typedef struct {
+    double  scale;
+    double  min_scale;
+    int32_t good_steps;
+    int32_t hysteresis_left;
+    int32_t window;
+    int32_t hysteresis;
+} zero_loss_scaler_t;
+
+int zero_loss_scaler_init(int32_t initial_scale_power, int32_t loss_scale_window,
+                          int32_t hysteresis, double min_loss_scale,
+                          zero_loss_scaler_t* st);
+
+int zero_loss_scaler_update(zero_loss_scaler_t* st, int32_t overflow,
+                            int32_t* skip_step);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ZERO_H */

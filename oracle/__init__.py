@@ -169,7 +169,7 @@ def bf16_to_f32(b: np.ndarray) -> np.ndarray:
     return out
 
 
-def cast(p: np.ndarray, dtype: int) -> np.ndarray:
+def to_low_precision(p: np.ndarray, dtype: int) -> np.ndarray:
     return f32_to_f16(p) if dtype == FP16 else f32_to_bf16(p)
 
 
@@ -269,7 +269,7 @@ class StepInfo:
 
 def step(replica_flats, dtype: int, numel: int, world_size: int,
          alignment: int, masters, exp_avgs, exp_avg_sqs, full_params,
-         hp: Hyper, t: int, keep_grads: bool = False) -> StepInfo:
+         hp: Hyper, t: int, keep_grads: bool = False, cast: bool = True) -> StepInfo:
     """One sharded step for every rank of the world, in rank order.
 
     replica_flats: N flat uint16 gradient buffers (one per data-parallel
@@ -279,7 +279,8 @@ def step(replica_flats, dtype: int, numel: int, world_size: int,
     full_params: uint16 array of the padded full length; each rank's real
         elements are overwritten with its cast masters.
     A step whose reduced gradient holds inf or nan anywhere is skipped: no
-    state changes, and the caller must not advance t.
+    state changes, and the caller must not advance t.  With cast=False the
+    full buffer is left alone (for steps whose cast nobody reads).
     """
     s, padded, valid = partition(numel, world_size, alignment)
     inv = inv_scale(hp.loss_scale, hp.predivide)
@@ -301,5 +302,6 @@ def step(replica_flats, dtype: int, numel: int, world_size: int,
         p, m, v = masters[r][:n], exp_avgs[r][:n], exp_avg_sqs[r][:n]
         adamw(grads[r], p, m, v, coef, hp.lr, hp.beta1, hp.beta2, hp.eps,
               hp.weight_decay, t)
-        full_params[lo:lo + n] = cast(p, dtype)
+        if cast:
+            full_params[lo:lo + n] = to_low_precision(p, dtype)
     return info

@@ -156,6 +156,20 @@ uint16_t oracle_f32_to_bf16(float x)
     return (uint16_t)(sign | encode_format(y, 7, -126, 127));
 }
 
+/* Every 16-bit code decoded once, by the functions above, when the library
+ * loads; the reduce looks values up here.  The tables hold exactly what the
+ * decoders return, so they change nothing but the speed. */
+static float f16_value[65536];
+static float bf16_value[65536];
+
+__attribute__((constructor)) static void build_decode_tables(void)
+{
+    for (uint32_t c = 0; c < 65536u; ++c) {
+        f16_value[c] = oracle_f16_to_f32((uint16_t)c);
+        bf16_value[c] = oracle_bf16_to_f32((uint16_t)c);
+    }
+}
+
 void oracle_f32_to_f16_array(int64_t n, const float* x, uint16_t* out)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_f32_to_f16(x[i]);
@@ -168,12 +182,12 @@ void oracle_f32_to_bf16_array(int64_t n, const float* x, uint16_t* out)
 
 void oracle_f16_to_f32_array(int64_t n, const uint16_t* h, float* out)
 {
-    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f16_to_f32(h[i]);
+    for (int64_t i = 0; i < n; ++i) out[i] = f16_value[h[i]];
 }
 
 void oracle_bf16_to_f32_array(int64_t n, const uint16_t* b, float* out)
 {
-    for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_to_f32(b[i]);
+    for (int64_t i = 0; i < n; ++i) out[i] = bf16_value[b[i]];
 }
 
 /* ------------------------------------------------------------------------ */
@@ -186,14 +200,13 @@ void oracle_reduce(int32_t n_replicas, const uint16_t* const* replicas,
                    int32_t dtype, int64_t n, float inv_scale, float* g,
                    double* sumsq, int32_t* overflow)
 {
+    const float* value = (dtype == ORACLE_FP16) ? f16_value : bf16_value;
     double ss = *sumsq;
     int32_t bad = *overflow;
     for (int64_t i = 0; i < n; ++i) {
         float acc = 0.0f;
         for (int32_t r = 0; r < n_replicas; ++r) {
-            uint16_t bits = replicas[r][i];
-            float x = (dtype == ORACLE_FP16) ? oracle_f16_to_f32(bits)
-                                             : oracle_bf16_to_f32(bits);
+            float x = value[replicas[r][i]];
             acc = (r == 0) ? x : acc + x;
         }
         float gi = acc * inv_scale;
@@ -223,26 +236,41 @@ int32_t oracle_clip(double sumsq, double max_norm, double* norm, double* coef)
 /* ------------------------------------------------------------------------ */
 /* AdamW on the owned shard.  [P1] §3.1: optimizer AdamW with lr 6e-5 and
  * weight_decay 0.01; [P1] §2.1: each GPU updates only its own partition;
- * [P3] FAQ: Adam keeps first and second moments next to fp32 master
- * weights.  Textbook AdamW (decoupled decay, bias correction from t = 1),
- * in fp64, each stored value rounded once to fp32.                        */
+ * [P3] FAQ and the [P2] memory arithmetic: fp32 master weights and fp32
+ * first and second moments.  Textbook AdamW (decoupled decay, bias
+ * correction from t = 1) evaluated in fp32, the precision of the state:
+ * the scalars are computed in fp64 and rounded once to fp32, then each
+ * element takes these fp32 operations, one rounding each, in this order:
+ *   g' = g * coef
+ *   m' = b1 * m + c1 * g'                      b1 = beta1, c1 = 1 - beta1
+ *   v' = b2 * v + c2 * (g' * g')               b2 = beta2, c2 = 1 - beta2
+ *   d  = sqrt(v') * inv_sqrt_bc2 + eps         inv_sqrt_bc2 = 1/sqrt(1 - beta2^t)
+ *   p' = p * decay - step_size * (m' / d)      decay = 1 - lr wd,
+ *                                              step_size = lr / (1 - beta1^t)
+ * which is lr * m_hat / (sqrt(v_hat) + eps) with m_hat = m'/(1 - beta1^t)
+ * and v_hat = v'/(1 - beta2^t) written out.                               */
 void oracle_adamw(int64_t n, const float* g, float* p, float* m, float* v,
                   double coef, double lr, double beta1, double beta2,
                   double eps, double weight_decay, int64_t t)
 {
-    double bc1 = 1.0 - pow(beta1, (double)t);
-    double bc2 = 1.0 - pow(beta2, (double)t);
+    const float cf = (float)coef;
+    const float b1 = (float)beta1;
+    const float c1 = (float)(1.0 - beta1);
+    const float b2 = (float)beta2;
+    const float c2 = (float)(1.0 - beta2);
+    const float decay = (float)(1.0 - lr * weight_decay);
+    const float step_size = (float)(lr / (1.0 - pow(beta1, (double)t)));
+    const float inv_sqrt_bc2 = (float)(1.0 / sqrt(1.0 - pow(beta2, (double)t)));
+    const float epsf = (float)eps;
     for (int64_t i = 0; i < n; ++i) {
-        double gi = (double)g[i] * coef;
-        double pi = (double)p[i];
-        double m1 = beta1 * (double)m[i] + (1.0 - beta1) * gi;
-        double v1 = beta2 * (double)v[i] + (1.0 - beta2) * gi * gi;
-        double m_hat = m1 / bc1;
-        double v_hat = v1 / bc2;
-        double p1 = pi - lr * weight_decay * pi - lr * m_hat / (sqrt(v_hat) + eps);
-        m[i] = (float)m1;
-        v[i] = (float)v1;
-        p[i] = (float)p1;
+        float gi = g[i] * cf;
+        float m1 = b1 * m[i] + c1 * gi;
+        float v1 = b2 * v[i] + c2 * (gi * gi);
+        float d = sqrtf(v1) * inv_sqrt_bc2 + epsf;
+        float p1 = p[i] * decay - step_size * (m1 / d);
+        m[i] = m1;
+        v[i] = v1;
+        p[i] = p1;
     }
 }
 

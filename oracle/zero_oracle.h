@@ -12,16 +12,16 @@
  *        no section numbers: cited by passage topic
  *   [P3] "ZeRO 和分片优化器" (aiunderstanding.org)
  *
- * Precision.  Where the pages fix a storage precision it is kept: fp32
- * master weights and Adam moments ([P3] FAQ on Adam state; [P2] memory
+ * Precision.  Where the pages fix a precision it is kept: fp32 master
+ * weights and fp32 Adam moments ([P3] FAQ on Adam state; [P2] memory
  * arithmetic for a d_model=4096 layer, which counts weights, gradients,
  * momentum and variance at 4 bytes each), fp16/bf16 gradients and working
- * parameters ([P1] §3.3).  The reduced gradient partition is held in fp32
- * (same [P2] passage) and is defined as the fp32 running sum in replica
- * order, so the overflow decision is taken in fp32.  Everything the pages
- * leave open (the AdamW update, the norm, the clip coefficient) is computed
- * here in fp64 and rounded once to the stored precision.
- *
+ * parameters ([P1] §3.3).  So the reduced gradient partition and the AdamW
+ * update are evaluated in fp32, one IEEE operation at a time in the order
+ * written below; the reduce is the fp32 running sum in replica order, so the
+ * overflow decision is taken in fp32 too.  What the pages leave open in
+ * precision (the norm, the clip factor, the update's scalar constants) is
+ * computed in fp64 and rounded once where it enters fp32 arithmetic.
  * Parity status of each function:
  *   oracle_partition, oracle_bucket_plan      pinned (brute force, page numbers)
  *   oracle_*_to_f32, oracle_f32_to_*          pinned (exhaustive / library)
@@ -94,8 +94,10 @@ int32_t oracle_clip(double sumsq, double max_norm, double* norm, double* coef);
  *   g'  = g * coef
  *   m'  = b1 m + (1 - b1) g'
  *   v'  = b2 v + (1 - b2) g'^2
- *   p'  = p - lr wd p - lr (m'/(1-b1^t)) / (sqrt(v'/(1-b2^t)) + eps)
- * evaluated in fp64 from the fp32 state and rounded once to fp32. */
+ *   p'  = p (1 - lr wd) - lr/(1-b1^t) * m' / (sqrt(v') / sqrt(1-b2^t) + eps)
+ * evaluated in fp32 in the order given in zero_oracle.c, with the scalar
+ * factors computed in fp64 and rounded once to fp32.  coef is the clip
+ * factor (1.0 when clipping does not apply). */
 void oracle_adamw(int64_t n, const float* g, float* p, float* m, float* v,
                   double coef, double lr, double beta1, double beta2,
                   double eps, double weight_decay, int64_t t);

@@ -1,0 +1,224 @@
+"""Side-by-side runs of the HIP library and the CPU oracle (test code).
+
+The inputs (gradients each step, the initial master weights) come from the
+seeded generators in zero_sharded_optimizer_step_amd.workloads; they are
+copied to the host for the oracle before any kernel has touched them.  From
+then on each side keeps its own state: nothing the HIP path writes is ever
+fed to the oracle.
+
+Tolerances, per element:
+  reduced fp32 gradient, overflow flag, skip, loss scale   bit-exact
+  fp32 master, exp_avg, exp_avg_sq                         1e-6 relative
+  global norm                                              1e-5 relative
+  cast fp16/bf16 parameters                                <= 1 ulp
+Both sides evaluate the reduce and the AdamW update in fp32 in the same
+order, so the state is expected to be bit-identical too; the report
+records how many elements are.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Callable, List, Optional
+
+import numpy as np
+import torch
+
+import oracle
+import zero_sharded_optimizer_step_amd as Z
+from zero_sharded_optimizer_step_amd import workloads as W
+from zero_sharded_optimizer_step_amd.world import Hyper, SimulatedWorld
+
+RTOL_STATE = 1e-6
+RTOL_NORM = 1e-5
+MAX_ULP_CAST = 1
+CANARY = 0x3C3C
+
+
+def u16(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def f32(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().cpu().numpy().astype(np.float32, copy=False)
+
+
+def oracle_dtype(dtype) -> int:
+    return oracle.FP16 if dtype == torch.float16 else oracle.BF16
+
+
+def _ordered(c: np.ndarray) -> np.ndarray:
+    c = c.astype(np.int64)
+    return np.where(c & 0x8000, -(c & 0x7FFF), c)
+
+
+def ulp16(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    return np.abs(_ordered(a) - _ordered(b))
+
+
+def assert_bitwise(name: str, got: np.ndarray, ref: np.ndarray) -> None:
+    g = got.view(np.uint32) if got.dtype == np.float32 else got
+    r = ref.view(np.uint32) if ref.dtype == np.float32 else ref
+    if got.dtype == np.float32:
+        both_nan = np.isnan(got) & np.isnan(ref)
+        bad = (g != r) & ~both_nan
+    else:
+        bad = g != r
+    if bad.any():
+        i = int(np.flatnonzero(bad)[0])
+        raise AssertionError("%s: %d of %d differ; first at %d: got %r, oracle %r"
+                             % (name, int(bad.sum()), bad.size, i, got[i], ref[i]))
+
+
+def assert_rel(name: str, got: np.ndarray, ref: np.ndarray, rtol: float) -> float:
+    """|got - ref| <= rtol |ref| element by element; returns the fraction of
+    bit-identical elements."""
+    err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
+    lim = rtol * np.abs(ref.astype(np.float64))
+    bad = ~(err <= lim)
+    if bad.any():
+        i = int(np.flatnonzero(bad)[0])
+        raise AssertionError("%s: %d of %d beyond %g relative; first at %d: got %r, oracle %r"
+                             % (name, int(bad.sum()), bad.size, rtol, i, got[i], ref[i]))
+    return float(np.mean(got.view(np.uint32) == ref.view(np.uint32))) if got.size else 1.0
+
+
+def assert_cast(name: str, got: np.ndarray, ref: np.ndarray, max_ulp: int = MAX_ULP_CAST) -> None:
+    d = ulp16(got, ref)
+    if d.size and d.max() > max_ulp:
+        i = int(np.argmax(d))
+        raise AssertionError("%s: %d ulp apart at %d (got %#06x, oracle %#06x)"
+                             % (name, int(d[i]), i, int(got[i]), int(ref[i])))
+
+
+@dataclass
+class Spec:
+    numel: int
+    world_size: int
+    grad_dtype: torch.dtype
+    grad_sigma: float
+    n_replicas: Optional[int] = None
+    alignment: int = 128
+    param_dtype: Optional[torch.dtype] = None
+    master_sigma: float = 0.02
+    steps: int = 1
+    hp: Hyper = field(default_factory=Hyper)
+    dynamic_scale: bool = False            # fp16 loss scaler drives the scale
+    scaler_args: tuple = (16, 100, 2, 1.0)
+    poison: Optional[List[Optional[W.Poison]]] = None
+    name: str = "case"
+    seed: int = 0
+
+
+@dataclass
+class Report:
+    steps: int = 0
+    skipped: int = 0
+    scales: List[float] = field(default_factory=list)
+    norms: List[float] = field(default_factory=list)
+    norm_rel_err: float = 0.0
+    state_bitwise: float = 1.0
+    cast_max_ulp: int = 0
+
+
+def run(spec: Spec, device="cuda", check_every_step: bool = True,
+        log: Optional[Callable[[str], None]] = None) -> Report:
+    """Run spec.steps steps on both sides and compare them."""
+    nrep = spec.n_replicas or spec.world_size
+    pdt = spec.param_dtype or spec.grad_dtype
+    world = SimulatedWorld(spec.numel, spec.world_size, nrep, spec.alignment, spec.grad_dtype,
+                           pdt, device)
+    s, P = world.s, spec.numel
+    odt = oracle_dtype(spec.grad_dtype)
+    podt = oracle_dtype(pdt)
+    assert odt == podt, "the oracle casts into the gradient's format"
+    # initial state: masters from the generator, zero moments, canary params
+    mkey = ("master", spec.name, spec.seed)
+    for k, r in enumerate(world.ranks):
+        W.flat_normal(world.master[k], r * s, P, spec.master_sigma, mkey)
+    world.full_params.view(torch.int16).fill_(CANARY)
+    o_master = [f32(m) for m in world.master]            # generator output
+    o_m = [np.zeros(s, np.float32) for _ in world.ranks]
+    o_v = [np.zeros(s, np.float32) for _ in world.ranks]
+    o_full = np.full(world.padded, CANARY, np.uint16)
+    hp = Hyper(**vars(spec.hp))
+    o_hp = oracle.Hyper(lr=hp.lr, beta1=hp.beta1, beta2=hp.beta2, eps=hp.eps,
+                        weight_decay=hp.weight_decay, max_grad_norm=hp.max_grad_norm,
+                        loss_scale=hp.loss_scale, predivide=hp.grad_predivide)
+    if spec.dynamic_scale:
+        sc_lib = Z.zero_loss_scaler_init(*spec.scaler_args)
+        sc_orc = oracle.LossScaler(*spec.scaler_args)
+    t_lib = t_orc = 1
+    rep = Report()
+    for step in range(spec.steps):
+        scale = sc_lib.scale if spec.dynamic_scale else hp.loss_scale
+        if spec.dynamic_scale:
+            assert sc_orc.scale == scale, (step, sc_orc.scale, scale)
+        hp.loss_scale = scale
+        o_hp.loss_scale = scale
+        for i in range(nrep):
+            W.flat_normal(world.grads[i], world.lo, P, spec.grad_sigma,
+                          ("grad", spec.name, spec.seed, step, i), scale=scale)
+        if spec.poison and spec.poison[step] is not None:
+            W.plant(world.grads[spec.poison[step].replica], spec.poison[step])
+        o_grads = [u16(gbuf) for gbuf in world.grads]     # generator output
+        world.step(hp, t_lib)
+        res = world.result()
+        info = oracle.step(o_grads, odt, P, spec.world_size, spec.alignment, o_master, o_m,
+                           o_v, o_full, o_hp, t_orc, keep_grads=True, cast=True)
+        # flags and the clip decision: exact
+        assert bool(res.overflow) == info.overflow, (step, res.overflow, info.overflow)
+        if not info.overflow:
+            assert bool(res.clipped) == info.clipped, (step, res.clipped, info.clipped)
+            rel = abs(res.norm - info.norm) / max(info.norm, 1e-300)
+            assert rel <= RTOL_NORM, (step, res.norm, info.norm)
+            rep.norm_rel_err = max(rep.norm_rel_err, rel)
+            rep.norms.append(info.norm)
+        if spec.dynamic_scale:
+            skip_lib = Z.zero_loss_scaler_update(sc_lib, bool(res.overflow))
+            skip_orc = sc_orc.update(info.overflow)
+            assert skip_lib == skip_orc and sc_lib.scale == sc_orc.scale
+            assert sc_lib.good_steps == sc_orc.good and sc_lib.hysteresis_left == sc_orc.hyst
+            rep.scales.append(sc_lib.scale)
+        if not res.overflow:
+            t_lib += 1
+        if not info.overflow:
+            t_orc += 1
+        else:
+            rep.skipped += 1
+        last = step == spec.steps - 1
+        if check_every_step or last:
+            _compare(world, info, o_master, o_m, o_v, o_full, odt, step, rep)
+        rep.steps += 1
+        if log:
+            log("step %d: overflow=%d norm=%.6g scale=%g" % (step, info.overflow, info.norm,
+                                                               scale))
+    assert t_lib == t_orc
+    return rep
+
+
+def _compare(world, info, o_master, o_m, o_v, o_full, odt, step, rep):
+    s = world.s
+    eq = []
+    for k, r in enumerate(world.ranks):
+        n = world.valid[r]
+        if info.grads:
+            assert_bitwise("step %d rank %d reduced grad" % (step, r),
+                           f32(world.reduced_grad(k)[:n]), info.grads[r])
+        for name, gpu, ref in (("master", world.master[k], o_master[k]),
+                               ("exp_avg", world.exp_avg[k], o_m[k]),
+                               ("exp_avg_sq", world.exp_avg_sq[k], o_v[k])):
+            got = f32(gpu)
+            eq.append(assert_rel("step %d rank %d %s" % (step, r, name), got[:n], ref[:n],
+                                 RTOL_STATE))
+            assert_bitwise("step %d rank %d %s padding" % (step, r, name), got[n:], ref[n:])
+    full = u16(world.full_params)
+    real = np.zeros(full.size, bool)
+    for r in range(world.world_size):
+        real[r * s:r * s + world.valid[r]] = True
+    assert_cast("step %d full params" % step, full[real], o_full[real])
+    assert_bitwise("step %d full params outside the ranks' real elements" % step,
+                   full[~real], o_full[~real])
+    d = ulp16(full[real], o_full[real])
+    rep.cast_max_ulp = max(rep.cast_max_ulp, int(d.max()) if d.size else 0)
+    rep.state_bitwise = min(rep.state_bitwise, min(eq) if eq else 1.0)

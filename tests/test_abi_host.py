@@ -1,0 +1,238 @@
+"""CPU tests of the C-ABI library: it loads, exports every declared symbol,
+and its host-only logic (partition, bucket plan, loss scaler, argument
+checks) matches the oracle.  No call here reaches the HIP runtime: device
+entry points are only called with arguments they reject before any work.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import zero_sharded_optimizer_step_amd as Z
+from zero_sharded_optimizer_step_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    names = set()
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", f)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(zero_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_symbols()
+    assert len(names) >= 13
+    L = ctypes.CDLL(_abi.LIB_PATH)
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+    assert set(names) == set(_abi._PROTOTYPES), "binding and header disagree"
+
+
+def test_binding_names_match_the_abi():
+    for n in declared_symbols():
+        assert callable(getattr(Z, n)), n
+
+
+# ---------------------------------------------------------------- partition
+def test_partition_matches_oracle():
+    rng = np.random.default_rng(0)
+    cases = [(P, N, A) for P in (0, 1, 7, 8, 127, 128, 129, 1000, 4096)
+             for N in (1, 2, 3, 4, 7, 8, 16) for A in (1, 2, 8, 128)]
+    cases += [(int(rng.integers(0, 2**40)), int(rng.integers(1, 1025)), int(2 ** rng.integers(0, 12)))
+              for _ in range(500)]
+    cases += [(13_000_000_000, 8, 128), (50_000_000, 4, 128), (67_125_248, 8, 128)]
+    for P, N, A in cases:
+        part = Z.zero_partition(P, N, A)
+        s, padded, valid = oracle.partition(P, N, A)
+        assert (part.shard_numel, part.padded_numel) == (s, padded), (P, N, A)
+        assert [Z.zero_partition_valid_numel(part, r) for r in range(N)] == valid
+
+
+@pytest.mark.parametrize("args", [(-1, 4, 8), (10, 0, 8), (10, 4, 0), (10, 4, 3), (10, 4, 96)])
+def test_partition_rejects(args):
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_partition(*args)
+    assert e.value.code == Z.ZERO_EINVAL
+    assert Z.zero_last_error()
+
+
+def test_partition_valid_numel_out_of_range():
+    part = Z.zero_partition(100, 4, 8)
+    with pytest.raises(ValueError):
+        Z.zero_partition_valid_numel(part, 4)
+
+
+# -------------------------------------------------------------- bucket plan
+def test_bucket_plan_matches_oracle():
+    rng = np.random.default_rng(1)
+    for _ in range(300):
+        T = int(rng.integers(0, 80))
+        sizes = [int(x) for x in rng.integers(0, 3000, size=T)]
+        if T and rng.random() < 0.3:
+            sizes[int(rng.integers(T))] = 0
+        cap = int(rng.integers(1, 6000))
+        slots, buckets = Z.zero_bucket_plan(sizes, cap)
+        off, bof, nb = oracle.bucket_plan(sizes, cap)
+        assert [s.offset for s in slots] == list(off)
+        assert [s.numel for s in slots] == sizes
+        assert [s.bucket for s in slots] == list(bof)
+        assert len(buckets) == nb
+        for b, bk in enumerate(buckets):
+            members = [t for t in range(T) if bof[t] == b]
+            assert bk.first_tensor == members[0] and bk.n_tensors == len(members)
+            assert bk.begin == off[members[0]]
+            assert bk.end == off[members[-1]] + sizes[members[-1]]
+
+
+def test_bucket_plan_ragged_workload():
+    from zero_sharded_optimizer_step_amd.workloads import RAGGED_2000
+    sizes = list(RAGGED_2000.tensor_sizes)
+    slots, buckets = Z.zero_bucket_plan(sizes, int(2e8))
+    off, bof, nb = oracle.bucket_plan(sizes, int(2e8))
+    assert len(buckets) == nb and [s.bucket for s in slots] == list(bof)
+    assert buckets[-1].end == sum(sizes) == RAGGED_2000.numel
+    assert all(b.end - b.begin <= 2e8 for b in buckets)
+
+
+def test_bucket_plan_reports_needed_capacity():
+    sizes = (_abi.i64 * 3)(5, 5, 5)
+    slots = (_abi.zero_tensor_slot_t * 3)()
+    buckets = (_abi.zero_bucket_t * 1)()
+    nb = _abi.i32()
+    rc = Z.lib().zero_bucket_plan(sizes, 3, 5, slots, buckets, 1, ctypes.byref(nb))
+    assert rc == Z.ZERO_ESIZE and nb.value == 3
+    rc = Z.lib().zero_bucket_plan(sizes, 3, 0, slots, buckets, 1, ctypes.byref(nb))
+    assert rc == Z.ZERO_EINVAL
+
+
+# ---------------------------------------------------------------- scaler
+@pytest.mark.parametrize("seed", range(6))
+def test_loss_scaler_matches_oracle(seed):
+    rng = np.random.default_rng(seed)
+    window = int(rng.integers(1, 8))
+    hyst = int(rng.integers(1, 4))
+    power = int(rng.integers(0, 20))
+    mine = Z.zero_loss_scaler_init(power, window, hyst, 1.0)
+    ref = oracle.LossScaler(power, window, hyst, 1.0)
+    for _ in range(400):
+        of = bool(rng.random() < 0.2)
+        assert Z.zero_loss_scaler_update(mine, of) == ref.update(of)
+        assert mine.scale == ref.scale
+        assert mine.good_steps == ref.good and mine.hysteresis_left == ref.hyst
+
+
+def test_loss_scaler_rejects():
+    for args in ((16, 0, 2, 1.0), (16, 100, 0, 1.0), (16, 100, 2, 0.0), (200, 100, 2, 1.0)):
+        with pytest.raises(Z.ZeroError):
+            Z.zero_loss_scaler_init(*args)
+    st = _abi.zero_loss_scaler_t()        # never initialised
+    with pytest.raises(Z.ZeroError):
+        Z.zero_loss_scaler_update(st, False)
+
+
+# ------------------------------------------------ argument checks, no device
+class FakeTensor:
+    """Stands in for a device tensor: only an address and a size."""
+
+    def __init__(self, addr, nbytes=1 << 20, dtype=None):
+        self.addr, self.nbytes, self.dtype = addr, nbytes, dtype
+
+    def data_ptr(self):
+        return self.addr
+
+    def numel(self):
+        return self.nbytes
+
+    def element_size(self):
+        return 1
+
+
+def good_args(**kw):
+    import torch
+    s = 1024
+    d = dict(world_size=4, rank=1, shard_numel=s, valid_numel=s,
+             replica_grads=[FakeTensor(0x10000 * (i + 1), dtype=torch.bfloat16) for i in range(4)],
+             master=FakeTensor(0x100000), exp_avg=FakeTensor(0x200000),
+             exp_avg_sq=FakeTensor(0x300000),
+             full_params=FakeTensor(0x400000, dtype=torch.bfloat16),
+             workspace=FakeTensor(0x500000, Z.zero_shard_workspace_bytes(s)),
+             grad_dtype=Z.ZERO_BF16, param_dtype=Z.ZERO_BF16)
+    d.update(kw)
+    return Z.StepArgs(**d)
+
+
+BAD = [
+    (dict(world_size=0), Z.ZERO_EINVAL), (dict(rank=4), Z.ZERO_EINVAL),
+    (dict(rank=-1), Z.ZERO_EINVAL), (dict(shard_numel=1001, valid_numel=10), Z.ZERO_EINVAL),
+    (dict(valid_numel=1025), Z.ZERO_EINVAL), (dict(step=0), Z.ZERO_EINVAL),
+    (dict(loss_scale=0.0), Z.ZERO_EINVAL), (dict(grad_predivide=-1.0), Z.ZERO_EINVAL),
+    (dict(beta1=1.0), Z.ZERO_EINVAL), (dict(beta2=-0.1), Z.ZERO_EINVAL),
+    (dict(eps=0.0), Z.ZERO_EINVAL), (dict(lr=float("nan")), Z.ZERO_EINVAL),
+    (dict(max_grad_norm=float("nan")), Z.ZERO_EINVAL), (dict(grad_dtype=3), Z.ZERO_EINVAL),
+    (dict(param_dtype=0), Z.ZERO_EINVAL), (dict(replica_grads=[]), Z.ZERO_EINVAL),
+    (dict(master=FakeTensor(0)), Z.ZERO_EINVAL),
+    (dict(master=FakeTensor(0x100004)), Z.ZERO_EALIGN),
+    (dict(full_params=FakeTensor(0x400002)), Z.ZERO_EALIGN),
+    (dict(workspace=FakeTensor(0x500000, 64)), Z.ZERO_ESIZE),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD)
+def test_step_rejects_bad_arguments_before_any_work(kw, code):
+    import torch
+    if kw.get("replica_grads") == []:
+        a = good_args()
+        c = a.c_args()
+        c.n_replicas = 0
+        rc = Z.lib().zero_shard_step(ctypes.byref(c), 0.0, 0, None, None)
+        assert rc == code
+        return
+    a = good_args(**kw)
+    for call in (lambda: Z.zero_shard_step(a, stream=0),
+                 lambda: Z.zero_shard_reduce(a, 0, FakeTensor(0x600000), stream=0),
+                 lambda: Z.zero_shard_apply(a, FakeTensor(0x700000), stream=0)):
+        with pytest.raises(Z.ZeroError) as e:
+            call()
+        assert e.value.code == code, Z.zero_last_error()
+
+
+def test_misaligned_replica_pointer():
+    import torch
+    reps = [FakeTensor(0x10000, dtype=torch.bfloat16), FakeTensor(0x20008, dtype=torch.bfloat16)]
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_shard_step(good_args(replica_grads=reps), stream=0)
+    assert e.value.code == Z.ZERO_EALIGN and "replica_grad[1]" in Z.zero_last_error()
+
+
+def test_combine_and_flatten_reject():
+    L = Z.lib()
+    assert L.zero_shard_combine(None, 1, 1.0, 0x1000, None) == Z.ZERO_EINVAL
+    assert L.zero_shard_combine(0x1000, 0, 1.0, 0x2000, None) == Z.ZERO_EINVAL
+    assert L.zero_shard_combine(0x1008, 1, 1.0, 0x2000, None) == Z.ZERO_EALIGN
+    assert L.zero_shard_combine(0x1000, 1, float("nan"), 0x2000, None) == Z.ZERO_EINVAL
+    slots = (_abi.zero_tensor_slot_t * 2)()
+    slots[0].offset, slots[0].numel = 0, 10
+    slots[1].offset, slots[1].numel = 5, 10          # overlaps slot 0
+    ptrs = (_abi.vp * 2)(0x1000, 0x2000)
+    assert L.zero_bucket_flatten(slots, 2, ptrs, Z.ZERO_BF16, 0x4000, 100, None) == Z.ZERO_EINVAL
+    slots[1].offset = 10
+    assert L.zero_bucket_flatten(slots, 2, ptrs, Z.ZERO_BF16, 0x4000, 15, None) == Z.ZERO_EINVAL
+    assert L.zero_bucket_flatten(slots, 2, ptrs, 7, 0x4000, 100, None) == Z.ZERO_EINVAL
+    assert L.zero_bucket_flatten(slots, 2, ptrs, Z.ZERO_BF16, 0x4002, 100, None) == Z.ZERO_EALIGN
+    ptrs[1] = 0x2001
+    assert L.zero_bucket_flatten(slots, 2, ptrs, Z.ZERO_BF16, 0x4000, 100, None) == Z.ZERO_EALIGN
+
+
+def test_workspace_and_partials_sizes():
+    for s in (0, 8, 1024, 1_625_000_064):
+        ws = Z.zero_shard_workspace_bytes(s)
+        assert ws >= 4 * s + 16 * 2048 + 32 and ws % 256 == 0
+    assert Z.zero_partials_bytes(8) == 8 * Z.zero_partials_bytes(1) > 0

@@ -1,0 +1,241 @@
+"""GPU parity of the HIP library against the CPU oracle, through the C ABI.
+
+Small and mid sizes that the oracle finishes in seconds but that span many
+blocks of the kernels' grid and end in ragged tails; empty ranks, poisoned
+gradients, both formats, clipping on and off, several steps.  Each case
+prints its name before touching the GPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+import parity
+import zero_sharded_optimizer_step_amd as Z
+from zero_sharded_optimizer_step_amd import workloads as W
+from zero_sharded_optimizer_step_amd.world import Hyper, SimulatedWorld
+
+pytestmark = pytest.mark.gpu
+
+BF16, FP16 = torch.bfloat16, torch.float16
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+CASES = [
+    # (numel, world, alignment, dtype, sigma, loss_scale, clip, steps)
+    (5, 4, 8, BF16, 1e-2, 1.0, 1.0, 2),             # three empty ranks, tail only
+    (1000, 3, 8, BF16, 1e-2, 1.0, 1.0, 3),
+    (4097, 4, 8, FP16, 1e-3, 2.0**16, 1.0, 3),
+    (100_003, 8, 128, BF16, 1e-3, 1.0, 1.0, 3),
+    (100_003, 8, 128, BF16, 1e-3, 1.0, 0.0, 3),     # clipping off
+    (1_048_583, 4, 128, FP16, 1e-3, 2.0**12, 1e9, 2),  # clip threshold never reached
+    (3_000_001, 2, 128, BF16, 3e-2, 1.0, 1.0, 2),   # >1 grid-stride iteration per thread
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"P{c[0]}-N{c[1]}-A{c[2]}-{str(c[3])[6:]}-clip{c[6]}"
+                                             for c in CASES])
+def test_world_matches_oracle(case):
+    numel, world, align, dt, sigma, scale, clip, steps = case
+    say("case %s" % (case,))
+    spec = parity.Spec(numel=numel, world_size=world, alignment=align, grad_dtype=dt,
+                       grad_sigma=sigma, steps=steps, name="small-%d-%d" % (numel, world),
+                       hp=Hyper(loss_scale=scale, max_grad_norm=clip))
+    rep = parity.run(spec)
+    say("norm rel err %.2e, bitwise state fraction %.6f, cast max ulp %d"
+        % (rep.norm_rel_err, rep.state_bitwise, rep.cast_max_ulp))
+
+
+def test_tiny_workload_matches_oracle():
+    w = W.TINY
+    say("tiny workload")
+    spec = parity.Spec(numel=w.numel, world_size=w.world_size, grad_dtype=w.grad_dtype,
+                       grad_sigma=w.grad_sigma, hp=Hyper(loss_scale=w.loss_scale), steps=2,
+                       name="tiny")
+    rep = parity.run(spec)
+    assert rep.norms[0] > 1.0          # the clip is active on this workload
+
+
+def test_more_replicas_than_ranks_and_generic_replica_count():
+    # 11 replicas (the kernel's generic replica loop) over 3 ranks.
+    say("11 replicas, 3 ranks")
+    spec = parity.Spec(numel=50_001, world_size=3, n_replicas=11, alignment=8, grad_dtype=BF16,
+                       grad_sigma=1e-2, steps=2, name="generic-replicas")
+    parity.run(spec)
+
+
+@pytest.mark.parametrize("kind", [0, 1, 2])
+@pytest.mark.parametrize("where", ["first", "last_rank_tail", "middle"])
+def test_poisoned_step_is_skipped_everywhere(kind, where):
+    numel, world = 20_011, 4
+    say("poison kind %d at %s" % (kind, where))
+    s = Z.zero_partition(numel, world, 8).shard_numel
+    idx = {"first": 0, "last_rank_tail": numel - 1, "middle": s + s // 2}[where]
+    sched = [None, W.Poison(1, 2, idx, kind), None]
+    spec = parity.Spec(numel=numel, world_size=world, alignment=8, grad_dtype=FP16,
+                       grad_sigma=1e-3, steps=3, poison=sched, dynamic_scale=True,
+                       scaler_args=(10, 2, 1, 1.0), name="poison")
+    rep = parity.run(spec)
+    assert rep.skipped == 1
+
+
+def test_dynamic_scale_trajectory_small():
+    # The scaled workload's schedule, at a size the oracle runs every step of.
+    steps = 200
+    numel, world = 65_543, 4
+    sched = W.poison_schedule(steps, world, numel, p=0.05, seed=0)
+    say("scaler trajectory, %d poisoned steps" % sum(x is not None for x in sched))
+    spec = parity.Spec(numel=numel, world_size=world, grad_dtype=FP16, grad_sigma=1e-3,
+                       steps=steps, poison=sched, dynamic_scale=True,
+                       scaler_args=(16, 100, 2, 1.0), name="scaler-small")
+    rep = parity.run(spec, check_every_step=False)
+    assert rep.skipped == sum(x is not None for x in sched)
+    assert min(rep.scales) < 2.0**16          # overflows halved the scale
+
+
+def test_dynamic_scale_grows_and_shrinks():
+    # A short window so the scale also grows; same poison rate.
+    steps = 120
+    numel, world = 10_007, 2
+    sched = W.poison_schedule(steps, world, numel, p=0.05, seed=1)
+    say("scaler window 5, %d poisoned steps" % sum(x is not None for x in sched))
+    spec = parity.Spec(numel=numel, world_size=world, alignment=8, grad_dtype=FP16,
+                       grad_sigma=1e-3, steps=steps, poison=sched, dynamic_scale=True,
+                       scaler_args=(10, 5, 2, 1.0), name="scaler-grow")
+    rep = parity.run(spec, check_every_step=False)
+    ups = sum(b > a for a, b in zip(rep.scales, rep.scales[1:]))
+    downs = sum(b < a for a, b in zip(rep.scales, rep.scales[1:]))
+    assert ups > 0 and downs > 0
+
+
+def _fill(world, seed):
+    for i in range(world.n_replicas):
+        W.flat_normal(world.grads[i], world.lo, world.numel, 1e-2, ("det", seed, i))
+    for k, r in enumerate(world.ranks):
+        W.flat_normal(world.master[k], r * world.s, world.numel, 0.02, ("detm", seed))
+
+
+def test_run_to_run_bitwise_determinism():
+    say("determinism")
+    outs = []
+    for _ in range(2):
+        world = SimulatedWorld(777_777, 8, alignment=128, grad_dtype=BF16)
+        _fill(world, 1)
+        for t in (1, 2):
+            world.step(Hyper(), t)
+        res = world.result()
+        outs.append((res.sumsq, res.norm, res.coef,
+                     [parity.f32(m) for m in world.master + world.exp_avg + world.exp_avg_sq],
+                     parity.u16(world.full_params)))
+    a, b = outs
+    assert a[:3] == b[:3]
+    for x, y in zip(a[3], b[3]):
+        parity.assert_bitwise("rerun", x, y)
+    parity.assert_bitwise("rerun params", a[4], b[4])
+
+
+def test_sharded_concatenation_equals_unsharded_on_gpu():
+    say("sharded == unsharded")
+    numel = 300_007
+    sharded = SimulatedWorld(numel, 4, alignment=8, grad_dtype=BF16)
+    whole = SimulatedWorld(numel, 1, n_replicas=4, alignment=8, grad_dtype=BF16)
+    _fill(sharded, 2)
+    for i in range(4):
+        W.flat_normal(whole.grads[i], 0, numel, 1e-2, ("det", 2, i))
+    W.flat_normal(whole.master[0], 0, numel, 0.02, ("detm", 2))
+    for w in (sharded, whole):
+        w.step(Hyper(), 1)
+    assert sharded.result().clipped and whole.result().clipped
+    assert abs(sharded.result().norm - whole.result().norm) <= 1e-12 * whole.result().norm
+    cat = torch.cat([m[:v] for m, v in zip(sharded.master, sharded.valid)])
+    parity.assert_rel("masters", parity.f32(cat), parity.f32(whole.master[0][:numel]), 1e-6)
+
+
+def test_fused_step_equals_split_calls_and_peer_sum():
+    say("zero_shard_step vs reduce/combine/apply")
+    numel, world = 123_457, 1
+    w1 = SimulatedWorld(numel, world, n_replicas=8, alignment=128, grad_dtype=BF16)
+    w2 = SimulatedWorld(numel, world, n_replicas=8, alignment=128, grad_dtype=BF16)
+    for w in (w1, w2):
+        for i in range(8):
+            W.flat_normal(w.grads[i], 0, numel, 1e-2, ("fused", i))
+        W.flat_normal(w.master[0], 0, numel, 0.02, ("fusedm",))
+    hp = Hyper()
+    w1.step(hp, 1)
+    info = Z.zero_shard_step(w2.rank_args(0, hp, 1), want_info=True)
+    r1 = w1.result()
+    assert (info.sumsq, info.coef, info.overflow) == (r1.sumsq, r1.coef, r1.overflow)
+    parity.assert_bitwise("master", parity.f32(w1.master[0]), parity.f32(w2.master[0]))
+    # peers' sum of squares enters the norm: with a large peer sum the clip
+    # factor follows the combined norm
+    w3 = SimulatedWorld(numel, world, n_replicas=8, alignment=128, grad_dtype=BF16)
+    for i in range(8):
+        W.flat_normal(w3.grads[i], 0, numel, 1e-2, ("fused", i))
+    info3 = Z.zero_shard_step(w3.rank_args(0, hp, 1), peer_sumsq=3 * r1.sumsq,
+                              want_info=True)
+    assert abs(info3.norm - 2 * r1.norm) <= 1e-12 * r1.norm
+    assert abs(info3.coef - np.float32(1.0 / (2 * r1.norm + 1e-6))) <= 1e-7 * info3.coef
+    info4 = Z.zero_shard_step(w3.rank_args(0, hp, 1), peer_overflow=True, want_info=True)
+    assert info4.overflow == 1
+
+
+# ---------------------------------------------------------------- flatten
+def _flatten_case(sizes, odd_views, flat_numel=None, seed=0):
+    rng = np.random.default_rng(seed)
+    srcs = []
+    for k, n in enumerate(sizes):
+        off = int(rng.integers(1, 8)) if odd_views and k % 2 else 0
+        base = torch.from_numpy(rng.integers(0, 65536, n + off, dtype=np.uint64)
+                                .astype(np.uint16).view(np.int16)).cuda()
+        srcs.append(base[off:off + n].view(torch.bfloat16))
+    slots, buckets = Z.zero_bucket_plan(sizes, 1 << 14)
+    total = sum(sizes)
+    flat_numel = flat_numel if flat_numel is not None else total + 77
+    flat = torch.full((flat_numel + 64,), 0x1357, dtype=torch.int16, device="cuda")
+    Z.zero_bucket_flatten(slots, srcs, torch.bfloat16, flat.view(torch.bfloat16), flat_numel)
+    got = parity.u16(flat.view(torch.bfloat16))
+    ref = np.concatenate([parity.u16(s) for s in srcs]) if sizes else np.zeros(0, np.uint16)
+    parity.assert_bitwise("flat", got[:total], ref)
+    assert (got[total:flat_numel] == 0).all(), "padding not zeroed"
+    assert (got[flat_numel:] == 0x1357).all(), "wrote past flat_numel"
+    return slots, buckets, srcs
+
+
+@pytest.mark.parametrize("odd", [False, True])
+def test_flatten_ragged_tensors(odd):
+    rng = np.random.default_rng(3)
+    sizes = [int(x) for x in rng.integers(0, 40_000, 300)]
+    sizes[5] = 0
+    sizes[6] = 1
+    sizes[7] = 7
+    sizes[8] = 9
+    say("flatten %d tensors, odd views %s" % (len(sizes), odd))
+    _flatten_case(sizes, odd)
+
+
+def test_flatten_edge_cases():
+    say("flatten edges")
+    _flatten_case([], False, flat_numel=100)
+    _flatten_case([3], True, flat_numel=3)
+    _flatten_case([1, 1, 1, 1, 1, 1, 1, 1, 1], True)
+    _flatten_case([5_000_001], True)
+    _flatten_case([8] * 130 + [13] * 131, True)             # more than one launch batch
+
+
+def test_flatten_per_bucket():
+    say("flatten bucket by bucket")
+    rng = np.random.default_rng(4)
+    sizes = [int(x) for x in rng.integers(1, 9000, 60)]
+    slots, buckets = Z.zero_bucket_plan(sizes, 20_000)
+    srcs = [torch.randint(-32768, 32767, (n,), dtype=torch.int16, device="cuda")
+            .view(torch.bfloat16) for n in sizes]
+    total = sum(sizes)
+    flat = torch.full((total,), 0x1111, dtype=torch.int16, device="cuda")
+    for b in buckets:
+        sl = slots[b.first_tensor:b.first_tensor + b.n_tensors]
+        Z.zero_bucket_flatten(sl, srcs[b.first_tensor:b.first_tensor + b.n_tensors],
+                              torch.bfloat16, flat.view(torch.bfloat16), b.end)
+    ref = np.concatenate([parity.u16(s) for s in srcs])
+    parity.assert_bitwise("flat", parity.u16(flat.view(torch.bfloat16)), ref)

@@ -20,14 +20,15 @@ PINS = [os.path.join(HERE, f) for f in
         ("test_oracle_partition.py", "test_oracle_formats.py", "test_oracle_step.py")]
 
 MUTANTS = {
-    "m_bias_correction_dropped": ("double m_hat = m1 / bc1;", "double m_hat = m1;"),
-    "v_bias_correction_dropped": ("double v_hat = v1 / bc2;", "double v_hat = v1;"),
-    "decay_sign_flipped": ("pi - lr * weight_decay * pi", "pi + lr * weight_decay * pi"),
-    "eps_inside_sqrt": ("(sqrt(v_hat) + eps)", "sqrt(v_hat + eps)"),
-    "v_uses_g_not_g2": ("(1.0 - beta2) * gi * gi", "(1.0 - beta2) * gi"),
-    "betas_swapped_in_m": ("beta1 * (double)m[i] + (1.0 - beta1)",
-                           "beta2 * (double)m[i] + (1.0 - beta2)"),
-    "clip_not_applied_to_g": ("double gi = (double)g[i] * coef;", "double gi = (double)g[i];"),
+    "m_bias_correction_dropped": ("(float)(lr / (1.0 - pow(beta1, (double)t)))", "(float)lr"),
+    "v_bias_correction_dropped": ("(float)(1.0 / sqrt(1.0 - pow(beta2, (double)t)))", "1.0f"),
+    "decay_sign_flipped": ("(float)(1.0 - lr * weight_decay)", "(float)(1.0 + lr * weight_decay)"),
+    "eps_inside_sqrt": ("sqrtf(v1) * inv_sqrt_bc2 + epsf", "sqrtf(v1 + epsf) * inv_sqrt_bc2"),
+    "v_uses_g_not_g2": ("c2 * (gi * gi)", "c2 * gi"),
+    "betas_swapped_in_m": ("b1 * m[i] + c1 * gi", "b2 * m[i] + c2 * gi"),
+    "clip_not_applied_to_g": ("float gi = g[i] * cf;", "float gi = g[i];"),
+    "decay_applied_to_update": ("p[i] * decay - step_size * (m1 / d)",
+                                "(p[i] - step_size * (m1 / d)) * decay * decay"),
     "ties_away_from_zero": ("nearbyint(units)", "round(units)"),
     "reduce_in_double": ("float acc = 0.0f;", "double acc = 0.0;"),
     "unscale_dropped": ("float gi = acc * inv_scale;", "float gi = acc;"),

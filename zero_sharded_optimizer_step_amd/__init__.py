@@ -1,0 +1,228 @@
+"""MI355X-native ZeRO sharded-optimizer step: Python binding.
+
+Every function here has the name of the C entry point it calls (see
+include/zero.h) and only marshals arguments: torch tensors become device
+pointers, the current torch stream becomes the hipStream_t, and negative
+status codes become ``ZeroError``.  All arithmetic of the step runs in the
+HIP kernels of libzero_mi355x.so; nothing here computes on the CPU.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+from . import _abi
+from ._abi import (ZERO_BF16, ZERO_EALIGN, ZERO_EDEVICE, ZERO_EINVAL, ZERO_ESIZE,
+                   ZERO_FP16, ZERO_MAX_REPLICAS, ZERO_OK, ZeroError, check, lib,
+                   zero_bucket_t, zero_global_t, zero_loss_scaler_t, zero_partition_t,
+                   zero_step_args, zero_step_info, zero_tensor_slot_t)
+
+__all__ = [
+    "ZERO_OK", "ZERO_EINVAL", "ZERO_EALIGN", "ZERO_ESIZE", "ZERO_EDEVICE",
+    "ZERO_FP16", "ZERO_BF16", "ZERO_MAX_REPLICAS", "ZeroError", "lib",
+    "zero_last_error", "zero_partition", "zero_partition_valid_numel",
+    "zero_bucket_plan", "zero_bucket_flatten", "zero_shard_workspace_bytes",
+    "zero_partials_bytes", "zero_shard_reduce", "zero_shard_combine",
+    "zero_shard_apply", "zero_shard_step", "zero_loss_scaler_init",
+    "zero_loss_scaler_update", "StepArgs", "dtype_code", "GLOBAL_BYTES",
+]
+
+GLOBAL_BYTES = ctypes.sizeof(zero_global_t)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(dtype) -> int:
+    """ZERO_FP16 / ZERO_BF16 for a torch dtype (or pass an int through)."""
+    if isinstance(dtype, int):
+        return dtype
+    torch = _torch()
+    if dtype == torch.float16:
+        return ZERO_FP16
+    if dtype == torch.bfloat16:
+        return ZERO_BF16
+    raise ValueError("only float16 and bfloat16 are supported, got %s" % dtype)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return _torch().cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+# ------------------------------------------------------------------ host only
+def zero_last_error() -> str:
+    return lib().zero_last_error().decode()
+
+
+def zero_partition(numel: int, world_size: int, alignment: int) -> zero_partition_t:
+    out = zero_partition_t()
+    check(lib().zero_partition(numel, world_size, alignment, ctypes.byref(out)),
+          "zero_partition")
+    return out
+
+
+def zero_partition_valid_numel(part: zero_partition_t, rank: int) -> int:
+    n = lib().zero_partition_valid_numel(ctypes.byref(part), rank)
+    if n < 0:
+        raise ValueError("rank %d outside the partition's world" % rank)
+    return n
+
+
+def zero_bucket_plan(tensor_numel: Sequence[int], reduce_bucket_size: int):
+    """Return (slots, buckets) as ctypes arrays of zero_tensor_slot_t and
+    zero_bucket_t."""
+    n = len(tensor_numel)
+    sizes = (_abi.i64 * max(n, 1))(*tensor_numel)
+    slots = (zero_tensor_slot_t * max(n, 1))()
+    nb = _abi.i32(0)
+    cap = 0
+    while True:
+        buckets = (zero_bucket_t * max(cap, 1))()
+        rc = lib().zero_bucket_plan(sizes, n, reduce_bucket_size, slots, buckets, cap,
+                                    ctypes.byref(nb))
+        if rc == ZERO_ESIZE and nb.value > cap:
+            cap = nb.value
+            continue
+        check(rc, "zero_bucket_plan")
+        break
+    return slots[:n], buckets[:nb.value]
+
+
+def zero_shard_workspace_bytes(shard_numel: int) -> int:
+    return lib().zero_shard_workspace_bytes(shard_numel)
+
+
+def zero_partials_bytes(n_slots: int) -> int:
+    return lib().zero_partials_bytes(n_slots)
+
+
+def zero_loss_scaler_init(initial_scale_power: int = 16, loss_scale_window: int = 100,
+                          hysteresis: int = 2, min_loss_scale: float = 1.0) -> zero_loss_scaler_t:
+    st = zero_loss_scaler_t()
+    check(lib().zero_loss_scaler_init(initial_scale_power, loss_scale_window, hysteresis,
+                                      min_loss_scale, ctypes.byref(st)),
+          "zero_loss_scaler_init")
+    return st
+
+
+def zero_loss_scaler_update(st: zero_loss_scaler_t, overflow: bool) -> bool:
+    """Advance the scaler by one step's overflow flag; True if skipped."""
+    skip = _abi.i32(0)
+    check(lib().zero_loss_scaler_update(ctypes.byref(st), 1 if overflow else 0,
+                                        ctypes.byref(skip)), "zero_loss_scaler_update")
+    return bool(skip.value)
+
+
+# --------------------------------------------------------------- device calls
+def zero_bucket_flatten(slots, srcs, dtype, flat, flat_numel: Optional[int] = None,
+                        stream=None) -> None:
+    """Copy tensors `srcs` (device) into `flat` at their slots' offsets and
+    zero [end of the last slot, flat_numel)."""
+    n = len(slots)
+    if len(srcs) != n:
+        raise ValueError("one source tensor per slot")
+    arr = (zero_tensor_slot_t * max(n, 1))(*slots)
+    ptrs = (_abi.vp * max(n, 1))(*[_dptr(s) for s in srcs])
+    if flat_numel is None:
+        flat_numel = flat.numel()
+    check(lib().zero_bucket_flatten(arr, n, ptrs, dtype_code(dtype), _dptr(flat), flat_numel,
+                                    _stream(stream)), "zero_bucket_flatten")
+
+
+@dataclass
+class StepArgs:
+    """Builds a zero_step_args from torch tensors and keeps the pointer
+    array it refers to alive.  `replica_grads` are the per-replica slices
+    that start at this rank's shard."""
+    world_size: int
+    rank: int
+    shard_numel: int
+    valid_numel: int
+    replica_grads: Sequence
+    master: object
+    exp_avg: object
+    exp_avg_sq: object
+    full_params: object
+    workspace: object
+    lr: float = 6e-5
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+    weight_decay: float = 0.01
+    step: int = 1
+    loss_scale: float = 1.0
+    grad_predivide: float = 1.0
+    max_grad_norm: float = 1.0
+    grad_dtype: Optional[int] = None
+    param_dtype: Optional[int] = None
+
+    def c_args(self) -> zero_step_args:
+        reps = list(self.replica_grads)
+        self._ptrs = (_abi.vp * max(len(reps), 1))(*[_dptr(r) for r in reps])
+        a = zero_step_args()
+        a.world_size = self.world_size
+        a.rank = self.rank
+        a.shard_numel = self.shard_numel
+        a.valid_numel = self.valid_numel
+        a.grad_dtype = dtype_code(self.grad_dtype if self.grad_dtype is not None else reps[0].dtype)
+        a.param_dtype = dtype_code(self.param_dtype if self.param_dtype is not None
+                                   else self.full_params.dtype)
+        a.n_replicas = len(reps)
+        a.replica_grad = ctypes.cast(self._ptrs, ctypes.POINTER(_abi.vp))
+        a.master = _dptr(self.master)
+        a.exp_avg = _dptr(self.exp_avg)
+        a.exp_avg_sq = _dptr(self.exp_avg_sq)
+        a.full_params = _dptr(self.full_params)
+        a.workspace = _dptr(self.workspace)
+        a.workspace_bytes = 0 if self.workspace is None else \
+            self.workspace.numel() * self.workspace.element_size()
+        a.lr, a.beta1, a.beta2, a.eps = self.lr, self.beta1, self.beta2, self.eps
+        a.weight_decay = self.weight_decay
+        a.step = self.step
+        a.loss_scale = self.loss_scale
+        a.grad_predivide = self.grad_predivide
+        a.max_grad_norm = self.max_grad_norm
+        self._c = a
+        return a
+
+
+def _args(a) -> zero_step_args:
+    return a.c_args() if isinstance(a, StepArgs) else a
+
+
+def zero_shard_reduce(args, slot: int, partials, stream=None) -> None:
+    check(lib().zero_shard_reduce(ctypes.byref(_args(args)), slot, _dptr(partials),
+                                  _stream(stream)), "zero_shard_reduce")
+
+
+def zero_shard_combine(partials, n_slots: int, max_grad_norm: float, global_buf,
+                       stream=None) -> None:
+    check(lib().zero_shard_combine(_dptr(partials), n_slots, max_grad_norm, _dptr(global_buf),
+                                   _stream(stream)), "zero_shard_combine")
+
+
+def zero_shard_apply(args, global_buf, stream=None) -> None:
+    check(lib().zero_shard_apply(ctypes.byref(_args(args)), _dptr(global_buf), _stream(stream)),
+          "zero_shard_apply")
+
+
+def zero_shard_step(args, peer_sumsq: float = 0.0, peer_overflow: bool = False,
+                    want_info: bool = False, stream=None) -> Optional[zero_step_info]:
+    """One rank's whole step.  With want_info the call waits for the stream
+    and returns the combine's result; otherwise it returns None at once."""
+    info = zero_step_info() if want_info else None
+    check(lib().zero_shard_step(ctypes.byref(_args(args)), peer_sumsq, 1 if peer_overflow else 0,
+                                ctypes.byref(info) if info is not None else None,
+                                _stream(stream)), "zero_shard_step")
+    return info

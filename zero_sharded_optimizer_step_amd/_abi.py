@@ -1,0 +1,119 @@
+"""ctypes mirror of include/zero.h and the loader of libzero_mi355x.so.
+
+Marshalling only: structures, argument types and the library handle.  The
+library is loaded from this package's directory; if it is not there the
+import of any entry point fails loudly (there is no fallback path).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libzero_mi355x.so")
+
+ZERO_OK = 0
+ZERO_EINVAL = -1
+ZERO_EALIGN = -2
+ZERO_ESIZE = -3
+ZERO_EDEVICE = -4
+ZERO_FP16 = 1
+ZERO_BF16 = 2
+ZERO_MAX_REPLICAS = 64
+
+i32, i64, f32, f64, vp, sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                              ctypes.c_double, ctypes.c_void_p, ctypes.c_size_t)
+
+
+class zero_partition_t(ctypes.Structure):
+    _fields_ = [("numel", i64), ("shard_numel", i64), ("padded_numel", i64),
+                ("world_size", i32), ("alignment", i32)]
+
+
+class zero_tensor_slot_t(ctypes.Structure):
+    _fields_ = [("offset", i64), ("numel", i64), ("bucket", i32), ("reserved", i32)]
+
+
+class zero_bucket_t(ctypes.Structure):
+    _fields_ = [("begin", i64), ("end", i64), ("first_tensor", i32), ("n_tensors", i32)]
+
+
+class zero_step_args(ctypes.Structure):
+    _fields_ = [("world_size", i32), ("rank", i32), ("shard_numel", i64),
+                ("valid_numel", i64), ("grad_dtype", i32), ("param_dtype", i32),
+                ("n_replicas", i32), ("reserved0", i32),
+                ("replica_grad", ctypes.POINTER(vp)),
+                ("master", vp), ("exp_avg", vp), ("exp_avg_sq", vp),
+                ("full_params", vp), ("workspace", vp), ("workspace_bytes", sz),
+                ("lr", f64), ("beta1", f64), ("beta2", f64), ("eps", f64),
+                ("weight_decay", f64), ("step", i64), ("loss_scale", f64),
+                ("grad_predivide", f64), ("max_grad_norm", f64)]
+
+
+class zero_global_t(ctypes.Structure):
+    _fields_ = [("sumsq", f64), ("norm", f64), ("coef", f32), ("overflow", i32),
+                ("clipped", i32), ("reserved", i32)]
+
+
+zero_step_info = zero_global_t
+
+
+class zero_loss_scaler_t(ctypes.Structure):
+    _fields_ = [("scale", f64), ("min_scale", f64), ("good_steps", i32),
+                ("hysteresis_left", i32), ("window", i32), ("hysteresis", i32)]
+
+
+_PROTOTYPES = {
+    "zero_last_error": (ctypes.c_char_p, []),
+    "zero_partition": (ctypes.c_int, [i64, i32, i32, ctypes.POINTER(zero_partition_t)]),
+    "zero_partition_valid_numel": (i64, [ctypes.POINTER(zero_partition_t), i32]),
+    "zero_bucket_plan": (ctypes.c_int, [ctypes.POINTER(i64), i32, i64,
+                                        ctypes.POINTER(zero_tensor_slot_t),
+                                        ctypes.POINTER(zero_bucket_t), i32,
+                                        ctypes.POINTER(i32)]),
+    "zero_bucket_flatten": (ctypes.c_int, [ctypes.POINTER(zero_tensor_slot_t), i32,
+                                           ctypes.POINTER(vp), i32, vp, i64, vp]),
+    "zero_shard_workspace_bytes": (sz, [i64]),
+    "zero_partials_bytes": (sz, [i32]),
+    "zero_shard_reduce": (ctypes.c_int, [ctypes.POINTER(zero_step_args), i32, vp, vp]),
+    "zero_shard_combine": (ctypes.c_int, [vp, i32, f64, vp, vp]),
+    "zero_shard_apply": (ctypes.c_int, [ctypes.POINTER(zero_step_args), vp, vp]),
+    "zero_shard_step": (ctypes.c_int, [ctypes.POINTER(zero_step_args), f64, i32,
+                                       ctypes.POINTER(zero_step_info), vp]),
+    "zero_loss_scaler_init": (ctypes.c_int, [i32, i32, i32, f64,
+                                             ctypes.POINTER(zero_loss_scaler_t)]),
+    "zero_loss_scaler_update": (ctypes.c_int, [ctypes.POINTER(zero_loss_scaler_t), i32,
+                                               ctypes.POINTER(i32)]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                "libzero_mi355x.so is not built (expected at %s); run "
+                "`python -m zero_sharded_optimizer_step_amd.build`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _PROTOTYPES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+class ZeroError(RuntimeError):
+    """A library call returned a negative ZERO_E* status."""
+
+    def __init__(self, code: int, where: str, message: str):
+        super().__init__("%s failed with %d: %s" % (where, code, message))
+        self.code = code
+
+
+def check(code: int, where: str) -> None:
+    if code != ZERO_OK:
+        raise ZeroError(code, where, lib().zero_last_error().decode())

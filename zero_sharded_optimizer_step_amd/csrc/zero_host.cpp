@@ -1,0 +1,221 @@
+// zero_host.cpp -- host-only parts of the library: errors, partition, bucket
+// plan, loss scaler and argument checks.  No HIP calls in this file, so these
+// entry points work on a machine without a GPU.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+
+#include "zero_internal.h"
+
+namespace zero {
+
+static thread_local char g_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_error, sizeof g_error, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+void clear_error() { g_error[0] = '\0'; }
+
+int reduce_blocks_for(int64_t valid_numel) {
+    int64_t vecs = (valid_numel + kVec - 1) / kVec;
+    int64_t blocks = (vecs + kReduceThreads - 1) / kReduceThreads;
+    if (blocks < 1) blocks = 1;
+    if (blocks > kMaxReduceBlocks) blocks = kMaxReduceBlocks;
+    return static_cast<int>(blocks);
+}
+
+static bool finite_positive(double x) { return std::isfinite(x) && x > 0.0; }
+
+int validate_step_args(const zero_step_args* a) {
+    if (!a) return fail(ZERO_EINVAL, "args is NULL");
+    if (a->world_size < 1) return fail(ZERO_EINVAL, "world_size %d < 1", a->world_size);
+    if (a->rank < 0 || a->rank >= a->world_size)
+        return fail(ZERO_EINVAL, "rank %d outside [0, %d)", a->rank, a->world_size);
+    if (a->shard_numel < 0 || a->shard_numel % kVec != 0)
+        return fail(ZERO_EINVAL, "shard_numel %lld must be a non-negative multiple of 8",
+                    (long long)a->shard_numel);
+    if (a->valid_numel < 0 || a->valid_numel > a->shard_numel)
+        return fail(ZERO_EINVAL, "valid_numel %lld outside [0, shard_numel=%lld]",
+                    (long long)a->valid_numel, (long long)a->shard_numel);
+    if (a->grad_dtype != ZERO_FP16 && a->grad_dtype != ZERO_BF16)
+        return fail(ZERO_EINVAL, "grad_dtype %d is not ZERO_FP16 or ZERO_BF16", a->grad_dtype);
+    if (a->param_dtype != ZERO_FP16 && a->param_dtype != ZERO_BF16)
+        return fail(ZERO_EINVAL, "param_dtype %d is not ZERO_FP16 or ZERO_BF16", a->param_dtype);
+    if (a->n_replicas < 1 || a->n_replicas > ZERO_MAX_REPLICAS)
+        return fail(ZERO_EINVAL, "n_replicas %d outside [1, %d]", a->n_replicas,
+                    ZERO_MAX_REPLICAS);
+    if (a->step < 1) return fail(ZERO_EINVAL, "step %lld < 1", (long long)a->step);
+    if (!finite_positive(a->loss_scale))
+        return fail(ZERO_EINVAL, "loss_scale must be finite and > 0");
+    if (!finite_positive(a->grad_predivide))
+        return fail(ZERO_EINVAL, "grad_predivide must be finite and > 0");
+    if (!std::isfinite(a->lr) || a->lr < 0.0) return fail(ZERO_EINVAL, "lr must be finite and >= 0");
+    if (!(a->beta1 >= 0.0 && a->beta1 < 1.0)) return fail(ZERO_EINVAL, "beta1 outside [0, 1)");
+    if (!(a->beta2 >= 0.0 && a->beta2 < 1.0)) return fail(ZERO_EINVAL, "beta2 outside [0, 1)");
+    if (!finite_positive(a->eps)) return fail(ZERO_EINVAL, "eps must be finite and > 0");
+    if (!std::isfinite(a->weight_decay)) return fail(ZERO_EINVAL, "weight_decay must be finite");
+    if (std::isnan(a->max_grad_norm)) return fail(ZERO_EINVAL, "max_grad_norm is NaN");
+    if (!a->workspace) return fail(ZERO_EINVAL, "workspace is NULL");
+    if (!aligned16(a->workspace)) return fail(ZERO_EALIGN, "workspace is not 16-byte aligned");
+    // A rank with no real elements reads and writes no element, so its data
+    // pointers may be NULL (empty tensors).
+    if (a->valid_numel > 0) {
+        if (!a->replica_grad || !a->master || !a->exp_avg || !a->exp_avg_sq || !a->full_params)
+            return fail(ZERO_EINVAL, "a required pointer is NULL");
+        for (int i = 0; i < a->n_replicas; ++i) {
+            if (!a->replica_grad[i]) return fail(ZERO_EINVAL, "replica_grad[%d] is NULL", i);
+            if (!aligned16(a->replica_grad[i]))
+                return fail(ZERO_EALIGN, "replica_grad[%d] is not 16-byte aligned", i);
+        }
+        if (!aligned16(a->master) || !aligned16(a->exp_avg) || !aligned16(a->exp_avg_sq) ||
+            !aligned16(a->full_params))
+            return fail(ZERO_EALIGN, "a state or parameter pointer is not 16-byte aligned");
+    }
+    // Start of this rank's slice of the full buffer: shard_numel is a
+    // multiple of 8, so 2-byte elements keep 16-byte alignment.
+    if (a->workspace_bytes < zero_shard_workspace_bytes(a->shard_numel))
+        return fail(ZERO_ESIZE, "workspace_bytes %zu < %zu needed", a->workspace_bytes,
+                    zero_shard_workspace_bytes(a->shard_numel));
+    return ZERO_OK;
+}
+
+}  // namespace zero
+
+using namespace zero;
+
+extern "C" {
+
+const char* zero_last_error(void) { return g_error; }
+
+int zero_partition(int64_t numel, int32_t world_size, int32_t alignment,
+                   zero_partition_t* out) {
+    clear_error();
+    if (!out) return fail(ZERO_EINVAL, "out is NULL");
+    if (numel < 0) return fail(ZERO_EINVAL, "numel %lld < 0", (long long)numel);
+    if (world_size < 1) return fail(ZERO_EINVAL, "world_size %d < 1", world_size);
+    if (alignment < 1 || (alignment & (alignment - 1)) != 0)
+        return fail(ZERO_EINVAL, "alignment %d is not a power of two", alignment);
+    // One aligned unit is world_size * alignment elements of the flat space;
+    // every rank gets the same number of units.
+    const int64_t unit = static_cast<int64_t>(world_size) * alignment;
+    const int64_t units = numel / unit + (numel % unit ? 1 : 0);
+    out->numel = numel;
+    out->shard_numel = units * alignment;
+    out->padded_numel = out->shard_numel * world_size;
+    out->world_size = world_size;
+    out->alignment = alignment;
+    return ZERO_OK;
+}
+
+int64_t zero_partition_valid_numel(const zero_partition_t* p, int32_t rank) {
+    if (!p || rank < 0 || rank >= p->world_size) return -1;
+    const int64_t begin = static_cast<int64_t>(rank) * p->shard_numel;
+    if (begin >= p->numel) return 0;
+    const int64_t left = p->numel - begin;
+    return left < p->shard_numel ? left : p->shard_numel;
+}
+
+int zero_bucket_plan(const int64_t* tensor_numel, int32_t n_tensors,
+                     int64_t reduce_bucket_size, zero_tensor_slot_t* slots,
+                     zero_bucket_t* buckets, int32_t bucket_cap, int32_t* n_buckets) {
+    clear_error();
+    if (n_tensors < 0) return fail(ZERO_EINVAL, "n_tensors %d < 0", n_tensors);
+    if (reduce_bucket_size < 1)
+        return fail(ZERO_EINVAL, "reduce_bucket_size %lld < 1", (long long)reduce_bucket_size);
+    if (!n_buckets || (n_tensors > 0 && (!tensor_numel || !slots)) || bucket_cap < 0 ||
+        (bucket_cap > 0 && !buckets))
+        return fail(ZERO_EINVAL, "a required pointer is NULL or bucket_cap < 0");
+    for (int32_t t = 0; t < n_tensors; ++t)
+        if (tensor_numel[t] < 0)
+            return fail(ZERO_EINVAL, "tensor_numel[%d] = %lld < 0", t, (long long)tensor_numel[t]);
+
+    int32_t count = 0;         // buckets opened so far
+    int64_t cursor = 0;        // flat offset of the next tensor
+    int64_t open_begin = 0;    // flat start of the open bucket
+    int32_t open_first = 0;    // first tensor of the open bucket
+    auto close_bucket = [&](int32_t end_tensor) {
+        if (count >= 1 && count <= bucket_cap) {
+            zero_bucket_t& b = buckets[count - 1];
+            b.begin = open_begin;
+            b.end = cursor;
+            b.first_tensor = open_first;
+            b.n_tensors = end_tensor - open_first;
+        }
+    };
+    for (int32_t t = 0; t < n_tensors; ++t) {
+        const int64_t n = tensor_numel[t];
+        // A new bucket starts at the first tensor, and whenever the open
+        // bucket already holds elements and this tensor would push it past
+        // the bucket size.  An oversize tensor therefore sits alone.
+        const bool holds_elements = cursor > open_begin;
+        if (count == 0 || (holds_elements && (cursor - open_begin) + n > reduce_bucket_size)) {
+            close_bucket(t);
+            open_begin = cursor;
+            open_first = t;
+            ++count;
+        }
+        slots[t].offset = cursor;
+        slots[t].numel = n;
+        slots[t].bucket = count - 1;
+        slots[t].reserved = 0;
+        cursor += n;
+    }
+    close_bucket(n_tensors);
+    *n_buckets = count;
+    if (count > bucket_cap)
+        return fail(ZERO_ESIZE, "plan needs %d buckets, capacity is %d", count, bucket_cap);
+    return ZERO_OK;
+}
+
+int zero_loss_scaler_init(int32_t initial_scale_power, int32_t loss_scale_window,
+                          int32_t hysteresis, double min_loss_scale,
+                          zero_loss_scaler_t* st) {
+    clear_error();
+    if (!st) return fail(ZERO_EINVAL, "st is NULL");
+    if (loss_scale_window < 1) return fail(ZERO_EINVAL, "loss_scale_window %d < 1", loss_scale_window);
+    if (hysteresis < 1) return fail(ZERO_EINVAL, "hysteresis %d < 1", hysteresis);
+    if (!finite_positive(min_loss_scale)) return fail(ZERO_EINVAL, "min_loss_scale must be > 0");
+    if (initial_scale_power < -126 || initial_scale_power > 127)
+        return fail(ZERO_EINVAL, "initial_scale_power %d outside [-126, 127]", initial_scale_power);
+    st->scale = std::ldexp(1.0, initial_scale_power);
+    st->min_scale = min_loss_scale;
+    st->good_steps = 0;
+    st->hysteresis_left = hysteresis;
+    st->window = loss_scale_window;
+    st->hysteresis = hysteresis;
+    return ZERO_OK;
+}
+
+int zero_loss_scaler_update(zero_loss_scaler_t* st, int32_t overflow, int32_t* skip_step) {
+    clear_error();
+    if (!st || !skip_step) return fail(ZERO_EINVAL, "st or skip_step is NULL");
+    if (st->window < 1 || st->hysteresis < 1 || !finite_positive(st->min_scale))
+        return fail(ZERO_EINVAL, "scaler state was not initialised");
+    if (overflow) {
+        // The step is dropped.  Hysteresis absorbs isolated overflows;
+        // once spent, every overflow halves the scale down to the floor.
+        *skip_step = 1;
+        st->good_steps = 0;
+        if (st->hysteresis_left > 1) {
+            st->hysteresis_left -= 1;
+        } else {
+            const double half = st->scale * 0.5;
+            st->scale = half < st->min_scale ? st->min_scale : half;
+        }
+        return ZERO_OK;
+    }
+    *skip_step = 0;
+    if (++st->good_steps >= st->window) {
+        st->scale *= 2.0;
+        st->good_steps = 0;
+        st->hysteresis_left = st->hysteresis;
+    }
+    return ZERO_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,589 @@
+// zero_kernels.hip -- gfx950 kernels of the ZeRO sharded-optimizer step and
+// the ABI entry points that launch them.
+//
+// The step is HBM-bound (about 50 bytes moved and ~25 flops per shard element
+// at 8 replicas), so the kernels are built around streaming: every thread
+// moves 8 elements per iteration with 16-byte vector loads and stores, a grid
+// of at most 2048 blocks strides over the shard, and reductions stay in
+// registers until one wavefront-shuffle + LDS step per block.  Nothing here
+// is a dense contraction, so there is no MFMA.
+//
+// Sources (cited by title and section):
+//   [P1] "ZeRO技术解析：大模型分布式训练的革命性突破"
+//   [P3] "ZeRO 和分片优化器"
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "zero_internal.h"
+
+namespace zero {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+struct ReplicaPtrs {
+    const u32x4* p[ZERO_MAX_REPLICAS];
+};
+
+// ---------------------------------------------------------------- formats
+// bf16 is the upper half of an fp32; fp16 goes through the hardware convert,
+// which is exact (every fp16 value, subnormals included, is an fp32 value).
+template <int DT>
+__device__ __forceinline__ float lo_to_f32(unsigned w) {
+    if constexpr (DT == ZERO_BF16) return __uint_as_float(w << 16);
+    else return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(w & 0xffffu)));
+}
+template <int DT>
+__device__ __forceinline__ float hi_to_f32(unsigned w) {
+    if constexpr (DT == ZERO_BF16) return __uint_as_float(w & 0xffff0000u);
+    else return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(w >> 16)));
+}
+template <int DT>
+__device__ __forceinline__ void decode8(const u32x4 v, float o[8]) {
+    o[0] = lo_to_f32<DT>(v.x); o[1] = hi_to_f32<DT>(v.x);
+    o[2] = lo_to_f32<DT>(v.y); o[3] = hi_to_f32<DT>(v.y);
+    o[4] = lo_to_f32<DT>(v.z); o[5] = hi_to_f32<DT>(v.z);
+    o[6] = lo_to_f32<DT>(v.w); o[7] = hi_to_f32<DT>(v.w);
+}
+template <int DT>
+__device__ __forceinline__ float scalar_to_f32(unsigned short h) {
+    return lo_to_f32<DT>(h);
+}
+
+// Round to nearest even with the gfx950 packed converts (v_cvt_pk_bf16_f32,
+// v_cvt_pk_f16_f32).
+template <int DT>
+__device__ __forceinline__ unsigned pack2(float a, float b) {
+    f32x2 v = {a, b};
+    if constexpr (DT == ZERO_BF16) return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
+    else return __builtin_bit_cast(unsigned, __builtin_convertvector(v, f16x2));
+}
+template <int DT>
+__device__ __forceinline__ unsigned short pack1(float a) {
+    return static_cast<unsigned short>(pack2<DT>(a, 0.0f) & 0xffffu);
+}
+
+__device__ __forceinline__ bool finite(float x) { return __builtin_isfinite(x); }
+
+// ------------------------------------------------------- block reduction
+// Fixed shuffle pattern and fixed wave order: the block's result depends
+// only on which values its threads hold, never on timing.
+__device__ __forceinline__ void block_reduce(double& ss, int& bad, double* s_ss, int* s_bad) {
+    #pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        ss += __shfl_xor(ss, off, 64);
+        bad |= __shfl_xor(bad, off, 64);
+    }
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (lane == 0) { s_ss[wave] = ss; s_bad[wave] = bad; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int waves = blockDim.x >> 6;
+        ss = s_ss[0];
+        bad = s_bad[0];
+        for (int w = 1; w < waves; ++w) { ss += s_ss[w]; bad |= s_bad[w]; }
+    }
+}
+
+// ============================================================ pass 1: reduce
+// [P1] §2.1 / [P3] technical insight: the reduce-scatter leaves each rank the
+// sum of all replicas' gradients over its own shard.  Here the replicas sit
+// in one HBM and the sum is an fp32 running sum in replica order; the loss
+// scale ([P1] §3.3, §5.1) is undone by one multiply; the inf/nan flag and
+// the fp64 sum of squares for clipping ([P1] §6) ride along in registers.
+template <int DT, int NR>
+__global__ __launch_bounds__(kReduceThreads) void reduce_kernel(
+    ReplicaPtrs reps, int nrep, int64_t nvec, int64_t n_valid, float inv_scale,
+    f32x4* __restrict__ g, Partial* __restrict__ partials, SlotHeader* __restrict__ header) {
+    double ss = 0.0;
+    int bad = 0;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kReduceThreads;
+    for (int64_t v = static_cast<int64_t>(blockIdx.x) * kReduceThreads + threadIdx.x; v < nvec;
+         v += stride) {
+        float acc[8];
+        if constexpr (NR > 0) {
+            u32x4 x[NR];
+            #pragma unroll
+            for (int r = 0; r < NR; ++r) x[r] = reps.p[r][v];
+            decode8<DT>(x[0], acc);
+            #pragma unroll
+            for (int r = 1; r < NR; ++r) {
+                float y[8];
+                decode8<DT>(x[r], y);
+                #pragma unroll
+                for (int k = 0; k < 8; ++k) acc[k] = acc[k] + y[k];
+            }
+        } else {
+            decode8<DT>(reps.p[0][v], acc);
+            for (int r = 1; r < nrep; ++r) {
+                float y[8];
+                decode8<DT>(reps.p[r][v], y);
+                #pragma unroll
+                for (int k = 0; k < 8; ++k) acc[k] = acc[k] + y[k];
+            }
+        }
+        f32x4 o0, o1;
+        #pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float gk = acc[k] * inv_scale;
+            bad |= !finite(gk);
+            ss += static_cast<double>(gk) * static_cast<double>(gk);
+            if (k < 4) o0[k] = gk; else o1[k - 4] = gk;
+        }
+        g[2 * v] = o0;
+        g[2 * v + 1] = o1;
+    }
+    // Ragged tail (fewer than 8 elements): block 0, one element per thread.
+    const int64_t tail0 = nvec * kVec;
+    if (blockIdx.x == 0 && tail0 + threadIdx.x < n_valid) {
+        const int64_t i = tail0 + threadIdx.x;
+        float acc = 0.0f;
+        for (int r = 0; r < nrep; ++r) {
+            const unsigned short* base = reinterpret_cast<const unsigned short*>(reps.p[r]);
+            const float x = scalar_to_f32<DT>(base[i]);
+            acc = (r == 0) ? x : acc + x;
+        }
+        const float gi = acc * inv_scale;
+        bad |= !finite(gi);
+        ss += static_cast<double>(gi) * static_cast<double>(gi);
+        reinterpret_cast<float*>(g)[i] = gi;
+    }
+    __shared__ double s_ss[kReduceThreads / 64];
+    __shared__ int s_bad[kReduceThreads / 64];
+    block_reduce(ss, bad, s_ss, s_bad);
+    if (threadIdx.x == 0) {
+        partials[blockIdx.x].sumsq = ss;
+        partials[blockIdx.x].flag = bad;
+        partials[blockIdx.x].pad = 0;
+        if (blockIdx.x == 0) header->n_blocks = static_cast<int32_t>(gridDim.x);
+    }
+}
+
+// =========================================================== combine (tiny)
+// The implied all-reduce of 16 bytes per rank: global sum of squares, norm,
+// clip factor ([P1] §6 gradient_clipping) and the OR of the overflow flags.
+constexpr int kCombineThreads = 256;
+
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(
+    const unsigned char* __restrict__ partials, int n_slots, double peer_sumsq, int peer_overflow,
+    double max_norm, zero_global_t* __restrict__ out) {
+    double ss = 0.0;
+    int bad = 0;
+    for (int s = 0; s < n_slots; ++s) {
+        const SlotHeader* h = reinterpret_cast<const SlotHeader*>(partials + static_cast<size_t>(s) * kSlotBytes);
+        int nb = h->n_blocks;
+        nb = nb < 0 ? 0 : (nb > kMaxReduceBlocks ? kMaxReduceBlocks : nb);
+        const Partial* p = reinterpret_cast<const Partial*>(h + 1);
+        for (int b = threadIdx.x; b < nb; b += kCombineThreads) {
+            ss += p[b].sumsq;
+            bad |= p[b].flag;
+        }
+    }
+    __shared__ double s_ss[kCombineThreads / 64];
+    __shared__ int s_bad[kCombineThreads / 64];
+    block_reduce(ss, bad, s_ss, s_bad);
+    if (threadIdx.x == 0) {
+        ss += peer_sumsq;
+        bad |= peer_overflow;
+        const double norm = sqrt(ss);
+        const double c = max_norm / (norm + 1e-6);
+        const int clipped = (max_norm > 0.0 && c < 1.0) ? 1 : 0;
+        out->sumsq = ss;
+        out->norm = norm;
+        out->coef = clipped ? static_cast<float>(c) : 1.0f;
+        out->overflow = (bad || !__builtin_isfinite(ss)) ? 1 : 0;
+        out->clipped = clipped;
+        out->reserved = 0;
+    }
+}
+
+// ============================================================ pass 2: apply
+// AdamW ([P1] §3.1) on the rank's fp32 masters and moments ([P3] FAQ), only
+// when no replica overflowed, then the cast of the new masters into the
+// rank's slice of the full low-precision buffer ([P1] §2.1 all-gather).
+struct AdamConsts {
+    float decay;          // 1 - lr * wd
+    float b1, c1;         // beta1, 1 - beta1
+    float b2, c2;         // beta2, 1 - beta2
+    float step_size;      // lr / (1 - beta1^t)
+    float inv_sqrt_bc2;   // 1 / sqrt(1 - beta2^t)
+    float eps;
+};
+
+// One element, in fp32 with one rounding per operation (no contraction):
+//   m' = b1 m + c1 g;  v' = b2 v + c2 g^2;  d = sqrt(v') / sqrt(1 - b2^t) + eps;
+//   p' = p (1 - lr wd) - lr / (1 - b1^t) * m' / d.
+__device__ __forceinline__ void adamw1(float g, float& p, float& m, float& v, const AdamConsts& k) {
+    m = k.b1 * m + k.c1 * g;
+    v = k.b2 * v + k.c2 * (g * g);
+    const float d = __builtin_sqrtf(v) * k.inv_sqrt_bc2 + k.eps;
+    p = p * k.decay - k.step_size * (m / d);
+}
+
+template <int PT>
+__global__ __launch_bounds__(kReduceThreads) void apply_kernel(
+    const f32x4* __restrict__ g, f32x4* __restrict__ p, f32x4* __restrict__ m, f32x4* __restrict__ v,
+    u32x4* __restrict__ out, int64_t nvec, int64_t n_valid, const zero_global_t* __restrict__ glob,
+    AdamConsts k) {
+    if (glob->overflow) return;                    // skipped step: touch nothing
+    const float coef = glob->coef;
+    const bool clip = glob->clipped != 0;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kReduceThreads;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kReduceThreads + threadIdx.x; i < nvec;
+         i += stride) {
+        f32x4 g0 = g[2 * i], g1 = g[2 * i + 1];
+        f32x4 p0 = p[2 * i], p1 = p[2 * i + 1];
+        f32x4 m0 = m[2 * i], m1 = m[2 * i + 1];
+        f32x4 v0 = v[2 * i], v1 = v[2 * i + 1];
+        if (clip) { g0 *= coef; g1 *= coef; }
+        #pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float pe = p0[e], me = m0[e], ve = v0[e];
+            adamw1(g0[e], pe, me, ve, k);
+            p0[e] = pe; m0[e] = me; v0[e] = ve;
+            pe = p1[e]; me = m1[e]; ve = v1[e];
+            adamw1(g1[e], pe, me, ve, k);
+            p1[e] = pe; m1[e] = me; v1[e] = ve;
+        }
+        p[2 * i] = p0; p[2 * i + 1] = p1;
+        m[2 * i] = m0; m[2 * i + 1] = m1;
+        v[2 * i] = v0; v[2 * i + 1] = v1;
+        u32x4 o;
+        o.x = pack2<PT>(p0.x, p0.y);
+        o.y = pack2<PT>(p0.z, p0.w);
+        o.z = pack2<PT>(p1.x, p1.y);
+        o.w = pack2<PT>(p1.z, p1.w);
+        out[i] = o;
+    }
+    const int64_t tail0 = nvec * kVec;
+    if (blockIdx.x == 0 && tail0 + threadIdx.x < n_valid) {
+        const int64_t j = tail0 + threadIdx.x;
+        const float* gs = reinterpret_cast<const float*>(g);
+        float* ps = reinterpret_cast<float*>(p);
+        float* ms = reinterpret_cast<float*>(m);
+        float* vs = reinterpret_cast<float*>(v);
+        float gj = gs[j];
+        if (clip) gj *= coef;
+        float pj = ps[j], mj = ms[j], vj = vs[j];
+        adamw1(gj, pj, mj, vj, k);
+        ps[j] = pj; ms[j] = mj; vs[j] = vj;
+        reinterpret_cast<unsigned short*>(out)[j] = pack1<PT>(pj);
+    }
+}
+
+// ================================================================ flatten
+// contiguous_gradients ([P1] §5.2): one replica's tensors are copied end to
+// end into its flat buffer, then the padding is zeroed.  Each destination
+// vector of 8 elements is written with one aligned 16-byte store; the source
+// side is read as aligned 16-byte vectors and shifted into place, so a
+// tensor's arbitrary offset costs no unaligned accesses.  The few elements
+// before the first and after the last aligned vector of a tensor are copied
+// one by one.
+constexpr int kFlatBatch = 128;       // tensors per launch (kernel arguments)
+constexpr int kFlatThreads = 256;
+constexpr int kFlatVecPerThread = 4;
+constexpr int64_t kFlatVecPerBlock = kFlatThreads * kFlatVecPerThread;
+constexpr int64_t kFlatMaxBlocksPerTensor = 65536;
+
+struct FlatBatch {
+    const unsigned short* src[kFlatBatch];   // nullptr: write zeros
+    int64_t dst[kFlatBatch];                 // first flat element
+    int64_t n[kFlatBatch];
+    int32_t first_block[kFlatBatch + 1];
+    int32_t count;
+};
+
+// Elements k..k+7 of the 16 packed in (lo, hi), k uniform in 1..7.
+__device__ __forceinline__ u32x4 shift_pick(const u32x4 lo, const u32x4 hi, int k) {
+    const unsigned w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    u32x4 o;
+#define ZERO_PICK_EVEN(K) o.x = w[K / 2]; o.y = w[K / 2 + 1]; o.z = w[K / 2 + 2]; o.w = w[K / 2 + 3];
+#define ZERO_PICK_ODD(K)                                              \
+    o.x = __builtin_amdgcn_alignbyte(w[(K + 1) / 2], w[(K - 1) / 2], 2);     \
+    o.y = __builtin_amdgcn_alignbyte(w[(K + 1) / 2 + 1], w[(K - 1) / 2 + 1], 2); \
+    o.z = __builtin_amdgcn_alignbyte(w[(K + 1) / 2 + 2], w[(K - 1) / 2 + 2], 2); \
+    o.w = __builtin_amdgcn_alignbyte(w[(K + 1) / 2 + 3], w[(K - 1) / 2 + 3], 2);
+    switch (k) {
+        case 1: ZERO_PICK_ODD(1) break;
+        case 2: ZERO_PICK_EVEN(2) break;
+        case 3: ZERO_PICK_ODD(3) break;
+        case 4: ZERO_PICK_EVEN(4) break;
+        case 5: ZERO_PICK_ODD(5) break;
+        case 6: ZERO_PICK_EVEN(6) break;
+        default: ZERO_PICK_ODD(7) break;
+    }
+#undef ZERO_PICK_EVEN
+#undef ZERO_PICK_ODD
+    return o;
+}
+
+__global__ __launch_bounds__(kFlatThreads) void flatten_kernel(FlatBatch b, unsigned short* __restrict__ flat) {
+    // Which tensor owns this block: binary search over the block prefix.
+    int lo = 0, hi = b.count - 1;
+    const int bid = static_cast<int>(blockIdx.x);
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (b.first_block[mid] <= bid) lo = mid; else hi = mid - 1;
+    }
+    const int t = lo;
+    const int jb = bid - b.first_block[t];
+    const int nblk = b.first_block[t + 1] - b.first_block[t];
+    const unsigned short* src = b.src[t];
+    const int64_t d0 = b.dst[t], n = b.n[t], d1 = d0 + n;
+    // Aligned body [a0, a1) of the destination, head [d0, a0), tail [a1, d1).
+    int64_t a0 = (d0 + 7) & ~int64_t(7);
+    if (a0 > d1) a0 = d1;
+    int64_t a1 = d1 & ~int64_t(7);
+    if (a1 < a0) a1 = a0;
+    u32x4* dvec = reinterpret_cast<u32x4*>(flat);
+    const int64_t nv = (a1 - a0) / 8;
+    if (src == nullptr) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        for (int64_t q = static_cast<int64_t>(jb) * kFlatThreads + threadIdx.x; q < nv;
+             q += static_cast<int64_t>(nblk) * kFlatThreads)
+            dvec[a0 / 8 + q] = z;
+        if (jb == 0) {
+            if (threadIdx.x < a0 - d0) flat[d0 + threadIdx.x] = 0;
+            if (threadIdx.x >= 8 && threadIdx.x - 8 < d1 - a1) flat[a1 + threadIdx.x - 8] = 0;
+        }
+        return;
+    }
+    // Source element s of the tensor sits at aligned-vector element
+    // s + ms of `sbase`; the body's first source element is a0 - d0.
+    const int ms = static_cast<int>((reinterpret_cast<uintptr_t>(src) & 15u) >> 1);
+    const u32x4* sbase = reinterpret_cast<const u32x4*>(src - ms);
+    const int64_t s0 = a0 - d0 + ms;        // aligned-space index of body start
+    const int k = static_cast<int>(s0 & 7);
+    const int64_t sv0 = s0 >> 3;            // aligned vector holding it
+    for (int64_t q = static_cast<int64_t>(jb) * kFlatThreads + threadIdx.x; q < nv;
+         q += static_cast<int64_t>(nblk) * kFlatThreads) {
+        u32x4 o;
+        if (k == 0) {
+            o = sbase[sv0 + q];
+        } else {
+            o = shift_pick(sbase[sv0 + q], sbase[sv0 + q + 1], k);
+        }
+        dvec[a0 / 8 + q] = o;
+    }
+    if (jb == 0) {
+        if (threadIdx.x < a0 - d0) flat[d0 + threadIdx.x] = src[threadIdx.x];
+        if (threadIdx.x >= 8 && threadIdx.x - 8 < d1 - a1) {
+            const int64_t e = a1 + threadIdx.x - 8;
+            flat[e] = src[e - d0];
+        }
+    }
+}
+
+// ================================================================ launches
+int launch_error(const char* what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(ZERO_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+    return ZERO_OK;
+}
+
+template <int DT>
+void launch_reduce_dt(const ReplicaPtrs& reps, int nrep, int64_t n_valid, float inv, float* g,
+                      unsigned char* slot, hipStream_t st) {
+    const int blocks = reduce_blocks_for(n_valid);
+    const int64_t nvec = n_valid / kVec;
+    SlotHeader* h = reinterpret_cast<SlotHeader*>(slot);
+    Partial* parts = reinterpret_cast<Partial*>(h + 1);
+    f32x4* gv = reinterpret_cast<f32x4*>(g);
+#define ZERO_REDUCE_CASE(NR)                                                                     \
+    case NR:                                                                                     \
+        hipLaunchKernelGGL((reduce_kernel<DT, NR>), dim3(blocks), dim3(kReduceThreads), 0, st, reps, \
+                           nrep, nvec, n_valid, inv, gv, parts, h);                              \
+        break;
+    switch (nrep) {
+        ZERO_REDUCE_CASE(1) ZERO_REDUCE_CASE(2) ZERO_REDUCE_CASE(3) ZERO_REDUCE_CASE(4)
+        ZERO_REDUCE_CASE(5) ZERO_REDUCE_CASE(6) ZERO_REDUCE_CASE(7) ZERO_REDUCE_CASE(8)
+        default:
+            hipLaunchKernelGGL((reduce_kernel<DT, 0>), dim3(blocks), dim3(kReduceThreads), 0, st, reps,
+                               nrep, nvec, n_valid, inv, gv, parts, h);
+    }
+#undef ZERO_REDUCE_CASE
+}
+
+int launch_reduce(const zero_step_args* a, unsigned char* slot, hipStream_t st) {
+    ReplicaPtrs reps;
+    for (int r = 0; r < ZERO_MAX_REPLICAS; ++r)
+        reps.p[r] = r < a->n_replicas ? static_cast<const u32x4*>(a->replica_grad[r]) : nullptr;
+    const float inv = static_cast<float>(1.0 / (a->loss_scale * a->grad_predivide));
+    float* g = static_cast<float*>(a->workspace);
+    if (a->grad_dtype == ZERO_BF16)
+        launch_reduce_dt<ZERO_BF16>(reps, a->n_replicas, a->valid_numel, inv, g, slot, st);
+    else
+        launch_reduce_dt<ZERO_FP16>(reps, a->n_replicas, a->valid_numel, inv, g, slot, st);
+    return launch_error("reduce kernel launch");
+}
+
+int launch_combine(const void* partials, int n_slots, double peer_ss, int peer_of, double max_norm,
+                   void* global, hipStream_t st) {
+    hipLaunchKernelGGL(combine_kernel, dim3(1), dim3(kCombineThreads), 0, st,
+                       static_cast<const unsigned char*>(partials), n_slots, peer_ss, peer_of, max_norm,
+                       static_cast<zero_global_t*>(global));
+    return launch_error("combine kernel launch");
+}
+
+int launch_apply(const zero_step_args* a, const void* global, hipStream_t st) {
+    AdamConsts k;
+    const double t = static_cast<double>(a->step);
+    k.decay = static_cast<float>(1.0 - a->lr * a->weight_decay);
+    k.b1 = static_cast<float>(a->beta1);
+    k.c1 = static_cast<float>(1.0 - a->beta1);
+    k.b2 = static_cast<float>(a->beta2);
+    k.c2 = static_cast<float>(1.0 - a->beta2);
+    k.step_size = static_cast<float>(a->lr / (1.0 - std::pow(a->beta1, t)));
+    k.inv_sqrt_bc2 = static_cast<float>(1.0 / std::sqrt(1.0 - std::pow(a->beta2, t)));
+    k.eps = static_cast<float>(a->eps);
+    const int64_t nvec = a->valid_numel / kVec;
+    const int blocks = reduce_blocks_for(a->valid_numel);
+    const size_t elem = 2;
+    unsigned char* out = static_cast<unsigned char*>(a->full_params) +
+                         static_cast<size_t>(a->rank) * static_cast<size_t>(a->shard_numel) * elem;
+    const zero_global_t* gl = static_cast<const zero_global_t*>(global);
+    auto* g = static_cast<const f32x4*>(a->workspace);
+    auto* p = reinterpret_cast<f32x4*>(a->master);
+    auto* m = reinterpret_cast<f32x4*>(a->exp_avg);
+    auto* v = reinterpret_cast<f32x4*>(a->exp_avg_sq);
+    auto* o = reinterpret_cast<u32x4*>(out);
+    if (a->param_dtype == ZERO_BF16)
+        hipLaunchKernelGGL(apply_kernel<ZERO_BF16>, dim3(blocks), dim3(kReduceThreads), 0, st, g, p, m, v,
+                           o, nvec, a->valid_numel, gl, k);
+    else
+        hipLaunchKernelGGL(apply_kernel<ZERO_FP16>, dim3(blocks), dim3(kReduceThreads), 0, st, g, p, m, v,
+                           o, nvec, a->valid_numel, gl, k);
+    return launch_error("apply kernel launch");
+}
+
+}  // namespace
+}  // namespace zero
+
+using namespace zero;
+
+extern "C" {
+
+size_t zero_shard_workspace_bytes(int64_t shard_numel) {
+    if (shard_numel < 0) return 0;
+    return ws_global_offset(shard_numel) + 256;
+}
+
+size_t zero_partials_bytes(int32_t n_slots) {
+    if (n_slots < 0) return 0;
+    return static_cast<size_t>(n_slots) * kSlotBytes;
+}
+
+int zero_shard_reduce(const zero_step_args* a, int32_t slot, void* partials_dev, void* stream) {
+    clear_error();
+    int rc = validate_step_args(a);
+    if (rc) return rc;
+    if (slot < 0) return fail(ZERO_EINVAL, "slot %d < 0", slot);
+    if (!partials_dev) return fail(ZERO_EINVAL, "partials_dev is NULL");
+    if (!aligned16(partials_dev)) return fail(ZERO_EALIGN, "partials_dev is not 16-byte aligned");
+    unsigned char* s = static_cast<unsigned char*>(partials_dev) + static_cast<size_t>(slot) * kSlotBytes;
+    return launch_reduce(a, s, static_cast<hipStream_t>(stream));
+}
+
+int zero_shard_combine(const void* partials_dev, int32_t n_slots, double max_grad_norm,
+                       void* global_dev, void* stream) {
+    clear_error();
+    if (!partials_dev || !global_dev) return fail(ZERO_EINVAL, "partials_dev or global_dev is NULL");
+    if (n_slots < 1) return fail(ZERO_EINVAL, "n_slots %d < 1", n_slots);
+    if (std::isnan(max_grad_norm)) return fail(ZERO_EINVAL, "max_grad_norm is NaN");
+    if (!aligned16(partials_dev) || !aligned16(global_dev))
+        return fail(ZERO_EALIGN, "partials_dev or global_dev is not 16-byte aligned");
+    return launch_combine(partials_dev, n_slots, 0.0, 0, max_grad_norm, global_dev,
+                          static_cast<hipStream_t>(stream));
+}
+
+int zero_shard_apply(const zero_step_args* a, const void* global_dev, void* stream) {
+    clear_error();
+    int rc = validate_step_args(a);
+    if (rc) return rc;
+    if (!global_dev) return fail(ZERO_EINVAL, "global_dev is NULL");
+    if (!aligned16(global_dev)) return fail(ZERO_EALIGN, "global_dev is not 16-byte aligned");
+    return launch_apply(a, global_dev, static_cast<hipStream_t>(stream));
+}
+
+int zero_shard_step(const zero_step_args* a, double peer_sumsq, int32_t peer_overflow,
+                    zero_step_info* info, void* stream) {
+    clear_error();
+    int rc = validate_step_args(a);
+    if (rc) return rc;
+    if (!(peer_sumsq >= 0.0)) return fail(ZERO_EINVAL, "peer_sumsq must be >= 0 (got NaN or negative)");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    unsigned char* ws = static_cast<unsigned char*>(a->workspace);
+    unsigned char* slot = ws + ws_partials_offset(a->shard_numel);
+    void* global = ws + ws_global_offset(a->shard_numel);
+    if ((rc = launch_reduce(a, slot, st))) return rc;
+    if ((rc = launch_combine(slot, 1, peer_sumsq, peer_overflow ? 1 : 0, a->max_grad_norm, global, st)))
+        return rc;
+    if ((rc = launch_apply(a, global, st))) return rc;
+    if (info) {
+        hipError_t e = hipMemcpyAsync(info, global, sizeof(zero_global_t), hipMemcpyDeviceToHost, st);
+        if (e == hipSuccess) e = hipStreamSynchronize(st);
+        if (e != hipSuccess) return fail(ZERO_EDEVICE, "reading the step result: %s", hipGetErrorString(e));
+    }
+    return ZERO_OK;
+}
+
+int zero_bucket_flatten(const zero_tensor_slot_t* slots, int32_t n_tensors, const void* const* src_dev,
+                        int32_t dtype, void* flat_dev, int64_t flat_numel, void* stream) {
+    clear_error();
+    if (n_tensors < 0) return fail(ZERO_EINVAL, "n_tensors %d < 0", n_tensors);
+    if (!flat_dev || (n_tensors > 0 && (!slots || !src_dev)))
+        return fail(ZERO_EINVAL, "a required pointer is NULL");
+    if (dtype != ZERO_FP16 && dtype != ZERO_BF16)
+        return fail(ZERO_EINVAL, "dtype %d is not ZERO_FP16 or ZERO_BF16", dtype);
+    if (flat_numel < 0) return fail(ZERO_EINVAL, "flat_numel %lld < 0", (long long)flat_numel);
+    if (!aligned16(flat_dev)) return fail(ZERO_EALIGN, "flat_dev is not 16-byte aligned");
+    int64_t prev_end = 0;
+    for (int32_t t = 0; t < n_tensors; ++t) {
+        const zero_tensor_slot_t& s = slots[t];
+        if (s.numel < 0 || s.offset < prev_end || s.offset + s.numel > flat_numel)
+            return fail(ZERO_EINVAL, "slot %d [%lld, +%lld) is out of order or outside [0, %lld)", t,
+                        (long long)s.offset, (long long)s.numel, (long long)flat_numel);
+        if (s.numel > 0 && !src_dev[t]) return fail(ZERO_EINVAL, "src_dev[%d] is NULL", t);
+        if (reinterpret_cast<uintptr_t>(src_dev[t]) & 1u)
+            return fail(ZERO_EALIGN, "src_dev[%d] is not 2-byte aligned", t);
+        prev_end = s.offset + s.numel;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    unsigned short* flat = static_cast<unsigned short*>(flat_dev);
+    FlatBatch b;
+    b.count = 0;
+    int32_t blocks = 0;
+    auto flush = [&]() -> int {
+        if (b.count == 0) return ZERO_OK;
+        b.first_block[b.count] = blocks;
+        hipLaunchKernelGGL(flatten_kernel, dim3(blocks), dim3(kFlatThreads), 0, st, b, flat);
+        b.count = 0;
+        blocks = 0;
+        return launch_error("flatten kernel launch");
+    };
+    auto add = [&](const void* src, int64_t dst, int64_t n) -> int {
+        if (n <= 0) return ZERO_OK;
+        const int64_t nv = n / 8 + 2;
+        int64_t nb = (nv + kFlatVecPerBlock - 1) / kFlatVecPerBlock;
+        if (nb > kFlatMaxBlocksPerTensor) nb = kFlatMaxBlocksPerTensor;
+        b.src[b.count] = static_cast<const unsigned short*>(src);
+        b.dst[b.count] = dst;
+        b.n[b.count] = n;
+        b.first_block[b.count] = blocks;
+        blocks += static_cast<int32_t>(nb);
+        if (++b.count == kFlatBatch) return flush();
+        return ZERO_OK;
+    };
+    int rc;
+    for (int32_t t = 0; t < n_tensors; ++t)
+        if ((rc = add(src_dev[t], slots[t].offset, slots[t].numel))) return rc;
+    if ((rc = add(nullptr, prev_end, flat_numel - prev_end))) return rc;
+    return flush();
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+"""A whole data-parallel world held by one process on one GPU.
+
+With one GPU the reduce-scatter's arithmetic becomes a read of N replica
+gradient buffers that sit in the same HBM, the all-reduce of the norm and
+overflow flag becomes the combine over every simulated rank's partials, and
+the all-gather becomes each rank's cast into its slice of one shared full
+parameter buffer.  This class only allocates the buffers (torch) and queues
+the library's calls in the step's order; it computes nothing itself.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+from . import (GLOBAL_BYTES, StepArgs, zero_global_t, zero_partials_bytes, zero_partition,
+               zero_partition_valid_numel, zero_shard_apply, zero_shard_combine,
+               zero_shard_reduce, zero_shard_workspace_bytes)
+
+
+@dataclass
+class Hyper:
+    lr: float = 6e-5
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+    weight_decay: float = 0.01
+    max_grad_norm: float = 1.0
+    loss_scale: float = 1.0
+    grad_predivide: float = 1.0
+
+
+class SimulatedWorld:
+    """Buffers of `ranks` (default: every rank) of a world of `world_size`.
+
+    grads[i] holds replica i's flat gradient over the simulated ranks'
+    range [lo, hi) of the padded flat space; full_params spans the whole
+    padded space; master/exp_avg/exp_avg_sq[k] are rank ranks[k]'s shard.
+    """
+
+    def __init__(self, numel: int, world_size: int, n_replicas: Optional[int] = None,
+                 alignment: int = 128, grad_dtype=torch.bfloat16, param_dtype=None,
+                 device="cuda", ranks: Optional[Sequence[int]] = None,
+                 allocate_grads: bool = True):
+        self.part = zero_partition(numel, world_size, alignment)
+        self.numel = numel
+        self.world_size = world_size
+        self.n_replicas = n_replicas or world_size
+        self.s = self.part.shard_numel
+        self.padded = self.part.padded_numel
+        self.valid = [zero_partition_valid_numel(self.part, r) for r in range(world_size)]
+        self.ranks = list(ranks) if ranks is not None else list(range(world_size))
+        self.grad_dtype = grad_dtype
+        self.param_dtype = param_dtype or grad_dtype
+        self.device = torch.device(device)
+        self.lo = min(self.ranks) * self.s
+        self.hi = (max(self.ranks) + 1) * self.s
+        d = self.device
+        self.grads = [torch.zeros(self.hi - self.lo, dtype=grad_dtype, device=d)
+                      for _ in range(self.n_replicas)] if allocate_grads else []
+        self.master = [torch.zeros(self.s, dtype=torch.float32, device=d) for _ in self.ranks]
+        self.exp_avg = [torch.zeros(self.s, dtype=torch.float32, device=d) for _ in self.ranks]
+        self.exp_avg_sq = [torch.zeros(self.s, dtype=torch.float32, device=d) for _ in self.ranks]
+        self.full_params = torch.zeros(self.padded, dtype=self.param_dtype, device=d)
+        ws = zero_shard_workspace_bytes(self.s)
+        self.workspace = [torch.empty(ws, dtype=torch.uint8, device=d) for _ in self.ranks]
+        self.partials = torch.zeros(zero_partials_bytes(len(self.ranks)), dtype=torch.uint8,
+                                    device=d)
+        self.global_buf = torch.zeros(256, dtype=torch.uint8, device=d)
+        assert GLOBAL_BYTES <= 256
+
+    def grad_slice(self, replica: int, rank: int) -> torch.Tensor:
+        off = rank * self.s - self.lo
+        return self.grads[replica][off:off + self.s]
+
+    def rank_args(self, k: int, hp: Hyper, t: int) -> StepArgs:
+        r = self.ranks[k]
+        return StepArgs(world_size=self.world_size, rank=r, shard_numel=self.s,
+                        valid_numel=self.valid[r],
+                        replica_grads=[self.grad_slice(i, r) for i in range(self.n_replicas)],
+                        master=self.master[k], exp_avg=self.exp_avg[k],
+                        exp_avg_sq=self.exp_avg_sq[k], full_params=self.full_params,
+                        workspace=self.workspace[k], lr=hp.lr, beta1=hp.beta1, beta2=hp.beta2,
+                        eps=hp.eps, weight_decay=hp.weight_decay, step=t,
+                        loss_scale=hp.loss_scale, grad_predivide=hp.grad_predivide,
+                        max_grad_norm=hp.max_grad_norm, grad_dtype=self.grad_dtype,
+                        param_dtype=self.param_dtype)
+
+    def step(self, hp: Hyper, t: int, stream=None) -> None:
+        """Queue one optimizer step of every simulated rank (no host wait)."""
+        args = [self.rank_args(k, hp, t) for k in range(len(self.ranks))]
+        for k, a in enumerate(args):
+            zero_shard_reduce(a, k, self.partials, stream)
+        zero_shard_combine(self.partials, len(self.ranks), hp.max_grad_norm, self.global_buf,
+                           stream)
+        for a in args:
+            zero_shard_apply(a, self.global_buf, stream)
+
+    def result(self) -> zero_global_t:
+        """The last combine's result (waits for the device)."""
+        raw = self.global_buf[:GLOBAL_BYTES].cpu().numpy().tobytes()
+        return zero_global_t.from_buffer_copy(raw)
+
+    def reduced_grad(self, k: int) -> torch.Tensor:
+        """Rank ranks[k]'s fp32 reduced gradient from its last reduce."""
+        return self.workspace[k][:self.s * 4].view(torch.float32)
