@@ -133,6 +133,8 @@ def run_shard13b(args, torch, Z, W):
     comb = sum(e[1].elapsed_time(e[2]) for e in ev) / K
     app = sum(e[2].elapsed_time(e[3]) for e in ev) / K
     ms = total_ms / K
+    per_step = sorted(e[0].elapsed_time(e[3]) for e in ev)
+    log("per-step ms: " + " ".join("%.3f" % e[0].elapsed_time(e[3]) for e in ev))
     # the fused entry point over the same inputs, as a cross-check
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -147,7 +149,8 @@ def run_shard13b(args, torch, Z, W):
     bytes_reduce = valid * (2 * nrep + 4)
     bytes_apply = valid * (16 + 14)
     bytes_step = bytes_reduce + bytes_apply
-    res = dict(ms=ms, wall_ms=wall * 1e3 / K, fused_ms=fused_ms, reduce_ms=red, combine_ms=comb,
+    res = dict(ms=ms, wall_ms=wall * 1e3 / K, step_ms_min=per_step[0],
+               step_ms_median=per_step[len(per_step) // 2], step_ms_max=per_step[-1], fused_ms=fused_ms, reduce_ms=red, combine_ms=comb,
                apply_ms=app, valid=valid, bytes_step=bytes_step, bytes_reduce=bytes_reduce,
                bytes_apply=bytes_apply, norm=info.norm, clipped=info.clipped,
                overflow=info.overflow, grads=st["grads"], master0=None, st=st)
@@ -232,6 +235,7 @@ def main():
         "bytes_per_step": r["bytes_step"],
         "kernels_ms": {"reduce": r["reduce_ms"], "combine": r["combine_ms"], "apply": r["apply_ms"]},
         "fused_call_ms_per_step": r["fused_ms"],
+        "step_ms": {"min": r["step_ms_min"], "median": r["step_ms_median"], "max": r["step_ms_max"]},
         "wall_ms_per_step": r["wall_ms"],
         "roofline": {"bound": "hbm", "kernel": "apply_kernel (AdamW + cast)",
                      "achieved": app_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

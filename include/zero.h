@@ -196,12 +196,14 @@ typedef struct {
 typedef zero_global_t zero_step_info;
 
 /* Bytes of workspace a rank needs: the fp32 reduced gradient of its shard
- * (shard_numel * 4, rounded up to 256) followed by the per-block partial
- * norms and flags and one zero_global_t.  Host only. */
+ * (shard_numel * 4, rounded up to 256), one 16-byte partial sum of squares
+ * and flag per 1024 elements of the reduce pass, one partials slot (see
+ * zero_partials_bytes) and one zero_global_t.  Host only. */
 size_t zero_shard_workspace_bytes(int64_t shard_numel);
 
 /* Bytes of the partials table zero_shard_reduce / zero_shard_combine share
- * for n_slots ranks.  Host only. */
+ * for n_slots ranks: per slot a 16-byte header and at most 256 partial sums
+ * of squares (fp64) with their flags, whatever the shard size.  Host only. */
 size_t zero_partials_bytes(int32_t n_slots);
 
 /* Pass 1 of a rank's step, for worlds simulated in one process.
@@ -209,9 +211,12 @@ size_t zero_partials_bytes(int32_t n_slots);
  * sum over replicas of its own gradient slice.  For i < valid_numel:
  *   acc  = g_0[i] + g_1[i] + ... + g_{R-1}[i]   (fp32, replica order)
  *   g[i] = acc * fp32(1 / (loss_scale * grad_predivide))
- * stored as fp32 at the start of a->workspace; then writes this rank's
- * per-block sums of g^2 (fp64) and inf/nan flags into slot `slot` of
- * partials_dev (device, zero_partials_bytes(n_slots) long).
+ * stored as fp32 at the start of a->workspace, with one fp64 sum of g^2 and
+ * one inf/nan flag per 1024 elements after it; then folds those, in a fixed
+ * order, into at most 256 partials in slot `slot` of partials_dev (device,
+ * zero_partials_bytes(n_slots) long).  Every partial sum, and hence the
+ * norm, depends only on the values and valid_numel: the result is the same
+ * from run to run.
  * Errors: as zero_shard_step; slot < 0 -> ZERO_EINVAL. */
 int zero_shard_reduce(const zero_step_args* a, int32_t slot,
                       void* partials_dev, void* stream);

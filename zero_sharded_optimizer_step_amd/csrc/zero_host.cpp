@@ -21,14 +21,6 @@ int fail(int code, const char* fmt, ...) {
 
 void clear_error() { g_error[0] = '\0'; }
 
-int reduce_blocks_for(int64_t valid_numel) {
-    int64_t vecs = (valid_numel + kVec - 1) / kVec;
-    int64_t blocks = (vecs + kReduceThreads - 1) / kReduceThreads;
-    if (blocks < 1) blocks = 1;
-    if (blocks > kMaxReduceBlocks) blocks = kMaxReduceBlocks;
-    return static_cast<int>(blocks);
-}
-
 static bool finite_positive(double x) { return std::isfinite(x) && x > 0.0; }
 
 int validate_step_args(const zero_step_args* a) {
@@ -36,7 +28,7 @@ int validate_step_args(const zero_step_args* a) {
     if (a->world_size < 1) return fail(ZERO_EINVAL, "world_size %d < 1", a->world_size);
     if (a->rank < 0 || a->rank >= a->world_size)
         return fail(ZERO_EINVAL, "rank %d outside [0, %d)", a->rank, a->world_size);
-    if (a->shard_numel < 0 || a->shard_numel % kVec != 0)
+    if (a->shard_numel < 0 || a->shard_numel % kShardMultiple != 0)
         return fail(ZERO_EINVAL, "shard_numel %lld must be a non-negative multiple of 8",
                     (long long)a->shard_numel);
     if (a->valid_numel < 0 || a->valid_numel > a->shard_numel)

@@ -20,38 +20,69 @@ inline bool aligned16(const void* p) {
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Reduce-pass geometry: each thread owns 8 consecutive elements per
-// iteration; a grid of at most kMaxReduceBlocks blocks strides over the
-// shard.  The block count depends only on valid_numel, so the per-block
-// partial sums, and hence the norm, are identical from run to run.
-constexpr int kReduceThreads = 256;
-constexpr int kVec = 8;
-constexpr int kMaxReduceBlocks = 2048;
+// Launch geometry.  Both streaming passes give each thread one "quad" of 4
+// consecutive elements and launch one thread per quad (no grid-stride
+// loop): blocks are dispatched in order, so the set of addresses in flight
+// stays a compact window of every stream, which keeps HBM pages open.  The
+// block count is a multiple of 8 and dispatch-order block b is mapped to
+// logical block (b % 8) * (blocks / 8) + b / 8: the hardware deals blocks to
+// the 8 XCDs round robin, so each XCD walks its own contiguous eighth of the
+// shard.  Everything depends only on valid_numel, so the per-block partial
+// sums, and hence the norm, are identical from run to run.
+constexpr int kQuad = 4;
+// shard_numel must be a multiple of this, so that every rank's slice of the
+// full 16-bit parameter buffer starts on a 16-byte boundary.
+constexpr int64_t kShardMultiple = 8;
+constexpr int kReduceThreads = 256;        // reduce: 1024 elements per block
+constexpr int kApplyThreads = 64;          // apply: 256 elements per block
+constexpr int kXcds = 8;
+constexpr int kFoldBlocks = 256;           // fixed-size per-rank summary
 
-// One partial per reduce block.
+// One partial sum of squares (fp64) and inf/nan flag.
 struct Partial {
     double sumsq;
     int32_t flag;
     int32_t pad;
 };
 
-// Layout of one slot of the partials table: a 16-byte header holding the
-// number of blocks the reduce wrote, then kMaxReduceBlocks partials.
+// One slot of the partials table: a 16-byte header holding how many
+// entries follow, then up to kFoldBlocks partials.
 struct SlotHeader {
     int32_t n_blocks;
     int32_t pad[3];
 };
-constexpr size_t kSlotBytes = sizeof(SlotHeader) + kMaxReduceBlocks * sizeof(Partial);
+constexpr size_t kSlotBytes = sizeof(SlotHeader) + kFoldBlocks * sizeof(Partial);
 
-int reduce_blocks_for(int64_t valid_numel);
+// Quads (the last one possibly partial) of n elements.
+inline int64_t quads_of(int64_t n) { return (n + kQuad - 1) / kQuad; }
 
-// Byte offsets inside a zero_shard_step workspace.
+// Blocks of `threads` threads covering quads_of(n) quads, at least one,
+// rounded up to a multiple of kXcds.
+inline int64_t grid_for(int64_t n, int threads) {
+    int64_t b = (quads_of(n) + threads - 1) / threads;
+    if (b < 1) b = 1;
+    return (b + kXcds - 1) / kXcds * kXcds;
+}
+inline int64_t reduce_blocks_for(int64_t n) { return grid_for(n, kReduceThreads); }
+inline int64_t apply_blocks_for(int64_t n) { return grid_for(n, kApplyThreads); }
+inline int fold_blocks_for(int64_t reduce_blocks) {
+    return static_cast<int>(reduce_blocks < kFoldBlocks ? reduce_blocks : kFoldBlocks);
+}
+
+// Byte offsets inside a zero_shard_step workspace: the fp32 reduced
+// gradient, the reduce's per-block partials, one slot, one zero_global_t.
 inline size_t ws_grad_bytes(int64_t shard_numel) {
     return round_up(static_cast<size_t>(shard_numel) * 4u, 256);
 }
-inline size_t ws_partials_offset(int64_t shard_numel) { return ws_grad_bytes(shard_numel); }
+inline size_t ws_blocks_offset(int64_t shard_numel) { return ws_grad_bytes(shard_numel); }
+inline size_t ws_blocks_bytes(int64_t shard_numel) {
+    return round_up(static_cast<size_t>(reduce_blocks_for(shard_numel)) * sizeof(Partial), 256);
+}
+inline size_t ws_slot_offset(int64_t shard_numel) {
+    return ws_blocks_offset(shard_numel) + ws_blocks_bytes(shard_numel);
+}
 inline size_t ws_global_offset(int64_t shard_numel) {
-    return ws_partials_offset(shard_numel) + round_up(kSlotBytes, 256);
+    return ws_slot_offset(shard_numel) + round_up(kSlotBytes, 256);
 }
 
 // Checks every field of a step's arguments (see zero_shard_step).

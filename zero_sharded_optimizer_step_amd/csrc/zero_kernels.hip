@@ -2,11 +2,15 @@
 // the ABI entry points that launch them.
 //
 // The step is HBM-bound (about 50 bytes moved and ~25 flops per shard element
-// at 8 replicas), so the kernels are built around streaming: every thread
-// moves 8 elements per iteration with 16-byte vector loads and stores, a grid
-// of at most 2048 blocks strides over the shard, and reductions stay in
-// registers until one wavefront-shuffle + LDS step per block.  Nothing here
-// is a dense contraction, so there is no MFMA.
+// at 8 replicas), so the kernels are built around streaming.  Each thread
+// owns one quad of 4 consecutive elements and the grid has one thread per
+// quad: waves load, compute, store and retire, and the dispatcher refills
+// the CUs in address order, so every stream is read and written through a
+// compact moving window.  Blocks are spread over the 8 XCDs so that each XCD
+// walks a contiguous eighth of the shard.  Reductions stay in registers
+// until one wavefront-shuffle + LDS step per block; a fixed-shape fold and
+// combine finish them in a fixed order.  Nothing here is a dense
+// contraction, so there is no MFMA.
 //
 // Sources (cited by title and section):
 //   [P1] "ZeRO技术解析：大模型分布式训练的革命性突破"
@@ -21,14 +25,22 @@ namespace zero {
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 struct ReplicaPtrs {
-    const u32x4* p[ZERO_MAX_REPLICAS];
+    const u32x2* p[ZERO_MAX_REPLICAS];
 };
+
+// Logical block of dispatch-order block b in a grid of nb (a multiple of
+// kXcds) blocks: XCD b % 8 takes the contiguous run of logical blocks
+// [(b % 8) * nb / 8, (b % 8 + 1) * nb / 8).
+__device__ __forceinline__ int64_t xcd_block(int64_t b, int64_t nb) {
+    return (b % kXcds) * (nb / kXcds) + b / kXcds;
+}
 
 // ---------------------------------------------------------------- formats
 // bf16 is the upper half of an fp32; fp16 goes through the hardware convert,
@@ -44,15 +56,9 @@ __device__ __forceinline__ float hi_to_f32(unsigned w) {
     else return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(w >> 16)));
 }
 template <int DT>
-__device__ __forceinline__ void decode8(const u32x4 v, float o[8]) {
+__device__ __forceinline__ void decode4(const u32x2 v, float o[4]) {
     o[0] = lo_to_f32<DT>(v.x); o[1] = hi_to_f32<DT>(v.x);
     o[2] = lo_to_f32<DT>(v.y); o[3] = hi_to_f32<DT>(v.y);
-    o[4] = lo_to_f32<DT>(v.z); o[5] = hi_to_f32<DT>(v.z);
-    o[6] = lo_to_f32<DT>(v.w); o[7] = hi_to_f32<DT>(v.w);
-}
-template <int DT>
-__device__ __forceinline__ float scalar_to_f32(unsigned short h) {
-    return lo_to_f32<DT>(h);
 }
 
 // Round to nearest even with the gfx950 packed converts (v_cvt_pk_bf16_f32,
@@ -72,21 +78,26 @@ __device__ __forceinline__ bool finite(float x) { return __builtin_isfinite(x); 
 
 // ------------------------------------------------------- block reduction
 // Fixed shuffle pattern and fixed wave order: the block's result depends
-// only on which values its threads hold, never on timing.
-__device__ __forceinline__ void block_reduce(double& ss, int& bad, double* s_ss, int* s_bad) {
+// only on which values its threads hold, never on timing.  Thread 0 ends
+// with the block's total.
+template <int THREADS>
+__device__ __forceinline__ void block_reduce(double& ss, int& bad) {
     #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
         ss += __shfl_xor(ss, off, 64);
         bad |= __shfl_xor(bad, off, 64);
     }
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    if (lane == 0) { s_ss[wave] = ss; s_bad[wave] = bad; }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int waves = blockDim.x >> 6;
-        ss = s_ss[0];
-        bad = s_bad[0];
-        for (int w = 1; w < waves; ++w) { ss += s_ss[w]; bad |= s_bad[w]; }
+    if constexpr (THREADS > 64) {
+        __shared__ double s_ss[THREADS / 64];
+        __shared__ int s_bad[THREADS / 64];
+        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        if (lane == 0) { s_ss[wave] = ss; s_bad[wave] = bad; }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            ss = s_ss[0];
+            bad = s_bad[0];
+            for (int w = 1; w < THREADS / 64; ++w) { ss += s_ss[w]; bad |= s_bad[w]; }
+        }
     }
 }
 
@@ -96,71 +107,100 @@ __device__ __forceinline__ void block_reduce(double& ss, int& bad, double* s_ss,
 // in one HBM and the sum is an fp32 running sum in replica order; the loss
 // scale ([P1] §3.3, §5.1) is undone by one multiply; the inf/nan flag and
 // the fp64 sum of squares for clipping ([P1] §6) ride along in registers.
+// Each replica is read once, so its loads are nontemporal.
+template <int DT, int NR>
+__device__ __forceinline__ void sum_quad(const ReplicaPtrs& reps, int nrep, int64_t q, float acc[4]) {
+    if constexpr (NR > 0) {
+        u32x2 x[NR];
+        #pragma unroll
+        for (int r = 0; r < NR; ++r) x[r] = __builtin_nontemporal_load(reps.p[r] + q);
+        decode4<DT>(x[0], acc);
+        #pragma unroll
+        for (int r = 1; r < NR; ++r) {
+            float y[4];
+            decode4<DT>(x[r], y);
+            #pragma unroll
+            for (int k = 0; k < 4; ++k) acc[k] = acc[k] + y[k];
+        }
+    } else {
+        decode4<DT>(__builtin_nontemporal_load(reps.p[0] + q), acc);
+        for (int r = 1; r < nrep; ++r) {
+            float y[4];
+            decode4<DT>(__builtin_nontemporal_load(reps.p[r] + q), y);
+            #pragma unroll
+            for (int k = 0; k < 4; ++k) acc[k] = acc[k] + y[k];
+        }
+    }
+}
+
 template <int DT, int NR>
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(
-    ReplicaPtrs reps, int nrep, int64_t nvec, int64_t n_valid, float inv_scale,
-    f32x4* __restrict__ g, Partial* __restrict__ partials, SlotHeader* __restrict__ header) {
+    ReplicaPtrs reps, int nrep, int64_t n_valid, float inv_scale, float* __restrict__ g,
+    Partial* __restrict__ partials) {
+    const int64_t blk = xcd_block(blockIdx.x, gridDim.x);
+    const int64_t q = blk * kReduceThreads + threadIdx.x;
+    const int64_t full = n_valid / kQuad;              // complete quads
     double ss = 0.0;
     int bad = 0;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kReduceThreads;
-    for (int64_t v = static_cast<int64_t>(blockIdx.x) * kReduceThreads + threadIdx.x; v < nvec;
-         v += stride) {
-        float acc[8];
-        if constexpr (NR > 0) {
-            u32x4 x[NR];
-            #pragma unroll
-            for (int r = 0; r < NR; ++r) x[r] = reps.p[r][v];
-            decode8<DT>(x[0], acc);
-            #pragma unroll
-            for (int r = 1; r < NR; ++r) {
-                float y[8];
-                decode8<DT>(x[r], y);
-                #pragma unroll
-                for (int k = 0; k < 8; ++k) acc[k] = acc[k] + y[k];
-            }
-        } else {
-            decode8<DT>(reps.p[0][v], acc);
-            for (int r = 1; r < nrep; ++r) {
-                float y[8];
-                decode8<DT>(reps.p[r][v], y);
-                #pragma unroll
-                for (int k = 0; k < 8; ++k) acc[k] = acc[k] + y[k];
-            }
-        }
-        f32x4 o0, o1;
+    if (q < full) {
+        float acc[4];
+        sum_quad<DT, NR>(reps, nrep, q, acc);
+        f32x4 o;
         #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < 4; ++k) {
             const float gk = acc[k] * inv_scale;
             bad |= !finite(gk);
             ss += static_cast<double>(gk) * static_cast<double>(gk);
-            if (k < 4) o0[k] = gk; else o1[k - 4] = gk;
+            o[k] = gk;
         }
-        g[2 * v] = o0;
-        g[2 * v + 1] = o1;
-    }
-    // Ragged tail (fewer than 8 elements): block 0, one element per thread.
-    const int64_t tail0 = nvec * kVec;
-    if (blockIdx.x == 0 && tail0 + threadIdx.x < n_valid) {
-        const int64_t i = tail0 + threadIdx.x;
-        float acc = 0.0f;
-        for (int r = 0; r < nrep; ++r) {
-            const unsigned short* base = reinterpret_cast<const unsigned short*>(reps.p[r]);
-            const float x = scalar_to_f32<DT>(base[i]);
-            acc = (r == 0) ? x : acc + x;
+        reinterpret_cast<f32x4*>(g)[q] = o;
+    } else if (q == full) {
+        // Ragged tail: the 0-3 elements after the last complete quad.
+        for (int64_t i = q * kQuad; i < n_valid; ++i) {
+            float acc = 0.0f;
+            for (int r = 0; r < nrep; ++r) {
+                const unsigned short* base = reinterpret_cast<const unsigned short*>(reps.p[r]);
+                const float x = lo_to_f32<DT>(base[i]);
+                acc = (r == 0) ? x : acc + x;
+            }
+            const float gi = acc * inv_scale;
+            bad |= !finite(gi);
+            ss += static_cast<double>(gi) * static_cast<double>(gi);
+            g[i] = gi;
         }
-        const float gi = acc * inv_scale;
-        bad |= !finite(gi);
-        ss += static_cast<double>(gi) * static_cast<double>(gi);
-        reinterpret_cast<float*>(g)[i] = gi;
     }
-    __shared__ double s_ss[kReduceThreads / 64];
-    __shared__ int s_bad[kReduceThreads / 64];
-    block_reduce(ss, bad, s_ss, s_bad);
+    block_reduce<kReduceThreads>(ss, bad);
     if (threadIdx.x == 0) {
-        partials[blockIdx.x].sumsq = ss;
-        partials[blockIdx.x].flag = bad;
-        partials[blockIdx.x].pad = 0;
-        if (blockIdx.x == 0) header->n_blocks = static_cast<int32_t>(gridDim.x);
+        partials[blk].sumsq = ss;
+        partials[blk].flag = bad;
+        partials[blk].pad = 0;
+    }
+}
+
+// ============================================================ fold (small)
+// The reduce leaves one partial per block (about a million for a 1.6e9
+// element shard).  Block b of the fold sums the contiguous run
+// [b * per, (b + 1) * per) of them, per = ceil(n / gridDim), in a fixed
+// order, and writes entry b of a slot; block 0 records the entry count.
+__global__ __launch_bounds__(256) void fold_kernel(const Partial* __restrict__ parts, int64_t n,
+                                                   unsigned char* __restrict__ slot) {
+    const int64_t per = (n + gridDim.x - 1) / gridDim.x;
+    const int64_t lo = static_cast<int64_t>(blockIdx.x) * per;
+    const int64_t hi = lo + per < n ? lo + per : n;
+    double ss = 0.0;
+    int bad = 0;
+    for (int64_t i = lo + threadIdx.x; i < hi; i += 256) {
+        ss += parts[i].sumsq;
+        bad |= parts[i].flag;
+    }
+    block_reduce<256>(ss, bad);
+    if (threadIdx.x == 0) {
+        SlotHeader* h = reinterpret_cast<SlotHeader*>(slot);
+        Partial* out = reinterpret_cast<Partial*>(h + 1);
+        out[blockIdx.x].sumsq = ss;
+        out[blockIdx.x].flag = bad;
+        out[blockIdx.x].pad = 0;
+        if (blockIdx.x == 0) h->n_blocks = static_cast<int32_t>(gridDim.x);
     }
 }
 
@@ -177,16 +217,14 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     for (int s = 0; s < n_slots; ++s) {
         const SlotHeader* h = reinterpret_cast<const SlotHeader*>(partials + static_cast<size_t>(s) * kSlotBytes);
         int nb = h->n_blocks;
-        nb = nb < 0 ? 0 : (nb > kMaxReduceBlocks ? kMaxReduceBlocks : nb);
+        nb = nb < 0 ? 0 : (nb > kFoldBlocks ? kFoldBlocks : nb);
         const Partial* p = reinterpret_cast<const Partial*>(h + 1);
         for (int b = threadIdx.x; b < nb; b += kCombineThreads) {
             ss += p[b].sumsq;
             bad |= p[b].flag;
         }
     }
-    __shared__ double s_ss[kCombineThreads / 64];
-    __shared__ int s_bad[kCombineThreads / 64];
-    block_reduce(ss, bad, s_ss, s_bad);
+    block_reduce<kCombineThreads>(ss, bad);
     if (threadIdx.x == 0) {
         ss += peer_sumsq;
         bad |= peer_overflow;
@@ -225,54 +263,41 @@ __device__ __forceinline__ void adamw1(float g, float& p, float& m, float& v, co
     p = p * k.decay - k.step_size * (m / d);
 }
 
+// coef is 1 when clipping does not apply; multiplying by it is then exact.
 template <int PT>
-__global__ __launch_bounds__(kReduceThreads) void apply_kernel(
-    const f32x4* __restrict__ g, f32x4* __restrict__ p, f32x4* __restrict__ m, f32x4* __restrict__ v,
-    u32x4* __restrict__ out, int64_t nvec, int64_t n_valid, const zero_global_t* __restrict__ glob,
+__global__ __launch_bounds__(kApplyThreads) void apply_kernel(
+    const float* __restrict__ g, float* __restrict__ p, float* __restrict__ m, float* __restrict__ v,
+    unsigned short* __restrict__ out, int64_t n_valid, const zero_global_t* __restrict__ glob,
     AdamConsts k) {
     if (glob->overflow) return;                    // skipped step: touch nothing
     const float coef = glob->coef;
-    const bool clip = glob->clipped != 0;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kReduceThreads;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kReduceThreads + threadIdx.x; i < nvec;
-         i += stride) {
-        f32x4 g0 = g[2 * i], g1 = g[2 * i + 1];
-        f32x4 p0 = p[2 * i], p1 = p[2 * i + 1];
-        f32x4 m0 = m[2 * i], m1 = m[2 * i + 1];
-        f32x4 v0 = v[2 * i], v1 = v[2 * i + 1];
-        if (clip) { g0 *= coef; g1 *= coef; }
+    const int64_t q = xcd_block(blockIdx.x, gridDim.x) * kApplyThreads + threadIdx.x;
+    const int64_t full = n_valid / kQuad;
+    if (q < full) {
+        f32x4 gq = reinterpret_cast<const f32x4*>(g)[q];
+        f32x4 pq = reinterpret_cast<const f32x4*>(p)[q];
+        f32x4 mq = reinterpret_cast<const f32x4*>(m)[q];
+        f32x4 vq = reinterpret_cast<const f32x4*>(v)[q];
         #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            float pe = p0[e], me = m0[e], ve = v0[e];
-            adamw1(g0[e], pe, me, ve, k);
-            p0[e] = pe; m0[e] = me; v0[e] = ve;
-            pe = p1[e]; me = m1[e]; ve = v1[e];
-            adamw1(g1[e], pe, me, ve, k);
-            p1[e] = pe; m1[e] = me; v1[e] = ve;
+            float pe = pq[e], me = mq[e], ve = vq[e];
+            adamw1(gq[e] * coef, pe, me, ve, k);
+            pq[e] = pe; mq[e] = me; vq[e] = ve;
         }
-        p[2 * i] = p0; p[2 * i + 1] = p1;
-        m[2 * i] = m0; m[2 * i + 1] = m1;
-        v[2 * i] = v0; v[2 * i + 1] = v1;
-        u32x4 o;
-        o.x = pack2<PT>(p0.x, p0.y);
-        o.y = pack2<PT>(p0.z, p0.w);
-        o.z = pack2<PT>(p1.x, p1.y);
-        o.w = pack2<PT>(p1.z, p1.w);
-        out[i] = o;
-    }
-    const int64_t tail0 = nvec * kVec;
-    if (blockIdx.x == 0 && tail0 + threadIdx.x < n_valid) {
-        const int64_t j = tail0 + threadIdx.x;
-        const float* gs = reinterpret_cast<const float*>(g);
-        float* ps = reinterpret_cast<float*>(p);
-        float* ms = reinterpret_cast<float*>(m);
-        float* vs = reinterpret_cast<float*>(v);
-        float gj = gs[j];
-        if (clip) gj *= coef;
-        float pj = ps[j], mj = ms[j], vj = vs[j];
-        adamw1(gj, pj, mj, vj, k);
-        ps[j] = pj; ms[j] = mj; vs[j] = vj;
-        reinterpret_cast<unsigned short*>(out)[j] = pack1<PT>(pj);
+        reinterpret_cast<f32x4*>(p)[q] = pq;
+        reinterpret_cast<f32x4*>(m)[q] = mq;
+        reinterpret_cast<f32x4*>(v)[q] = vq;
+        u32x2 o;
+        o.x = pack2<PT>(pq.x, pq.y);
+        o.y = pack2<PT>(pq.z, pq.w);
+        reinterpret_cast<u32x2*>(out)[q] = o;
+    } else if (q == full) {
+        for (int64_t j = q * kQuad; j < n_valid; ++j) {
+            float pj = p[j], mj = m[j], vj = v[j];
+            adamw1(g[j] * coef, pj, mj, vj, k);
+            p[j] = pj; m[j] = mj; v[j] = vj;
+            out[j] = pack1<PT>(pj);
+        }
     }
 }
 
@@ -388,38 +413,41 @@ int launch_error(const char* what) {
 
 template <int DT>
 void launch_reduce_dt(const ReplicaPtrs& reps, int nrep, int64_t n_valid, float inv, float* g,
-                      unsigned char* slot, hipStream_t st) {
-    const int blocks = reduce_blocks_for(n_valid);
-    const int64_t nvec = n_valid / kVec;
-    SlotHeader* h = reinterpret_cast<SlotHeader*>(slot);
-    Partial* parts = reinterpret_cast<Partial*>(h + 1);
-    f32x4* gv = reinterpret_cast<f32x4*>(g);
-#define ZERO_REDUCE_CASE(NR)                                                                     \
-    case NR:                                                                                     \
-        hipLaunchKernelGGL((reduce_kernel<DT, NR>), dim3(blocks), dim3(kReduceThreads), 0, st, reps, \
-                           nrep, nvec, n_valid, inv, gv, parts, h);                              \
+                      Partial* parts, hipStream_t st) {
+    const dim3 grid(static_cast<unsigned>(reduce_blocks_for(n_valid)));
+#define ZERO_REDUCE_CASE(NR)                                                                       \
+    case NR:                                                                                       \
+        hipLaunchKernelGGL((reduce_kernel<DT, NR>), grid, dim3(kReduceThreads), 0, st, reps, nrep, \
+                           n_valid, inv, g, parts);                                                \
         break;
     switch (nrep) {
         ZERO_REDUCE_CASE(1) ZERO_REDUCE_CASE(2) ZERO_REDUCE_CASE(3) ZERO_REDUCE_CASE(4)
         ZERO_REDUCE_CASE(5) ZERO_REDUCE_CASE(6) ZERO_REDUCE_CASE(7) ZERO_REDUCE_CASE(8)
         default:
-            hipLaunchKernelGGL((reduce_kernel<DT, 0>), dim3(blocks), dim3(kReduceThreads), 0, st, reps,
-                               nrep, nvec, n_valid, inv, gv, parts, h);
+            hipLaunchKernelGGL((reduce_kernel<DT, 0>), grid, dim3(kReduceThreads), 0, st, reps, nrep,
+                               n_valid, inv, g, parts);
     }
 #undef ZERO_REDUCE_CASE
 }
 
+// Pass 1 into the workspace, then the fold of its block partials into `slot`.
 int launch_reduce(const zero_step_args* a, unsigned char* slot, hipStream_t st) {
     ReplicaPtrs reps;
     for (int r = 0; r < ZERO_MAX_REPLICAS; ++r)
-        reps.p[r] = r < a->n_replicas ? static_cast<const u32x4*>(a->replica_grad[r]) : nullptr;
+        reps.p[r] = r < a->n_replicas ? static_cast<const u32x2*>(a->replica_grad[r]) : nullptr;
     const float inv = static_cast<float>(1.0 / (a->loss_scale * a->grad_predivide));
-    float* g = static_cast<float*>(a->workspace);
+    unsigned char* ws = static_cast<unsigned char*>(a->workspace);
+    float* g = reinterpret_cast<float*>(ws);
+    Partial* parts = reinterpret_cast<Partial*>(ws + ws_blocks_offset(a->shard_numel));
     if (a->grad_dtype == ZERO_BF16)
-        launch_reduce_dt<ZERO_BF16>(reps, a->n_replicas, a->valid_numel, inv, g, slot, st);
+        launch_reduce_dt<ZERO_BF16>(reps, a->n_replicas, a->valid_numel, inv, g, parts, st);
     else
-        launch_reduce_dt<ZERO_FP16>(reps, a->n_replicas, a->valid_numel, inv, g, slot, st);
-    return launch_error("reduce kernel launch");
+        launch_reduce_dt<ZERO_FP16>(reps, a->n_replicas, a->valid_numel, inv, g, parts, st);
+    int rc = launch_error("reduce kernel launch");
+    if (rc) return rc;
+    const int64_t nb = reduce_blocks_for(a->valid_numel);
+    hipLaunchKernelGGL(fold_kernel, dim3(fold_blocks_for(nb)), dim3(256), 0, st, parts, nb, slot);
+    return launch_error("fold kernel launch");
 }
 
 int launch_combine(const void* partials, int n_slots, double peer_ss, int peer_of, double max_norm,
@@ -441,23 +469,17 @@ int launch_apply(const zero_step_args* a, const void* global, hipStream_t st) {
     k.step_size = static_cast<float>(a->lr / (1.0 - std::pow(a->beta1, t)));
     k.inv_sqrt_bc2 = static_cast<float>(1.0 / std::sqrt(1.0 - std::pow(a->beta2, t)));
     k.eps = static_cast<float>(a->eps);
-    const int64_t nvec = a->valid_numel / kVec;
-    const int blocks = reduce_blocks_for(a->valid_numel);
-    const size_t elem = 2;
-    unsigned char* out = static_cast<unsigned char*>(a->full_params) +
-                         static_cast<size_t>(a->rank) * static_cast<size_t>(a->shard_numel) * elem;
+    const dim3 grid(static_cast<unsigned>(apply_blocks_for(a->valid_numel)));
+    unsigned short* out = static_cast<unsigned short*>(a->full_params) +
+                          static_cast<size_t>(a->rank) * static_cast<size_t>(a->shard_numel);
     const zero_global_t* gl = static_cast<const zero_global_t*>(global);
-    auto* g = static_cast<const f32x4*>(a->workspace);
-    auto* p = reinterpret_cast<f32x4*>(a->master);
-    auto* m = reinterpret_cast<f32x4*>(a->exp_avg);
-    auto* v = reinterpret_cast<f32x4*>(a->exp_avg_sq);
-    auto* o = reinterpret_cast<u32x4*>(out);
+    const float* g = static_cast<const float*>(a->workspace);
     if (a->param_dtype == ZERO_BF16)
-        hipLaunchKernelGGL(apply_kernel<ZERO_BF16>, dim3(blocks), dim3(kReduceThreads), 0, st, g, p, m, v,
-                           o, nvec, a->valid_numel, gl, k);
+        hipLaunchKernelGGL(apply_kernel<ZERO_BF16>, grid, dim3(kApplyThreads), 0, st, g, a->master,
+                           a->exp_avg, a->exp_avg_sq, out, a->valid_numel, gl, k);
     else
-        hipLaunchKernelGGL(apply_kernel<ZERO_FP16>, dim3(blocks), dim3(kReduceThreads), 0, st, g, p, m, v,
-                           o, nvec, a->valid_numel, gl, k);
+        hipLaunchKernelGGL(apply_kernel<ZERO_FP16>, grid, dim3(kApplyThreads), 0, st, g, a->master,
+                           a->exp_avg, a->exp_avg_sq, out, a->valid_numel, gl, k);
     return launch_error("apply kernel launch");
 }
 
@@ -518,7 +540,7 @@ int zero_shard_step(const zero_step_args* a, double peer_sumsq, int32_t peer_ove
     if (!(peer_sumsq >= 0.0)) return fail(ZERO_EINVAL, "peer_sumsq must be >= 0 (got NaN or negative)");
     hipStream_t st = static_cast<hipStream_t>(stream);
     unsigned char* ws = static_cast<unsigned char*>(a->workspace);
-    unsigned char* slot = ws + ws_partials_offset(a->shard_numel);
+    unsigned char* slot = ws + ws_slot_offset(a->shard_numel);
     void* global = ws + ws_global_offset(a->shard_numel);
     if ((rc = launch_reduce(a, slot, st))) return rc;
     if ((rc = launch_combine(slot, 1, peer_sumsq, peer_overflow ? 1 : 0, a->max_grad_norm, global, st)))
