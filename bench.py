@@ -39,7 +39,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="shard13b", choices=["shard13b"])
+    ap.add_argument("--workload", default="shard13b", choices=["shard13b", "ragged"],
+                    help="shard13b: rank 0 of the 13B/8 flat model (the headline); "
+                         "ragged: 2000 tensors flattened bucket by bucket, then the step of "
+                         "all 8 ranks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 28,
                     help="elements of the shard the CPU oracle is timed on")
@@ -181,6 +184,104 @@ def cpu_baseline_shard13b(args, torch, W, st):
                        "AdamW, bf16 cast; one host thread, %.1f s" % (n, dt))
 
 
+def run_ragged(args, torch, Z, W):
+    """The ragged workload: every replica's 2000 per-tensor gradients (at odd
+    offsets of one pool) flattened bucket by bucket into its flat buffer,
+    then the step of all 8 ranks (reduce per rank, one combine, AdamW +
+    cast per rank).  One step = both; HIP events split them."""
+    import ctypes
+    from zero_sharded_optimizer_step_amd import _abi
+    from zero_sharded_optimizer_step_amd.world import Hyper, SimulatedWorld
+    w = W.RAGGED_2000
+    sizes = list(w.tensor_sizes)
+    P, N = w.numel, w.world_size
+    slots, buckets = Z.zero_bucket_plan(sizes, int(2e8))
+    world = SimulatedWorld(P, N, alignment=w.alignment, grad_dtype=torch.bfloat16)
+    padded = world.padded
+    log("ragged: %d tensors, %d params, %d buckets; generating 8 replicas" % (len(sizes), P,
+                                                                           len(buckets)))
+    pools, calls = [], []
+    ref = torch.empty(padded, dtype=torch.bfloat16, device="cuda")
+    for i in range(N):
+        W.flat_normal(ref, 0, P, w.grad_sigma, W.grad_key(w, 0, 0, i))
+        pool = torch.empty(P + len(sizes) + 8, dtype=torch.bfloat16, device="cuda")
+        ptrs = []
+        for k, x in enumerate(slots):
+            src = pool[x.offset + k + 1:x.offset + k + 1 + x.numel]
+            src.copy_(ref[x.offset:x.offset + x.numel])
+            ptrs.append(src.data_ptr())
+        pools.append(pool)
+        for bi, b in enumerate(buckets):
+            sl = slots[b.first_tensor:b.first_tensor + b.n_tensors]
+            arr = (_abi.zero_tensor_slot_t * len(sl))(*sl)
+            parr = (_abi.vp * len(sl))(*ptrs[b.first_tensor:b.first_tensor + b.n_tensors])
+            flat_numel = padded if bi == len(buckets) - 1 else b.end
+            calls.append((arr, len(sl), parr, world.grads[i].data_ptr(), flat_numel))
+    del ref
+    for k, r in enumerate(world.ranks):
+        W.flat_normal(world.master[k], r * world.s, P, w.master_sigma, W.master_key(w, 0))
+    hp = Hyper(lr=w.lr, weight_decay=w.weight_decay, max_grad_norm=w.max_grad_norm)
+    L = Z.lib()
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def flatten_all():
+        for arr, n, parr, dst, fn in calls:
+            Z.check(L.zero_bucket_flatten(arr, n, parr, Z.ZERO_BF16, dst, fn, sp),
+                    "zero_bucket_flatten")
+
+    t = 1
+    for _ in range(args.warmup):
+        flatten_all()
+        world.step(hp, t, stream)
+        t += 1
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for k in range(K):
+        ev[k][0].record(stream)
+        flatten_all()
+        ev[k][1].record(stream)
+        world.step(hp, t, stream)
+        ev[k][2].record(stream)
+        t += 1
+    torch.cuda.synchronize()
+    flat_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    step_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    res = world.result()
+    return dict(P=P, N=N, s=world.s, flat_ms=flat_ms, step_ms=step_ms,
+                ms=ev[0][0].elapsed_time(ev[-1][2]) / K, n_buckets=len(buckets),
+                norm=res.norm, clipped=res.clipped, overflow=res.overflow)
+
+
+def report_ragged(args, r, W):
+    P, N = r["P"], r["N"]
+    flat_bytes = N * P * 4                   # each replica: 2 B read + 2 B written per element
+    step_bytes = P * (2 * N + 34)
+    flat_gbps = flat_bytes / (r["flat_ms"] * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": P / (r["ms"] * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": r["ms"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": W.RAGGED_2000.name, "params": P, "tensors": 2000,
+                   "buckets": r["n_buckets"], "world_size": N, "replicas": N,
+                   "shard_numel": r["s"], "grad_dtype": "bf16", "param_dtype": "bf16"},
+        "hbm_gbps": (flat_bytes + step_bytes) / (r["ms"] * 1e-3) / 1e9,
+        "hbm_frac": (flat_bytes + step_bytes) / (r["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "bytes_per_step": flat_bytes + step_bytes,
+        "phases_ms": {"flatten_8_replicas": r["flat_ms"], "step_8_ranks": r["step_ms"]},
+        "step_gbps": step_bytes / (r["step_ms"] * 1e-3) / 1e9,
+        "roofline": {"bound": "hbm", "kernel": "flatten_kernel (all launches of one step)",
+                     "achieved": flat_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": flat_gbps / HBM_PEAK_GBPS, "traffic": None},
+        "step_check": {"norm": r["norm"], "clipped": r["clipped"], "overflow": r["overflow"]},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def calibrate_copy(torch, n):
     """Plain copies of a known size, for scaling the HBM byte counters."""
     nbytes = 4 << 30
@@ -209,6 +310,9 @@ def main():
     Z.lib()
     if args.calibrate_copy:
         calibrate_copy(torch, args.calibrate_copy)
+        return
+    if args.workload == "ragged":
+        report_ragged(args, run_ragged(args, torch, Z, W), W)
         return
     r = run_shard13b(args, torch, Z, W)
     app_gbps = r["bytes_apply"] / (r["apply_ms"] * 1e-3) / 1e9

@@ -239,3 +239,22 @@ def test_flatten_per_bucket():
                               torch.bfloat16, flat.view(torch.bfloat16), b.end)
     ref = np.concatenate([parity.u16(s) for s in srcs])
     parity.assert_bitwise("flat", parity.u16(flat.view(torch.bfloat16)), ref)
+
+
+def test_flatten_pieces_beyond_one_table_entry():
+    # A tensor and a padding run longer than one table entry (2^30
+    # elements), the tensor at an odd source offset.
+    n = (1 << 30) + 12_345
+    pad = (1 << 30) + 77
+    say("flatten one tensor of %d elements and %d padding" % (n, pad))
+    base = torch.randint(-32768, 32767, (n + 3,), dtype=torch.int16, device="cuda")
+    src = base[3:].view(torch.bfloat16)
+    slots, _ = Z.zero_bucket_plan([n], 1 << 40)
+    flat = torch.full((n + pad + 64,), 0x1357, dtype=torch.int16, device="cuda")
+    # destination offset 5: shift the slot so the copy is misaligned on both sides
+    slots[0].offset = 5
+    Z.zero_bucket_flatten(slots, [src], torch.bfloat16, flat.view(torch.bfloat16), n + pad)
+    assert torch.equal(flat[5:5 + n], base[3:]), "body differs"
+    assert bool((flat[:5] == 0x1357).all()), "wrote before the slot"
+    assert bool((flat[5 + n:n + pad] == 0).all()), "padding not zeroed"
+    assert bool((flat[n + pad:] == 0x1357).all()), "wrote past flat_numel"

@@ -303,23 +303,24 @@ __global__ __launch_bounds__(kApplyThreads) void apply_kernel(
 
 // ================================================================ flatten
 // contiguous_gradients ([P1] §5.2): one replica's tensors are copied end to
-// end into its flat buffer, then the padding is zeroed.  Each destination
-// vector of 8 elements is written with one aligned 16-byte store; the source
-// side is read as aligned 16-byte vectors and shifted into place, so a
-// tensor's arbitrary offset costs no unaligned accesses.  The few elements
-// before the first and after the last aligned vector of a tensor are copied
-// one by one.
-constexpr int kFlatBatch = 128;       // tensors per launch (kernel arguments)
+// end into its flat buffer, then the padding is zeroed.  Each thread writes
+// one aligned 16-byte vector of 8 destination elements.  The source side is
+// read as aligned 16-byte vectors and shifted into place, so a tensor's
+// arbitrary offset costs no unaligned accesses (the second vector of a
+// shifted pair is the next thread's first, served from cache).  The few
+// elements before the first and after the last aligned destination vector
+// of a tensor are copied one by one by its first block.  Blocks of one
+// launch are spread over the XCDs like the step's kernels, so each XCD
+// copies a contiguous run of the batch's tensors.
+constexpr int kFlatBatch = 128;            // tensors per launch (kernel arguments)
 constexpr int kFlatThreads = 256;
-constexpr int kFlatVecPerThread = 4;
-constexpr int64_t kFlatVecPerBlock = kFlatThreads * kFlatVecPerThread;
-constexpr int64_t kFlatMaxBlocksPerTensor = 65536;
+constexpr int64_t kFlatMaxPiece = int64_t(1) << 30;   // elements per table entry
 
 struct FlatBatch {
     const unsigned short* src[kFlatBatch];   // nullptr: write zeros
     int64_t dst[kFlatBatch];                 // first flat element
     int64_t n[kFlatBatch];
-    int32_t first_block[kFlatBatch + 1];
+    int32_t first_block[kFlatBatch + 1];     // prefix of blocks per entry
     int32_t count;
 };
 
@@ -348,16 +349,16 @@ __device__ __forceinline__ u32x4 shift_pick(const u32x4 lo, const u32x4 hi, int 
 }
 
 __global__ __launch_bounds__(kFlatThreads) void flatten_kernel(FlatBatch b, unsigned short* __restrict__ flat) {
-    // Which tensor owns this block: binary search over the block prefix.
+    const int64_t blk = xcd_block(blockIdx.x, gridDim.x);
+    if (blk >= b.first_block[b.count]) return;       // grid rounded up to the XCD count
+    // Which table entry owns this block: binary search over the prefix.
     int lo = 0, hi = b.count - 1;
-    const int bid = static_cast<int>(blockIdx.x);
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (b.first_block[mid] <= bid) lo = mid; else hi = mid - 1;
+        if (b.first_block[mid] <= blk) lo = mid; else hi = mid - 1;
     }
     const int t = lo;
-    const int jb = bid - b.first_block[t];
-    const int nblk = b.first_block[t + 1] - b.first_block[t];
+    const int64_t jb = blk - b.first_block[t];
     const unsigned short* src = b.src[t];
     const int64_t d0 = b.dst[t], n = b.n[t], d1 = d0 + n;
     // Aligned body [a0, a1) of the destination, head [d0, a0), tail [a1, d1).
@@ -367,32 +368,26 @@ __global__ __launch_bounds__(kFlatThreads) void flatten_kernel(FlatBatch b, unsi
     if (a1 < a0) a1 = a0;
     u32x4* dvec = reinterpret_cast<u32x4*>(flat);
     const int64_t nv = (a1 - a0) / 8;
+    const int64_t q = jb * kFlatThreads + threadIdx.x;   // body vector of this thread
     if (src == nullptr) {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        for (int64_t q = static_cast<int64_t>(jb) * kFlatThreads + threadIdx.x; q < nv;
-             q += static_cast<int64_t>(nblk) * kFlatThreads)
-            dvec[a0 / 8 + q] = z;
+        if (q < nv) dvec[a0 / 8 + q] = u32x4{0u, 0u, 0u, 0u};
         if (jb == 0) {
             if (threadIdx.x < a0 - d0) flat[d0 + threadIdx.x] = 0;
             if (threadIdx.x >= 8 && threadIdx.x - 8 < d1 - a1) flat[a1 + threadIdx.x - 8] = 0;
         }
         return;
     }
-    // Source element s of the tensor sits at aligned-vector element
-    // s + ms of `sbase`; the body's first source element is a0 - d0.
+    // Source element e of the entry sits at aligned-vector element e + ms
+    // of `sbase`; the body's first source element is a0 - d0.
     const int ms = static_cast<int>((reinterpret_cast<uintptr_t>(src) & 15u) >> 1);
     const u32x4* sbase = reinterpret_cast<const u32x4*>(src - ms);
-    const int64_t s0 = a0 - d0 + ms;        // aligned-space index of body start
+    const int64_t s0 = a0 - d0 + ms;        // aligned-space index of the body start
     const int k = static_cast<int>(s0 & 7);
     const int64_t sv0 = s0 >> 3;            // aligned vector holding it
-    for (int64_t q = static_cast<int64_t>(jb) * kFlatThreads + threadIdx.x; q < nv;
-         q += static_cast<int64_t>(nblk) * kFlatThreads) {
+    if (q < nv) {
         u32x4 o;
-        if (k == 0) {
-            o = sbase[sv0 + q];
-        } else {
-            o = shift_pick(sbase[sv0 + q], sbase[sv0 + q + 1], k);
-        }
+        if (k == 0) o = sbase[sv0 + q];
+        else o = shift_pick(sbase[sv0 + q], sbase[sv0 + q + 1], k);
         dvec[a0 / 8 + q] = o;
     }
     if (jb == 0) {
@@ -579,26 +574,44 @@ int zero_bucket_flatten(const zero_tensor_slot_t* slots, int32_t n_tensors, cons
     unsigned short* flat = static_cast<unsigned short*>(flat_dev);
     FlatBatch b;
     b.count = 0;
-    int32_t blocks = 0;
+    int64_t blocks = 0;
     auto flush = [&]() -> int {
         if (b.count == 0) return ZERO_OK;
-        b.first_block[b.count] = blocks;
-        hipLaunchKernelGGL(flatten_kernel, dim3(blocks), dim3(kFlatThreads), 0, st, b, flat);
+        b.first_block[b.count] = static_cast<int32_t>(blocks);
+        const int64_t grid = (blocks + kXcds - 1) / kXcds * kXcds;
+        hipLaunchKernelGGL(flatten_kernel, dim3(static_cast<unsigned>(grid)), dim3(kFlatThreads), 0, st,
+                           b, flat);
         b.count = 0;
         blocks = 0;
         return launch_error("flatten kernel launch");
     };
-    auto add = [&](const void* src, int64_t dst, int64_t n) -> int {
-        if (n <= 0) return ZERO_OK;
-        const int64_t nv = n / 8 + 2;
-        int64_t nb = (nv + kFlatVecPerBlock - 1) / kFlatVecPerBlock;
-        if (nb > kFlatMaxBlocksPerTensor) nb = kFlatMaxBlocksPerTensor;
-        b.src[b.count] = static_cast<const unsigned short*>(src);
+    // One table entry per piece of at most kFlatMaxPiece elements; a
+    // piece's blocks cover its aligned body vectors, at least one block
+    // (its head and tail).
+    auto add_piece = [&](const unsigned short* src, int64_t dst, int64_t n) -> int {
+        const int64_t a0 = (dst + 7) & ~int64_t(7);
+        const int64_t body = (dst + n) / 8 * 8 > a0 ? ((dst + n) / 8 * 8 - a0) / 8 : 0;
+        int64_t nb = (body + kFlatThreads - 1) / kFlatThreads;
+        if (nb < 1) nb = 1;
+        if (b.count == kFlatBatch || blocks + nb > (int64_t(1) << 30)) {
+            int rc = flush();
+            if (rc) return rc;
+        }
+        b.src[b.count] = src;
         b.dst[b.count] = dst;
         b.n[b.count] = n;
-        b.first_block[b.count] = blocks;
-        blocks += static_cast<int32_t>(nb);
-        if (++b.count == kFlatBatch) return flush();
+        b.first_block[b.count] = static_cast<int32_t>(blocks);
+        blocks += nb;
+        ++b.count;
+        return ZERO_OK;
+    };
+    auto add = [&](const void* src, int64_t dst, int64_t n) -> int {
+        const unsigned short* s16 = static_cast<const unsigned short*>(src);
+        for (int64_t done = 0; done < n; done += kFlatMaxPiece) {
+            const int64_t len = n - done < kFlatMaxPiece ? n - done : kFlatMaxPiece;
+            int rc = add_piece(s16 ? s16 + done : nullptr, dst + done, len);
+            if (rc) return rc;
+        }
         return ZERO_OK;
     };
     int rc;
