@@ -95,6 +95,8 @@ def lib():
             getattr(L, name).restype = None
         L.oracle_reduce.argtypes = [i32, vp, i32, i64, f32, vp, vp, vp]
         L.oracle_reduce.restype = None
+        L.oracle_reduce_accumulate.argtypes = [i32, vp, i32, i64, f32, vp, vp, vp]
+        L.oracle_reduce_accumulate.restype = None
         L.oracle_clip.argtypes = [f64, f64, vp, vp]
         L.oracle_clip.restype = i32
         L.oracle_adamw.argtypes = [i64, vp, vp, vp, vp, f64, f64, f64, f64,
@@ -195,6 +197,22 @@ def reduce(replicas, dtype: int, inv: float, sumsq: float = 0.0,
     return g, ss.value, of.value
 
 
+def reduce_accumulate(replicas, dtype: int, inv: float, g: np.ndarray, sumsq: float = 0.0,
+                      overflow: int = 0):
+    """Add one more micro-batch's reduced, unscaled slice into g (fp32, in
+    place); return (sumsq, overflow) of the updated g, accumulated."""
+    reps = [np.ascontiguousarray(r, dtype=np.uint16) for r in replicas]
+    n = reps[0].size
+    assert all(r.size == n for r in reps) and g.size == n
+    assert g.dtype == np.float32 and g.flags["C_CONTIGUOUS"]
+    arr = (ctypes.c_void_p * len(reps))(*[_ptr(r) for r in reps])
+    ss = ctypes.c_double(sumsq)
+    of = ctypes.c_int32(overflow)
+    lib().oracle_reduce_accumulate(len(reps), ctypes.addressof(arr), dtype, n, np.float32(inv),
+                                   _ptr(g), ctypes.addressof(ss), ctypes.addressof(of))
+    return ss.value, of.value
+
+
 def clip(sumsq: float, max_norm: float):
     """Return (applies, norm, coef)."""
     norm = ctypes.c_double()
@@ -282,14 +300,39 @@ def step(replica_flats, dtype: int, numel: int, world_size: int,
     state changes, and the caller must not advance t.  With cast=False the
     full buffer is left alone (for steps whose cast nobody reads).
     """
+    return step_accumulated([replica_flats], dtype, numel, world_size, alignment, masters,
+                            exp_avgs, exp_avg_sqs, full_params, hp, t, keep_grads, cast)
+
+
+def step_accumulated(micro_batches, dtype: int, numel: int, world_size: int,
+                     alignment: int, masters, exp_avgs, exp_avg_sqs, full_params,
+                     hp: Hyper, t: int, keep_grads: bool = False,
+                     cast: bool = True) -> StepInfo:
+    """One sharded step over an accumulation window of K micro-batches.
+
+    micro_batches: K lists of N replica flats (as `step` takes one).  For
+    each rank, micro-batch 1 sets the rank's fp32 reduced slice and each
+    later one adds to it; the norm, the overflow flag, clipping and AdamW
+    then act on the accumulated slice, as in `step`.
+    """
     s, padded, valid = partition(numel, world_size, alignment)
     inv = inv_scale(hp.loss_scale, hp.predivide)
     sumsq, overflow = 0.0, 0
     grads = []
     for r in range(world_size):
         lo, n = r * s, valid[r]
-        g, sumsq, overflow = reduce([f[lo:lo + n] for f in replica_flats],
-                                    dtype, inv, sumsq, overflow)
+        g = None
+        for k, flats in enumerate(micro_batches):
+            reps = [f[lo:lo + n] for f in flats]
+            last = k == len(micro_batches) - 1
+            if k == 0:
+                g, ss, of = reduce(reps, dtype, inv, sumsq if last else 0.0,
+                                   overflow if last else 0)
+            else:
+                ss, of = reduce_accumulate(reps, dtype, inv, g, sumsq if last else 0.0,
+                                           overflow if last else 0)
+            if last:
+                sumsq, overflow = ss, of
         grads.append(g)
     overflow = overflow or not math.isfinite(sumsq)
     applies, norm, coef = clip(sumsq, hp.max_grad_norm)

@@ -219,6 +219,35 @@ void oracle_reduce(int32_t n_replicas, const uint16_t* const* replicas,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Gradient accumulation.  [P1] §3.1 lists gradient_accumulation_steps; [P2]
+ * practice notes: accumulation simulates a large batch with small ones;
+ * [P3] technical insight: each GPU keeps only the gradient slice of its own
+ * parameters, so the accumulated gradient is the rank's slice.  Each later
+ * micro-batch's reduced, unscaled slice is added to the running fp32 slice;
+ * the flag and the sum of squares are those of the updated slice.        */
+void oracle_reduce_accumulate(int32_t n_replicas, const uint16_t* const* replicas,
+                              int32_t dtype, int64_t n, float inv_scale, float* g,
+                              double* sumsq, int32_t* overflow)
+{
+    const float* value = (dtype == ORACLE_FP16) ? f16_value : bf16_value;
+    double ss = *sumsq;
+    int32_t bad = *overflow;
+    for (int64_t i = 0; i < n; ++i) {
+        float acc = 0.0f;
+        for (int32_t r = 0; r < n_replicas; ++r) {
+            float x = value[replicas[r][i]];
+            acc = (r == 0) ? x : acc + x;
+        }
+        float gi = g[i] + acc * inv_scale;
+        g[i] = gi;
+        if (!isfinite(gi)) bad = 1;
+        ss += (double)gi * (double)gi;
+    }
+    *sumsq = ss;
+    *overflow = bad;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Global-norm clipping.  [P1] §6 configuration: gradient_clipping 1.0.
  * The factor max_norm / (norm + 1e-6) applies only when it is below one.  */
 int32_t oracle_clip(double sumsq, double max_norm, double* norm, double* coef)

@@ -26,6 +26,9 @@
  *   oracle_partition, oracle_bucket_plan      pinned (brute force, page numbers)
  *   oracle_*_to_f32, oracle_f32_to_*          pinned (exhaustive / library)
  *   oracle_reduce                             pinned (identity, N*g, fsum)
+ *   oracle_reduce_accumulate                  pinned (numpy fp32 sum over
+ *                                             micro-batches, one micro-batch,
+ *                                             sign of zero)
  *   oracle_clip                               pinned (library clip, closed form)
  *   oracle_adamw                              pinned (closed form, library AdamW)
  *   oracle_scaler_*                           parity unpinned by the pages:
@@ -82,6 +85,22 @@ void oracle_bf16_to_f32_array(int64_t n, const uint16_t* b, float* out);
 void oracle_reduce(int32_t n_replicas, const uint16_t* const* replicas,
                    int32_t dtype, int64_t n, float inv_scale, float* g,
                    double* sumsq, int32_t* overflow);
+
+/* ---- gradient accumulation over micro-batches --------------------------- *
+ * [P1] §3.1 configuration (gradient_accumulation_steps), [P2] practice notes
+ * (accumulation stands in for a larger batch), [P3] technical insight (each
+ * GPU keeps only the gradient slice of its own parameters).  Reading: every
+ * micro-batch is reduce-scattered, and the rank accumulates its own slice in
+ * fp32.  For micro-batch 2..K of a window, for i in [0, n):
+ *   acc  = replica[0][i] + replica[1][i] + ... (fp32, left to right)
+ *   g[i] = g[i] + acc * inv_scale                (fp32, g read and written)
+ *   *overflow |= g[i] is inf or nan
+ *   *sumsq    += (double)g[i] * (double)g[i]     (fp64, index order)
+ * Micro-batch 1 is oracle_reduce, which sets g.  The flags and sums of the
+ * last micro-batch are the ones the step uses. */
+void oracle_reduce_accumulate(int32_t n_replicas, const uint16_t* const* replicas,
+                              int32_t dtype, int64_t n, float inv_scale, float* g,
+                              double* sumsq, int32_t* overflow);
 
 /* ---- gradient clipping ([P1] §6 configuration: gradient_clipping 1.0) --- *
  * norm = sqrt(sumsq); coef = max_norm / (norm + 1e-6); the gradient is

@@ -31,7 +31,9 @@ MUTANTS = {
                                 "(p[i] - step_size * (m1 / d)) * decay * decay"),
     "ties_away_from_zero": ("nearbyint(units)", "round(units)"),
     "reduce_in_double": ("float acc = 0.0f;", "double acc = 0.0;"),
-    "unscale_dropped": ("float gi = acc * inv_scale;", "float gi = acc;"),
+    "unscale_dropped": ("float gi = acc * inv_scale;\n        g[i] = gi;", "float gi = acc;\n        g[i] = gi;"),
+    "accumulate_overwrites": ("float gi = g[i] + acc * inv_scale;", "float gi = acc * inv_scale;"),
+    "accumulate_unscale_dropped": ("float gi = g[i] + acc * inv_scale;", "float gi = g[i] + acc;"),
     "nan_not_flagged": ("if (!isfinite(gi)) bad = 1;", "if (isinf(gi)) bad = 1;"),
     "clip_eps_dropped": ("max_norm / (*norm + 1e-6)", "max_norm / (*norm)"),
     "partition_floor_not_ceil": ("(numel % world_size != 0 ? 1 : 0)", "0"),
@@ -48,7 +50,8 @@ MUTANTS = {
 def test_pins_kill_mutant(name, tmp_path):
     before, after = MUTANTS[name]
     src = open(SRC).read()
-    assert src.count(before) == 1, "mutation site not found: " + name
+    # a site shared by the plain and the accumulating reduce is mutated in both
+    assert src.count(before) >= 1, "mutation site not found: " + name
     mutant_src = tmp_path / "zero_oracle.c"
     mutant_src.write_text(src.replace(before, after))
     lib = str(tmp_path / "liboracle_mutant.so")

@@ -341,3 +341,85 @@ def test_overflow_anywhere_skips_every_rank(where):
     assert info.overflow and info.skipped
     for a, b in zip(before, ps_ + ms + vs + [full]):
         assert np.array_equal(a, b)
+
+
+# ----------------------------------------------------- gradient accumulation
+@pytest.mark.parametrize("dtype", [oracle.FP16, oracle.BF16])
+def test_accumulate_adds_the_reduced_micro_batch(dtype):
+    # The accumulated slice equals the first micro-batch's reduced slice
+    # plus the second's, added in fp32 by numpy; the sum of squares is that
+    # of the updated slice.
+    rng = np.random.default_rng(21)
+    n, N = 3001, 4
+    mb1 = [rand_codes(rng, n, dtype, sigma=10.0 ** rng.uniform(-3, 1)) for _ in range(N)]
+    mb2 = [rand_codes(rng, n, dtype, sigma=10.0 ** rng.uniform(-3, 1)) for _ in range(N)]
+    inv = oracle.inv_scale(4.0)
+    g1, _, _ = oracle.reduce(mb1, dtype, inv)
+    g2, _, _ = oracle.reduce(mb2, dtype, inv)
+    acc = g1.copy()
+    ss, of = oracle.reduce_accumulate(mb2, dtype, inv, acc)
+    assert np.array_equal(acc, np.add(g1, g2, dtype=np.float32))
+    assert of == 0
+    assert ss == pytest.approx(math.fsum(float(v) * float(v) for v in acc), rel=1e-12)
+
+
+def test_accumulate_exact_closed_form():
+    # Dyadic values whose sums are exact: K micro-batches of N equal
+    # replicas give exactly K * N * x.
+    x = np.array([0.5, -0.25, 3.0, 1.0 / 64, -7.0, 0.0], np.float32)
+    codes = oracle.f32_to_bf16(x)
+    N, K = 4, 5
+    g, _, _ = oracle.reduce([codes] * N, oracle.BF16, oracle.inv_scale(1.0))
+    for _ in range(K - 1):
+        oracle.reduce_accumulate([codes] * N, oracle.BF16, oracle.inv_scale(1.0), g)
+    assert np.array_equal(g, x * np.float32(K * N))
+
+
+def test_accumulate_sign_of_zero_and_overflow():
+    neg0 = oracle.f32_to_f16(np.array([-0.0], np.float32))
+    g, _, _ = oracle.reduce([neg0], oracle.FP16, oracle.inv_scale(1.0))
+    assert np.signbit(g[0])                     # the first micro-batch sets g
+    oracle.reduce_accumulate([oracle.f32_to_f16(np.array([0.0], np.float32))], oracle.FP16,
+                             oracle.inv_scale(1.0), g)
+    assert g[0] == 0 and not np.signbit(g[0])   # -0 + 0 = +0 in round-to-nearest
+    # an inf in an early micro-batch survives later finite ones
+    inf = oracle.f32_to_f16(np.array([np.inf, 1.0], np.float32))
+    fin = oracle.f32_to_f16(np.array([1.0, 1.0], np.float32))
+    g, _, of = oracle.reduce([inf], oracle.FP16, oracle.inv_scale(1.0))
+    ss, of = oracle.reduce_accumulate([fin], oracle.FP16, oracle.inv_scale(1.0), g)
+    assert of == 1 and np.isinf(g[0]) and g[1] == 2.0
+
+
+def test_accumulated_step_equals_one_step_over_all_gradients_when_sums_are_exact():
+    # With dyadic gradients every sum is exact, so K micro-batches of N
+    # replicas give the same step as one reduce over all K * N gradients.
+    rng = np.random.default_rng(22)
+    P, N, A, K = 5003, 4, 8, 3
+    s, padded, valid = oracle.partition(P, N, A)
+
+    def dyadic():
+        f = np.zeros(padded, np.uint16)
+        f[:P] = oracle.f32_to_bf16((rng.integers(-64, 65, P) / 1024.0).astype(np.float32))
+        return f
+
+    micro = [[dyadic() for _ in range(N)] for _ in range(K)]
+    master = (rng.standard_normal(padded) * 0.02).astype(np.float32)
+    hp = oracle.Hyper(max_grad_norm=1.0)
+
+    def run(fn, batches):
+        ps = split(master, N, s)
+        ms = split(np.zeros(padded, np.float32), N, s)
+        vs = split(np.zeros(padded, np.float32), N, s)
+        full = np.zeros(padded, np.uint16)
+        info = fn(batches, oracle.BF16, P, N, A, ps, ms, vs, full, hp, 1, keep_grads=True)
+        return info, ps, ms, vs, full
+
+    a = run(oracle.step_accumulated, micro)
+    b = run(oracle.step, [f for mb in micro for f in mb])
+    assert a[0].sumsq == b[0].sumsq and a[0].clipped and b[0].clipped
+    for x, y in zip(a[0].grads, b[0].grads):
+        assert np.array_equal(x, y)
+    for xs, ys in zip(a[1:4], b[1:4]):
+        for x, y in zip(xs, ys):
+            assert np.array_equal(x, y)
+    assert np.array_equal(a[4], b[4])
