@@ -43,6 +43,10 @@ def parse():
                     help="shard13b: rank 0 of the 13B/8 flat model (the headline); "
                          "ragged: 2000 tensors flattened bucket by bucket, then the step of "
                          "all 8 ranks")
+    ap.add_argument("--micro-batches", type=int, default=1,
+                    help="shard13b: gradient-accumulation window K; each step reduces K "
+                         "micro-batches (the first sets the fp32 slice, the others add to it) "
+                         "before the combine and AdamW")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 28,
                     help="elements of the shard the CPU oracle is timed on")
@@ -102,26 +106,35 @@ def run_shard13b(args, torch, Z, W):
     w, s, valid = st["w"], st["s"], st["valid"]
     torch.cuda.synchronize()
 
-    def step_args(t):
+    MB = args.micro_batches
+
+    def step_args(t, accumulate=False):
         return Z.StepArgs(world_size=w.world_size, rank=0, shard_numel=s, valid_numel=valid,
                           replica_grads=st["grads"], master=st["master"], exp_avg=st["m"],
                           exp_avg_sq=st["v"], full_params=st["full"], workspace=st["ws"],
                           lr=w.lr, weight_decay=w.weight_decay, step=t,
-                          max_grad_norm=w.max_grad_norm)
+                          max_grad_norm=w.max_grad_norm, accumulate=accumulate)
+
+    def fused_step(t):
+        for j in range(MB - 1):
+            Z.zero_shard_accumulate(step_args(t, accumulate=j > 0), stream)
+        return Z.zero_shard_step(step_args(t, accumulate=MB > 1), stream=stream)
 
     stream = torch.cuda.current_stream()
     t = 1
     for _ in range(args.warmup):
-        Z.zero_shard_step(step_args(t), stream=stream)
+        fused_step(t)
         t += 1
     torch.cuda.synchronize()
     K = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     wall0 = time.perf_counter()
     for k in range(K):
-        a = step_args(t)
+        a = step_args(t, accumulate=MB > 1)
         e = ev[k]
         e[0].record(stream)
+        for j in range(MB - 1):
+            Z.zero_shard_accumulate(step_args(t, accumulate=j > 0), stream)
         Z.zero_shard_reduce(a, 0, st["partials"], stream)
         e[1].record(stream)
         Z.zero_shard_combine(st["partials"], 1, w.max_grad_norm, st["glob"], stream)
@@ -142,14 +155,17 @@ def run_shard13b(args, torch, Z, W):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(K):
-        Z.zero_shard_step(step_args(t), stream=stream)
+        fused_step(t)
         t += 1
     e1.record(stream)
     torch.cuda.synchronize()
     fused_ms = e0.elapsed_time(e1) / K
-    info = Z.zero_shard_step(step_args(t), want_info=True)
+    for j in range(MB - 1):
+        Z.zero_shard_accumulate(step_args(t, accumulate=j > 0), stream)
+    info = Z.zero_shard_step(step_args(t, accumulate=MB > 1), want_info=True)
     nrep = st["nrep"]
-    bytes_reduce = valid * (2 * nrep + 4)
+    # pass 1 of the first micro-batch writes the fp32 slice; later ones also read it
+    bytes_reduce = valid * (MB * 2 * nrep + 4 + (MB - 1) * 8)
     bytes_apply = valid * (16 + 14)
     bytes_step = bytes_reduce + bytes_apply
     res = dict(ms=ms, wall_ms=wall * 1e3 / K, step_ms_min=per_step[0],
@@ -332,12 +348,14 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": W.SHARD_13B_OF_8.name, "shard_numel": r["st"]["s"],
-                   "world_size": 8, "replicas": 8, "grad_dtype": "bf16", "param_dtype": "bf16",
+                   "world_size": 8, "replicas": 8, "micro_batches": args.micro_batches,
+                   "grad_dtype": "bf16", "param_dtype": "bf16",
                    "lr": 6e-5, "weight_decay": 0.01, "max_grad_norm": 1.0},
         "hbm_gbps": step_gbps,
         "hbm_frac": step_gbps / HBM_PEAK_GBPS,
         "bytes_per_step": r["bytes_step"],
-        "kernels_ms": {"reduce": r["reduce_ms"], "combine": r["combine_ms"], "apply": r["apply_ms"]},
+        "kernels_ms": {"reduce_and_fold": r["reduce_ms"], "combine": r["combine_ms"],
+                       "apply": r["apply_ms"]},
         "fused_call_ms_per_step": r["fused_ms"],
         "step_ms": {"min": r["step_ms_min"], "median": r["step_ms_median"], "max": r["step_ms_max"]},
         "wall_ms_per_step": r["wall_ms"],
@@ -347,7 +365,7 @@ def main():
         "reduce_gbps": r["bytes_reduce"] / (r["reduce_ms"] * 1e-3) / 1e9,
         "step_check": {"norm": r["norm"], "clipped": r["clipped"], "overflow": r["overflow"]},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.micro_batches == 1:
         log("timing the CPU oracle on a sample")
         out["cpu_baseline"] = cpu_baseline_shard13b(args, torch, W, r["st"])
     print(json.dumps(out), flush=True)

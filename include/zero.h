@@ -162,7 +162,10 @@ typedef struct {
     int32_t grad_dtype;       /* ZERO_FP16 or ZERO_BF16                    */
     int32_t param_dtype;      /* ZERO_FP16 or ZERO_BF16                    */
     int32_t n_replicas;       /* gradients summed, 1..ZERO_MAX_REPLICAS    */
-    int32_t reserved0;
+    /* 0: pass 1 sets the workspace's fp32 gradient slice to this reduce's
+     * result; 1: it adds the result to the slice already there (micro-batch
+     * 2..K of a gradient-accumulation window, see zero_shard_accumulate).  */
+    int32_t accumulate;
     /* host array of n_replicas device pointers; entry i points at this
      * rank's slice (flat element rank*shard_numel) of replica i's flat
      * gradient buffer.  valid_numel values are read from each.            */
@@ -221,6 +224,21 @@ size_t zero_partials_bytes(int32_t n_slots);
 int zero_shard_reduce(const zero_step_args* a, int32_t slot,
                       void* partials_dev, void* stream);
 
+/* Gradient accumulation over micro-batches: [P1] §3.1 configuration
+ * (gradient_accumulation_steps), [P2] practice notes (accumulating small
+ * batches stands in for a large one), [P3] technical insight (each GPU keeps
+ * only the gradient slice of its own parameters).  Every micro-batch is
+ * reduced over the replicas as in zero_shard_reduce, and the rank's fp32
+ * slice in the workspace accumulates them: with a->accumulate = 0 the slice
+ * is set, with 1 it becomes
+ *   g[i] = g[i] + (g_0[i] + ... + g_{R-1}[i]) * fp32(1 / (loss_scale * grad_predivide))
+ * This call runs that pass only, for the micro-batches before the last of a
+ * window; the last one goes through zero_shard_step (or zero_shard_reduce,
+ * combine and apply) with accumulate = 1, so that the norm, the overflow
+ * flag, clipping and AdamW act on the accumulated slice.  The loss scale
+ * must stay the same within a window.  Errors: as zero_shard_step. */
+int zero_shard_accumulate(const zero_step_args* a, void* stream);
+
 /* Combine slots [0, n_slots) of partials_dev in a fixed order into one
  * zero_global_t at global_dev (device): the global sum of squares and norm,
  * the overflow flag (any slot flagged, or a non-finite sum), and the clip
@@ -249,7 +267,7 @@ int zero_shard_apply(const zero_step_args* a, const void* global_dev,
  * combine's result into *info (host); otherwise it does not wait.
  * Errors: world_size < 1, rank outside [0, world_size), valid_numel outside
  * [0, shard_numel], shard_numel not a multiple of 8, bad dtype, n_replicas
- * outside [1, ZERO_MAX_REPLICAS], step < 1, loss_scale or grad_predivide
+ * outside [1, ZERO_MAX_REPLICAS], accumulate not 0 or 1, step < 1, loss_scale or grad_predivide
  * <= 0, lr, betas or eps out of range, a NULL pointer -> ZERO_EINVAL; a
  * misaligned device pointer -> ZERO_EALIGN; workspace_bytes too small ->
  * ZERO_ESIZE; a HIP failure -> ZERO_EDEVICE.  When valid_numel is 0 the

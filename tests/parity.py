@@ -106,6 +106,8 @@ class Spec:
     dynamic_scale: bool = False            # fp16 loss scaler drives the scale
     scaler_args: tuple = (16, 100, 2, 1.0)
     poison: Optional[List[Optional[W.Poison]]] = None
+    micro_batches: int = 1                 # gradient-accumulation window
+    poison_micro: int = 0                  # micro-batch the poison lands in
     name: str = "case"
     seed: int = 0
 
@@ -156,20 +158,28 @@ def run(spec: Spec, device="cuda", check_every_step: bool = True,
             assert sc_orc.scale == scale, (step, sc_orc.scale, scale)
         hp.loss_scale = scale
         o_hp.loss_scale = scale
-        for i in range(nrep):
-            W.flat_normal(world.grads[i], world.lo, P, spec.grad_sigma,
-                          ("grad", spec.name, spec.seed, step, i), scale=scale)
-        if spec.poison and spec.poison[step] is not None:
-            W.plant(world.grads[spec.poison[step].replica], spec.poison[step])
-        o_grads = [u16(gbuf) for gbuf in world.grads]     # generator output
-        world.step(hp, t_lib)
+        K = spec.micro_batches
+        micro = []
+        for j in range(K):
+            for i in range(nrep):
+                key = ("grad", spec.name, spec.seed, step, i) if K == 1 else \
+                    ("grad", spec.name, spec.seed, step, i, j)
+                W.flat_normal(world.grads[i], world.lo, P, spec.grad_sigma, key, scale=scale)
+            if spec.poison and spec.poison[step] is not None and spec.poison_micro == j:
+                W.plant(world.grads[spec.poison[step].replica], spec.poison[step])
+            micro.append([u16(gbuf) for gbuf in world.grads])     # generator output
+            if j < K - 1:
+                world.accumulate(hp, first=j == 0)
+            else:
+                world.step(hp, t_lib, accumulate=K > 1)
         res = world.result()
         last = step == spec.steps - 1
         compare = check_every_step or last
         # Every step overwrites all real elements of the full buffer, so the
         # oracle casts only on the steps whose result is compared.
-        info = oracle.step(o_grads, odt, P, spec.world_size, spec.alignment, o_master, o_m,
-                           o_v, o_full, o_hp, t_orc, keep_grads=compare, cast=compare)
+        info = oracle.step_accumulated(micro, odt, P, spec.world_size, spec.alignment, o_master,
+                                       o_m, o_v, o_full, o_hp, t_orc, keep_grads=compare,
+                                       cast=compare)
         if compare and info.overflow and t_orc > 1:
             # a skipped step leaves the last applied step's cast in place
             s_, _, valid_ = oracle.partition(P, spec.world_size, spec.alignment)

@@ -240,3 +240,12 @@ def test_workspace_and_partials_sizes():
         # reduced gradient, one 16-byte partial per 1024 elements, a slot, the result
         assert ws >= 4 * s + 16 * -(-s // 1024) + slot + 32 and ws % 256 == 0
     assert Z.zero_shard_workspace_bytes(1_625_000_064) < 4 * 1_625_000_064 * 1.01
+
+
+def test_accumulate_flag_must_be_zero_or_one():
+    a = good_args()
+    c = a.c_args()
+    c.accumulate = 2
+    for rc in (Z.lib().zero_shard_step(ctypes.byref(c), 0.0, 0, None, None),
+               Z.lib().zero_shard_accumulate(ctypes.byref(c), None)):
+        assert rc == Z.ZERO_EINVAL and "accumulate" in Z.zero_last_error()

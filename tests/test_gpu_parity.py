@@ -258,3 +258,64 @@ def test_flatten_pieces_beyond_one_table_entry():
     assert bool((flat[:5] == 0x1357).all()), "wrote before the slot"
     assert bool((flat[5 + n:n + pad] == 0).all()), "padding not zeroed"
     assert bool((flat[n + pad:] == 0x1357).all()), "wrote past flat_numel"
+
+
+# ---------------------------------------------------- gradient accumulation
+ACC_CASES = [
+    # (numel, world, alignment, dtype, sigma, loss_scale, micro_batches, steps)
+    (5, 4, 8, BF16, 1e-2, 1.0, 2, 2),              # empty ranks, tail only
+    (4097, 4, 8, FP16, 1e-3, 2.0**12, 3, 2),
+    (100_003, 8, 128, BF16, 1e-3, 1.0, 4, 2),
+    (1_000_003, 2, 128, BF16, 3e-2, 1.0, 2, 3),
+]
+
+
+@pytest.mark.parametrize("case", ACC_CASES, ids=["P%d-N%d-%s-K%d" % (c[0], c[1], str(c[3])[6:], c[6])
+                                                 for c in ACC_CASES])
+def test_accumulation_window_matches_oracle(case):
+    numel, world, align, dt, sigma, scale, K, steps = case
+    say("accumulation %s" % (case,))
+    spec = parity.Spec(numel=numel, world_size=world, alignment=align, grad_dtype=dt,
+                       grad_sigma=sigma, steps=steps, micro_batches=K,
+                       name="acc-%d-%d-%d" % (numel, world, K), hp=Hyper(loss_scale=scale))
+    rep = parity.run(spec)
+    say("norm rel err %.2e, bitwise state %.6f" % (rep.norm_rel_err, rep.state_bitwise))
+
+
+@pytest.mark.parametrize("micro", [0, 1, 2])
+def test_accumulation_poison_in_any_micro_batch_skips(micro):
+    numel, world = 20_011, 4
+    say("accumulation, poison in micro-batch %d" % micro)
+    sched = [None, W.Poison(1, 1, 777, 2), None]
+    spec = parity.Spec(numel=numel, world_size=world, alignment=8, grad_dtype=FP16,
+                       grad_sigma=1e-3, steps=3, poison=sched, poison_micro=micro,
+                       micro_batches=3, dynamic_scale=True, scaler_args=(10, 2, 1, 1.0),
+                       name="acc-poison")
+    rep = parity.run(spec)
+    assert rep.skipped == 1
+
+
+def test_accumulate_then_fused_step_equals_split_calls():
+    say("zero_shard_accumulate + zero_shard_step vs the split world")
+    numel, K = 123_457, 3
+    w1 = SimulatedWorld(numel, 1, n_replicas=8, alignment=128, grad_dtype=BF16)
+    w2 = SimulatedWorld(numel, 1, n_replicas=8, alignment=128, grad_dtype=BF16)
+    for w in (w1, w2):
+        W.flat_normal(w.master[0], 0, numel, 0.02, ("accm",))
+    hp = Hyper()
+    for j in range(K):
+        for w in (w1, w2):
+            for i in range(8):
+                W.flat_normal(w.grads[i], 0, numel, 1e-2, ("acc", i, j))
+        if j < K - 1:
+            w1.accumulate(hp, first=j == 0)
+            Z.zero_shard_accumulate(w2.rank_args(0, hp, 1, accumulate=j > 0))
+        else:
+            w1.step(hp, 1, accumulate=True)
+            info = Z.zero_shard_step(w2.rank_args(0, hp, 1, accumulate=True), want_info=True)
+    r1 = w1.result()
+    assert (info.sumsq, info.coef, info.overflow) == (r1.sumsq, r1.coef, r1.overflow)
+    # real elements only: the workspace's padding tail is never written
+    for a, b in ((w1.master[0], w2.master[0]), (w1.exp_avg[0], w2.exp_avg[0]),
+                 (w1.reduced_grad(0), w2.reduced_grad(0))):
+        parity.assert_bitwise("fused vs split", parity.f32(a[:numel]), parity.f32(b[:numel]))

@@ -23,7 +23,7 @@ __all__ = [
     "ZERO_FP16", "ZERO_BF16", "ZERO_MAX_REPLICAS", "ZeroError", "lib",
     "zero_last_error", "zero_partition", "zero_partition_valid_numel",
     "zero_bucket_plan", "zero_bucket_flatten", "zero_shard_workspace_bytes",
-    "zero_partials_bytes", "zero_shard_reduce", "zero_shard_combine",
+    "zero_partials_bytes", "zero_shard_reduce", "zero_shard_accumulate", "zero_shard_combine",
     "zero_shard_apply", "zero_shard_step", "zero_loss_scaler_init",
     "zero_loss_scaler_update", "StepArgs", "dtype_code", "GLOBAL_BYTES",
 ]
@@ -166,6 +166,7 @@ class StepArgs:
     max_grad_norm: float = 1.0
     grad_dtype: Optional[int] = None
     param_dtype: Optional[int] = None
+    accumulate: bool = False
 
     def c_args(self) -> zero_step_args:
         reps = list(self.replica_grads)
@@ -179,6 +180,7 @@ class StepArgs:
         a.param_dtype = dtype_code(self.param_dtype if self.param_dtype is not None
                                    else self.full_params.dtype)
         a.n_replicas = len(reps)
+        a.accumulate = 1 if self.accumulate else 0
         a.replica_grad = ctypes.cast(self._ptrs, ctypes.POINTER(_abi.vp))
         a.master = _dptr(self.master)
         a.exp_avg = _dptr(self.exp_avg)
@@ -204,6 +206,13 @@ def _args(a) -> zero_step_args:
 def zero_shard_reduce(args, slot: int, partials, stream=None) -> None:
     check(lib().zero_shard_reduce(ctypes.byref(_args(args)), slot, _dptr(partials),
                                   _stream(stream)), "zero_shard_reduce")
+
+
+def zero_shard_accumulate(args, stream=None) -> None:
+    """Pass 1 only, into the rank's workspace (micro-batches before the last
+    of an accumulation window; args.accumulate selects set or add)."""
+    check(lib().zero_shard_accumulate(ctypes.byref(_args(args)), _stream(stream)),
+          "zero_shard_accumulate")
 
 
 def zero_shard_combine(partials, n_slots: int, max_grad_norm: float, global_buf,

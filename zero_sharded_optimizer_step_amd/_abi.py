@@ -41,7 +41,7 @@ class zero_bucket_t(ctypes.Structure):
 class zero_step_args(ctypes.Structure):
     _fields_ = [("world_size", i32), ("rank", i32), ("shard_numel", i64),
                 ("valid_numel", i64), ("grad_dtype", i32), ("param_dtype", i32),
-                ("n_replicas", i32), ("reserved0", i32),
+                ("n_replicas", i32), ("accumulate", i32),
                 ("replica_grad", ctypes.POINTER(vp)),
                 ("master", vp), ("exp_avg", vp), ("exp_avg_sq", vp),
                 ("full_params", vp), ("workspace", vp), ("workspace_bytes", sz),
@@ -76,6 +76,7 @@ _PROTOTYPES = {
     "zero_shard_workspace_bytes": (sz, [i64]),
     "zero_partials_bytes": (sz, [i32]),
     "zero_shard_reduce": (ctypes.c_int, [ctypes.POINTER(zero_step_args), i32, vp, vp]),
+    "zero_shard_accumulate": (ctypes.c_int, [ctypes.POINTER(zero_step_args), vp]),
     "zero_shard_combine": (ctypes.c_int, [vp, i32, f64, vp, vp]),
     "zero_shard_apply": (ctypes.c_int, [ctypes.POINTER(zero_step_args), vp, vp]),
     "zero_shard_step": (ctypes.c_int, [ctypes.POINTER(zero_step_args), f64, i32,

@@ -41,6 +41,8 @@ int validate_step_args(const zero_step_args* a) {
     if (a->n_replicas < 1 || a->n_replicas > ZERO_MAX_REPLICAS)
         return fail(ZERO_EINVAL, "n_replicas %d outside [1, %d]", a->n_replicas,
                     ZERO_MAX_REPLICAS);
+    if (a->accumulate != 0 && a->accumulate != 1)
+        return fail(ZERO_EINVAL, "accumulate %d is not 0 or 1", a->accumulate);
     if (a->step < 1) return fail(ZERO_EINVAL, "step %lld < 1", (long long)a->step);
     if (!finite_positive(a->loss_scale))
         return fail(ZERO_EINVAL, "loss_scale must be finite and > 0");

@@ -133,7 +133,9 @@ __device__ __forceinline__ void sum_quad(const ReplicaPtrs& reps, int nrep, int6
     }
 }
 
-template <int DT, int NR>
+// With ACC the result is added to the slice already in g (gradient
+// accumulation over micro-batches; [P1] §3.1 gradient_accumulation_steps).
+template <int DT, int NR, bool ACC>
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(
     ReplicaPtrs reps, int nrep, int64_t n_valid, float inv_scale, float* __restrict__ g,
     Partial* __restrict__ partials) {
@@ -144,11 +146,14 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(
     int bad = 0;
     if (q < full) {
         float acc[4];
+        f32x4 prev;
+        if constexpr (ACC) prev = reinterpret_cast<const f32x4*>(g)[q];
         sum_quad<DT, NR>(reps, nrep, q, acc);
         f32x4 o;
         #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const float gk = acc[k] * inv_scale;
+            float gk = acc[k] * inv_scale;
+            if constexpr (ACC) gk = prev[k] + gk;
             bad |= !finite(gk);
             ss += static_cast<double>(gk) * static_cast<double>(gk);
             o[k] = gk;
@@ -163,7 +168,8 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(
                 const float x = lo_to_f32<DT>(base[i]);
                 acc = (r == 0) ? x : acc + x;
             }
-            const float gi = acc * inv_scale;
+            float gi = acc * inv_scale;
+            if constexpr (ACC) gi = g[i] + gi;
             bad |= !finite(gi);
             ss += static_cast<double>(gi) * static_cast<double>(gi);
             g[i] = gi;
@@ -406,27 +412,27 @@ int launch_error(const char* what) {
     return ZERO_OK;
 }
 
-template <int DT>
+template <int DT, bool ACC>
 void launch_reduce_dt(const ReplicaPtrs& reps, int nrep, int64_t n_valid, float inv, float* g,
                       Partial* parts, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(reduce_blocks_for(n_valid)));
-#define ZERO_REDUCE_CASE(NR)                                                                       \
-    case NR:                                                                                       \
-        hipLaunchKernelGGL((reduce_kernel<DT, NR>), grid, dim3(kReduceThreads), 0, st, reps, nrep, \
-                           n_valid, inv, g, parts);                                                \
+#define ZERO_REDUCE_CASE(NR)                                                                   \
+    case NR:                                                                                   \
+        hipLaunchKernelGGL((reduce_kernel<DT, NR, ACC>), grid, dim3(kReduceThreads), 0, st, reps, \
+                           nrep, n_valid, inv, g, parts);                                      \
         break;
     switch (nrep) {
         ZERO_REDUCE_CASE(1) ZERO_REDUCE_CASE(2) ZERO_REDUCE_CASE(3) ZERO_REDUCE_CASE(4)
         ZERO_REDUCE_CASE(5) ZERO_REDUCE_CASE(6) ZERO_REDUCE_CASE(7) ZERO_REDUCE_CASE(8)
         default:
-            hipLaunchKernelGGL((reduce_kernel<DT, 0>), grid, dim3(kReduceThreads), 0, st, reps, nrep,
-                               n_valid, inv, g, parts);
+            hipLaunchKernelGGL((reduce_kernel<DT, 0, ACC>), grid, dim3(kReduceThreads), 0, st, reps,
+                               nrep, n_valid, inv, g, parts);
     }
 #undef ZERO_REDUCE_CASE
 }
 
-// Pass 1 into the workspace, then the fold of its block partials into `slot`.
-int launch_reduce(const zero_step_args* a, unsigned char* slot, hipStream_t st) {
+// Pass 1 into the workspace; with fold, its block partials then go to `slot`.
+int launch_pass1(const zero_step_args* a, hipStream_t st) {
     ReplicaPtrs reps;
     for (int r = 0; r < ZERO_MAX_REPLICAS; ++r)
         reps.p[r] = r < a->n_replicas ? static_cast<const u32x2*>(a->replica_grad[r]) : nullptr;
@@ -434,13 +440,24 @@ int launch_reduce(const zero_step_args* a, unsigned char* slot, hipStream_t st) 
     unsigned char* ws = static_cast<unsigned char*>(a->workspace);
     float* g = reinterpret_cast<float*>(ws);
     Partial* parts = reinterpret_cast<Partial*>(ws + ws_blocks_offset(a->shard_numel));
-    if (a->grad_dtype == ZERO_BF16)
-        launch_reduce_dt<ZERO_BF16>(reps, a->n_replicas, a->valid_numel, inv, g, parts, st);
-    else
-        launch_reduce_dt<ZERO_FP16>(reps, a->n_replicas, a->valid_numel, inv, g, parts, st);
-    int rc = launch_error("reduce kernel launch");
+    const bool bf = a->grad_dtype == ZERO_BF16;
+    if (a->accumulate) {
+        if (bf) launch_reduce_dt<ZERO_BF16, true>(reps, a->n_replicas, a->valid_numel, inv, g, parts, st);
+        else launch_reduce_dt<ZERO_FP16, true>(reps, a->n_replicas, a->valid_numel, inv, g, parts, st);
+    } else {
+        if (bf) launch_reduce_dt<ZERO_BF16, false>(reps, a->n_replicas, a->valid_numel, inv, g, parts, st);
+        else launch_reduce_dt<ZERO_FP16, false>(reps, a->n_replicas, a->valid_numel, inv, g, parts, st);
+    }
+    return launch_error("reduce kernel launch");
+}
+
+// Pass 1 into the workspace, then the fold of its block partials into `slot`.
+int launch_reduce(const zero_step_args* a, unsigned char* slot, hipStream_t st) {
+    int rc = launch_pass1(a, st);
     if (rc) return rc;
     const int64_t nb = reduce_blocks_for(a->valid_numel);
+    const Partial* parts = reinterpret_cast<const Partial*>(static_cast<unsigned char*>(a->workspace) +
+                                                            ws_blocks_offset(a->shard_numel));
     hipLaunchKernelGGL(fold_kernel, dim3(fold_blocks_for(nb)), dim3(256), 0, st, parts, nb, slot);
     return launch_error("fold kernel launch");
 }
@@ -504,6 +521,13 @@ int zero_shard_reduce(const zero_step_args* a, int32_t slot, void* partials_dev,
     if (!aligned16(partials_dev)) return fail(ZERO_EALIGN, "partials_dev is not 16-byte aligned");
     unsigned char* s = static_cast<unsigned char*>(partials_dev) + static_cast<size_t>(slot) * kSlotBytes;
     return launch_reduce(a, s, static_cast<hipStream_t>(stream));
+}
+
+int zero_shard_accumulate(const zero_step_args* a, void* stream) {
+    clear_error();
+    int rc = validate_step_args(a);
+    if (rc) return rc;
+    return launch_pass1(a, static_cast<hipStream_t>(stream));
 }
 
 int zero_shard_combine(const void* partials_dev, int32_t n_slots, double max_grad_norm,

@@ -15,8 +15,8 @@ from typing import Optional, Sequence
 import torch
 
 from . import (GLOBAL_BYTES, StepArgs, zero_global_t, zero_partials_bytes, zero_partition,
-               zero_partition_valid_numel, zero_shard_apply, zero_shard_combine,
-               zero_shard_reduce, zero_shard_workspace_bytes)
+               zero_partition_valid_numel, zero_shard_accumulate, zero_shard_apply,
+               zero_shard_combine, zero_shard_reduce, zero_shard_workspace_bytes)
 
 
 @dataclass
@@ -74,7 +74,7 @@ class SimulatedWorld:
         off = rank * self.s - self.lo
         return self.grads[replica][off:off + self.s]
 
-    def rank_args(self, k: int, hp: Hyper, t: int) -> StepArgs:
+    def rank_args(self, k: int, hp: Hyper, t: int, accumulate: bool = False) -> StepArgs:
         r = self.ranks[k]
         return StepArgs(world_size=self.world_size, rank=r, shard_numel=self.s,
                         valid_numel=self.valid[r],
@@ -85,11 +85,20 @@ class SimulatedWorld:
                         eps=hp.eps, weight_decay=hp.weight_decay, step=t,
                         loss_scale=hp.loss_scale, grad_predivide=hp.grad_predivide,
                         max_grad_norm=hp.max_grad_norm, grad_dtype=self.grad_dtype,
-                        param_dtype=self.param_dtype)
+                        param_dtype=self.param_dtype, accumulate=accumulate)
 
-    def step(self, hp: Hyper, t: int, stream=None) -> None:
-        """Queue one optimizer step of every simulated rank (no host wait)."""
-        args = [self.rank_args(k, hp, t) for k in range(len(self.ranks))]
+    def accumulate(self, hp: Hyper, first: bool, stream=None) -> None:
+        """Queue pass 1 only for every simulated rank: a micro-batch before
+        the last of an accumulation window (`first` sets the slices, later
+        ones add to them)."""
+        for k in range(len(self.ranks)):
+            zero_shard_accumulate(self.rank_args(k, hp, 1, accumulate=not first), stream)
+
+    def step(self, hp: Hyper, t: int, stream=None, accumulate: bool = False) -> None:
+        """Queue one optimizer step of every simulated rank (no host wait).
+        With accumulate, pass 1 adds this micro-batch to the slices the
+        earlier micro-batches of the window left in the workspaces."""
+        args = [self.rank_args(k, hp, t, accumulate) for k in range(len(self.ranks))]
         for k, a in enumerate(args):
             zero_shard_reduce(a, k, self.partials, stream)
         zero_shard_combine(self.partials, len(self.ranks), hp.max_grad_norm, self.global_buf,
