@@ -305,6 +305,71 @@ int zero_loss_scaler_init(int32_t initial_scale_power, int32_t loss_scale_window
 int zero_loss_scaler_update(zero_loss_scaler_t* st, int32_t overflow,
                             int32_t* skip_step);
 
+/* ------------------------------------------------------------------------
+ * Sharded checkpoint and resume.  [P2] practice notes: a sharded run must be
+ * saved through the engine (engine.save_checkpoint()), because a plain
+ * torch.save of the state dict loses the shard information.  Each rank
+ * saves one file holding its part of the optimizer state together with the
+ * partition it was cut by, so a run can resume on the same world or be
+ * re-partitioned onto a different one.
+ *
+ * File layout (all little-endian), one file per rank:
+ *   bytes [0, 128)                          zero_ckpt_header_t
+ *   then valid_numel fp32 values each of    master, exp_avg, exp_avg_sq
+ * Element e of the rank's slice is flat parameter rank*shard_numel + e.
+ */
+#define ZERO_CKPT_MAGIC   0x3143535AU   /* "ZSC1" */
+#define ZERO_CKPT_VERSION 1
+
+typedef struct {
+    uint32_t magic;           /* ZERO_CKPT_MAGIC                            */
+    uint32_t version;         /* ZERO_CKPT_VERSION                          */
+    int64_t  numel;           /* flat parameter count of the run            */
+    int64_t  shard_numel;     /* elements per rank, padding included        */
+    int64_t  valid_numel;     /* real elements saved for this rank          */
+    int32_t  world_size;
+    int32_t  rank;
+    int32_t  alignment;
+    int32_t  param_dtype;     /* ZERO_FP16 or ZERO_BF16                     */
+    int64_t  step;            /* optimizer steps applied; next t = step + 1 */
+    int32_t  has_scaler;      /* 1: the scaler fields below are in use      */
+    int32_t  reserved0;
+    zero_loss_scaler_t scaler;
+    uint64_t payload_bytes;   /* 3 * valid_numel * 4                        */
+    uint8_t  pad[24];         /* zero; the header is 128 bytes            */
+} zero_ckpt_header_t;
+
+/* Fill *out for `rank` of partition *p.  scaler may be NULL (bf16 runs).
+ * Errors: NULL p or out, rank out of range, bad dtype, step < 0 ->
+ * ZERO_EINVAL.  Host only. */
+int zero_ckpt_header_make(const zero_partition_t* p, int32_t rank, int32_t param_dtype,
+                          int64_t step, const zero_loss_scaler_t* scaler,
+                          zero_ckpt_header_t* out);
+
+/* Check a header read from a file of file_bytes bytes: magic, version, a
+ * partition that zero_partition reproduces from (numel, world_size,
+ * alignment), the rank's valid count and the payload size.  On success
+ * *part receives that partition (may be NULL).  Errors: anything
+ * inconsistent -> ZERO_EINVAL; a short file -> ZERO_ESIZE.  Host only. */
+int zero_ckpt_header_check(const zero_ckpt_header_t* h, uint64_t file_bytes,
+                           zero_partition_t* part);
+
+/* Re-partition one fp32 state array (master, exp_avg or exp_avg_sq) from
+ * partition *from to partition *to of the same numel: the elastic resume
+ * of a checkpoint on a different world size.  src_dev is a host array of
+ * from->world_size device pointers, entry k holding old rank k's slice
+ * (at least its valid elements); dst_dev is a host array of
+ * to->world_size device pointers to new slices of to->shard_numel
+ * elements each (16-byte aligned).  Every flat element i < numel is copied
+ * from old rank i / from->shard_numel to new rank i / to->shard_numel; the
+ * new slices' padding is zeroed.  Source and destination must not
+ * overlap.  Device work only, queued on `stream`.
+ * Errors: NULL arguments, different numel, a NULL pointer for a rank that
+ * holds elements -> ZERO_EINVAL; misaligned pointers -> ZERO_EALIGN;
+ * launch -> ZERO_EDEVICE. */
+int zero_repartition(const zero_partition_t* from, const float* const* src_dev,
+                     const zero_partition_t* to, float* const* dst_dev, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -233,6 +233,26 @@ def adamw(g, p, m, v, coef, lr, beta1, beta2, eps, weight_decay, t):
                        float(weight_decay), int(t))
 
 
+# ------------------------------------------------- sharded checkpoint layout
+def repartition(slices, numel: int, from_world: int, from_align: int, to_world: int,
+                to_align: int):
+    """Re-cut a sharded state array ("大模型分片训练" practice notes: a
+    sharded checkpoint keeps the shard information).  The old ranks' real
+    elements, concatenated in rank order, are the flat vector; it is cut by
+    the new partition, each new slice padded with zeros to the shard size."""
+    s_old, _, valid_old = partition(numel, from_world, from_align)
+    s_new, _, valid_new = partition(numel, to_world, to_align)
+    flat = np.concatenate([np.asarray(slices[r][:valid_old[r]]) for r in range(from_world)] +
+                          [np.zeros(0, np.float32)])
+    assert flat.size == numel
+    out = []
+    for r in range(to_world):
+        x = np.zeros(s_new, np.float32)
+        x[:valid_new[r]] = flat[r * s_new:r * s_new + valid_new[r]]
+        out.append(x)
+    return out
+
+
 # ------------------------------------------------------------------ scaler
 class LossScaler:
     """Dynamic loss scaler (reading; parity unpinned by the pages)."""

@@ -13,10 +13,11 @@ from dataclasses import dataclass
 from typing import Optional, Sequence
 
 from . import _abi
-from ._abi import (ZERO_BF16, ZERO_EALIGN, ZERO_EDEVICE, ZERO_EINVAL, ZERO_ESIZE,
-                   ZERO_FP16, ZERO_MAX_REPLICAS, ZERO_OK, ZeroError, check, lib,
-                   zero_bucket_t, zero_global_t, zero_loss_scaler_t, zero_partition_t,
-                   zero_step_args, zero_step_info, zero_tensor_slot_t)
+from ._abi import (ZERO_BF16, ZERO_CKPT_MAGIC, ZERO_CKPT_VERSION, ZERO_EALIGN, ZERO_EDEVICE,
+                   ZERO_EINVAL, ZERO_ESIZE, ZERO_FP16, ZERO_MAX_REPLICAS, ZERO_OK, ZeroError,
+                   check, lib, zero_bucket_t, zero_ckpt_header_t, zero_global_t,
+                   zero_loss_scaler_t, zero_partition_t, zero_step_args, zero_step_info,
+                   zero_tensor_slot_t)
 
 __all__ = [
     "ZERO_OK", "ZERO_EINVAL", "ZERO_EALIGN", "ZERO_ESIZE", "ZERO_EDEVICE",
@@ -25,7 +26,8 @@ __all__ = [
     "zero_bucket_plan", "zero_bucket_flatten", "zero_shard_workspace_bytes",
     "zero_partials_bytes", "zero_shard_reduce", "zero_shard_accumulate", "zero_shard_combine",
     "zero_shard_apply", "zero_shard_step", "zero_loss_scaler_init",
-    "zero_loss_scaler_update", "StepArgs", "dtype_code", "GLOBAL_BYTES",
+    "zero_loss_scaler_update", "zero_ckpt_header_make", "zero_ckpt_header_check",
+    "zero_repartition", "StepArgs", "dtype_code", "GLOBAL_BYTES",
 ]
 
 GLOBAL_BYTES = ctypes.sizeof(zero_global_t)
@@ -235,3 +237,34 @@ def zero_shard_step(args, peer_sumsq: float = 0.0, peer_overflow: bool = False,
                                 ctypes.byref(info) if info is not None else None,
                                 _stream(stream)), "zero_shard_step")
     return info
+
+
+# ------------------------------------------------------- sharded checkpoint
+def zero_ckpt_header_make(part: zero_partition_t, rank: int, param_dtype, step: int,
+                          scaler: Optional[zero_loss_scaler_t] = None) -> zero_ckpt_header_t:
+    h = zero_ckpt_header_t()
+    check(lib().zero_ckpt_header_make(ctypes.byref(part), rank, dtype_code(param_dtype), step,
+                                      ctypes.byref(scaler) if scaler is not None else None,
+                                      ctypes.byref(h)), "zero_ckpt_header_make")
+    return h
+
+
+def zero_ckpt_header_check(header: zero_ckpt_header_t, file_bytes: int) -> zero_partition_t:
+    """Validate a header read from a file of file_bytes bytes; return the
+    partition it was saved under."""
+    part = zero_partition_t()
+    check(lib().zero_ckpt_header_check(ctypes.byref(header), file_bytes, ctypes.byref(part)),
+          "zero_ckpt_header_check")
+    return part
+
+
+def zero_repartition(from_part: zero_partition_t, srcs: Sequence, to_part: zero_partition_t,
+                     dsts: Sequence, stream=None) -> None:
+    """Move one fp32 state array from partition from_part (one device tensor
+    per old rank) to to_part (one device tensor per new rank)."""
+    sp = (_abi.vp * max(len(srcs), 1))(*[_dptr(t) for t in srcs])
+    dp = (_abi.vp * max(len(dsts), 1))(*[_dptr(t) for t in dsts])
+    if len(srcs) != from_part.world_size or len(dsts) != to_part.world_size:
+        raise ValueError("one tensor per rank of each partition")
+    check(lib().zero_repartition(ctypes.byref(from_part), sp, ctypes.byref(to_part), dp,
+                                 _stream(stream)), "zero_repartition")

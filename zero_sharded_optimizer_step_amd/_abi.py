@@ -63,6 +63,20 @@ class zero_loss_scaler_t(ctypes.Structure):
                 ("hysteresis_left", i32), ("window", i32), ("hysteresis", i32)]
 
 
+ZERO_CKPT_MAGIC = 0x3143535A
+ZERO_CKPT_VERSION = 1
+
+
+class zero_ckpt_header_t(ctypes.Structure):
+    _fields_ = [("magic", ctypes.c_uint32), ("version", ctypes.c_uint32), ("numel", i64),
+                ("shard_numel", i64), ("valid_numel", i64), ("world_size", i32), ("rank", i32),
+                ("alignment", i32), ("param_dtype", i32), ("step", i64), ("has_scaler", i32),
+                ("reserved0", i32), ("scaler", zero_loss_scaler_t),
+                ("payload_bytes", ctypes.c_uint64), ("pad", ctypes.c_uint8 * 24)]
+
+
+assert ctypes.sizeof(zero_ckpt_header_t) == 128
+
 _PROTOTYPES = {
     "zero_last_error": (ctypes.c_char_p, []),
     "zero_partition": (ctypes.c_int, [i64, i32, i32, ctypes.POINTER(zero_partition_t)]),
@@ -85,6 +99,13 @@ _PROTOTYPES = {
                                              ctypes.POINTER(zero_loss_scaler_t)]),
     "zero_loss_scaler_update": (ctypes.c_int, [ctypes.POINTER(zero_loss_scaler_t), i32,
                                                ctypes.POINTER(i32)]),
+    "zero_ckpt_header_make": (ctypes.c_int, [ctypes.POINTER(zero_partition_t), i32, i32, i64,
+                                             ctypes.POINTER(zero_loss_scaler_t),
+                                             ctypes.POINTER(zero_ckpt_header_t)]),
+    "zero_ckpt_header_check": (ctypes.c_int, [ctypes.POINTER(zero_ckpt_header_t), ctypes.c_uint64,
+                                              ctypes.POINTER(zero_partition_t)]),
+    "zero_repartition": (ctypes.c_int, [ctypes.POINTER(zero_partition_t), ctypes.POINTER(vp),
+                                        ctypes.POINTER(zero_partition_t), ctypes.POINTER(vp), vp]),
 }
 
 _lib = None

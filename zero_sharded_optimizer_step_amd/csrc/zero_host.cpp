@@ -212,4 +212,75 @@ int zero_loss_scaler_update(zero_loss_scaler_t* st, int32_t overflow, int32_t* s
     return ZERO_OK;
 }
 
+static_assert(sizeof(zero_ckpt_header_t) == 128, "checkpoint header is 128 bytes");
+
+int zero_ckpt_header_make(const zero_partition_t* p, int32_t rank, int32_t param_dtype,
+                          int64_t step, const zero_loss_scaler_t* scaler,
+                          zero_ckpt_header_t* out) {
+    clear_error();
+    if (!p || !out) return fail(ZERO_EINVAL, "p or out is NULL");
+    if (rank < 0 || rank >= p->world_size)
+        return fail(ZERO_EINVAL, "rank %d outside [0, %d)", rank, p->world_size);
+    if (param_dtype != ZERO_FP16 && param_dtype != ZERO_BF16)
+        return fail(ZERO_EINVAL, "param_dtype %d is not ZERO_FP16 or ZERO_BF16", param_dtype);
+    if (step < 0) return fail(ZERO_EINVAL, "step %lld < 0", (long long)step);
+    std::memset(out, 0, sizeof *out);
+    out->magic = ZERO_CKPT_MAGIC;
+    out->version = ZERO_CKPT_VERSION;
+    out->numel = p->numel;
+    out->shard_numel = p->shard_numel;
+    out->valid_numel = zero_partition_valid_numel(p, rank);
+    out->world_size = p->world_size;
+    out->rank = rank;
+    out->alignment = p->alignment;
+    out->param_dtype = param_dtype;
+    out->step = step;
+    if (scaler) {
+        out->has_scaler = 1;
+        out->scaler = *scaler;
+    }
+    out->payload_bytes = 3u * static_cast<uint64_t>(out->valid_numel) * 4u;
+    return ZERO_OK;
+}
+
+int zero_ckpt_header_check(const zero_ckpt_header_t* h, uint64_t file_bytes,
+                           zero_partition_t* part) {
+    clear_error();
+    if (!h) return fail(ZERO_EINVAL, "h is NULL");
+    if (h->magic != ZERO_CKPT_MAGIC) return fail(ZERO_EINVAL, "not a checkpoint shard (bad magic)");
+    if (h->version != ZERO_CKPT_VERSION)
+        return fail(ZERO_EINVAL, "checkpoint version %u, this library reads %d", h->version,
+                    ZERO_CKPT_VERSION);
+    zero_partition_t p;
+    if (zero_partition(h->numel, h->world_size, h->alignment, &p) != ZERO_OK)
+        return fail(ZERO_EINVAL, "checkpoint partition (%lld, %d, %d) is invalid",
+                    (long long)h->numel, h->world_size, h->alignment);
+    if (p.shard_numel != h->shard_numel)
+        return fail(ZERO_EINVAL, "shard_numel %lld does not match the partition's %lld",
+                    (long long)h->shard_numel, (long long)p.shard_numel);
+    if (h->rank < 0 || h->rank >= h->world_size)
+        return fail(ZERO_EINVAL, "rank %d outside [0, %d)", h->rank, h->world_size);
+    if (h->valid_numel != zero_partition_valid_numel(&p, h->rank))
+        return fail(ZERO_EINVAL, "valid_numel %lld does not match rank %d of the partition",
+                    (long long)h->valid_numel, h->rank);
+    if (h->param_dtype != ZERO_FP16 && h->param_dtype != ZERO_BF16)
+        return fail(ZERO_EINVAL, "param_dtype %d is not ZERO_FP16 or ZERO_BF16", h->param_dtype);
+    if (h->step < 0) return fail(ZERO_EINVAL, "step %lld < 0", (long long)h->step);
+    if (h->has_scaler != 0 && h->has_scaler != 1) return fail(ZERO_EINVAL, "has_scaler is not 0 or 1");
+    if (h->has_scaler &&
+        (h->scaler.window < 1 || h->scaler.hysteresis < 1 || !finite_positive(h->scaler.scale) ||
+         !finite_positive(h->scaler.min_scale)))
+        return fail(ZERO_EINVAL, "saved loss-scaler state is invalid");
+    const uint64_t payload = 3u * static_cast<uint64_t>(h->valid_numel) * 4u;
+    if (h->payload_bytes != payload)
+        return fail(ZERO_EINVAL, "payload_bytes %llu, expected %llu",
+                    (unsigned long long)h->payload_bytes, (unsigned long long)payload);
+    if (file_bytes < sizeof(zero_ckpt_header_t) + payload)
+        return fail(ZERO_ESIZE, "file holds %llu bytes, header and payload need %llu",
+                    (unsigned long long)file_bytes,
+                    (unsigned long long)(sizeof(zero_ckpt_header_t) + payload));
+    if (part) *part = p;
+    return ZERO_OK;
+}
+
 }  // extern "C"

@@ -495,6 +495,65 @@ int launch_apply(const zero_step_args* a, const void* global, hipStream_t st) {
     return launch_error("apply kernel launch");
 }
 
+// Copy n ranges of 16-bit values, range t from src(t) to flat elements
+// [dst(t), dst(t) + len(t)) (ascending, non-overlapping), then zero
+// [end of the last range, flat_numel); batched into flatten launches.
+template <class Src, class Dst, class Len>
+int copy_ranges(int32_t n, Src src_of, Dst dst_of, Len len_of, unsigned short* flat, int64_t flat_numel,
+                hipStream_t st) {
+    FlatBatch b;
+    b.count = 0;
+    int64_t blocks = 0;
+    auto flush = [&]() -> int {
+        if (b.count == 0) return ZERO_OK;
+        b.first_block[b.count] = static_cast<int32_t>(blocks);
+        const int64_t grid = (blocks + kXcds - 1) / kXcds * kXcds;
+        hipLaunchKernelGGL(flatten_kernel, dim3(static_cast<unsigned>(grid)), dim3(kFlatThreads), 0, st,
+                           b, flat);
+        b.count = 0;
+        blocks = 0;
+        return launch_error("flatten kernel launch");
+    };
+    // One table entry per piece of at most kFlatMaxPiece elements; a
+    // piece's blocks cover its aligned body vectors, at least one block
+    // (its head and tail).
+    auto add_piece = [&](const unsigned short* src, int64_t dst, int64_t n) -> int {
+        const int64_t a0 = (dst + 7) & ~int64_t(7);
+        const int64_t body = (dst + n) / 8 * 8 > a0 ? ((dst + n) / 8 * 8 - a0) / 8 : 0;
+        int64_t nb = (body + kFlatThreads - 1) / kFlatThreads;
+        if (nb < 1) nb = 1;
+        if (b.count == kFlatBatch || blocks + nb > (int64_t(1) << 30)) {
+            int rc = flush();
+            if (rc) return rc;
+        }
+        b.src[b.count] = src;
+        b.dst[b.count] = dst;
+        b.n[b.count] = n;
+        b.first_block[b.count] = static_cast<int32_t>(blocks);
+        blocks += nb;
+        ++b.count;
+        return ZERO_OK;
+    };
+    auto add = [&](const void* src, int64_t dst, int64_t n) -> int {
+        const unsigned short* s16 = static_cast<const unsigned short*>(src);
+        for (int64_t done = 0; done < n; done += kFlatMaxPiece) {
+            const int64_t len = n - done < kFlatMaxPiece ? n - done : kFlatMaxPiece;
+            int rc = add_piece(s16 ? s16 + done : nullptr, dst + done, len);
+            if (rc) return rc;
+        }
+        return ZERO_OK;
+    };
+    int rc;
+    int64_t end = 0;
+    for (int32_t t = 0; t < n; ++t) {
+        const int64_t d = dst_of(t), len = len_of(t);
+        if ((rc = add(src_of(t), d, len))) return rc;
+        end = d + len;
+    }
+    if ((rc = add(nullptr, end, flat_numel - end))) return rc;
+    return flush();
+}
+
 }  // namespace
 }  // namespace zero
 
@@ -594,55 +653,60 @@ int zero_bucket_flatten(const zero_tensor_slot_t* slots, int32_t n_tensors, cons
             return fail(ZERO_EALIGN, "src_dev[%d] is not 2-byte aligned", t);
         prev_end = s.offset + s.numel;
     }
+    return copy_ranges(
+        n_tensors, [&](int32_t t) { return static_cast<const unsigned short*>(src_dev[t]); },
+        [&](int32_t t) { return slots[t].offset; }, [&](int32_t t) { return slots[t].numel; },
+        static_cast<unsigned short*>(flat_dev), flat_numel, static_cast<hipStream_t>(stream));
+}
+
+int zero_repartition(const zero_partition_t* from, const float* const* src_dev,
+                     const zero_partition_t* to, float* const* dst_dev, void* stream) {
+    clear_error();
+    if (!from || !to || !src_dev || !dst_dev) return fail(ZERO_EINVAL, "a required pointer is NULL");
+    if (from->numel != to->numel)
+        return fail(ZERO_EINVAL, "partitions cover %lld and %lld elements", (long long)from->numel,
+                    (long long)to->numel);
+    if (from->world_size < 1 || to->world_size < 1 ||
+        from->shard_numel * from->world_size < from->numel || to->shard_numel * to->world_size < to->numel)
+        return fail(ZERO_EINVAL, "a partition is invalid (use zero_partition)");
+    for (int32_t k = 0; k < from->world_size; ++k) {
+        if (zero_partition_valid_numel(from, k) > 0 && !src_dev[k])
+            return fail(ZERO_EINVAL, "src_dev[%d] is NULL", k);
+        if (reinterpret_cast<uintptr_t>(src_dev[k]) & 3u)
+            return fail(ZERO_EALIGN, "src_dev[%d] is not 4-byte aligned", k);
+    }
+    for (int32_t j = 0; j < to->world_size; ++j) {
+        if (to->shard_numel > 0 && !dst_dev[j]) return fail(ZERO_EINVAL, "dst_dev[%d] is NULL", j);
+        if (!aligned16(dst_dev[j])) return fail(ZERO_EALIGN, "dst_dev[%d] is not 16-byte aligned", j);
+    }
+    // New rank j's real range [j*s', j*s' + n'_j) meets old ranks
+    // lo/s .. (hi-1)/s; each overlap is one contiguous copy, done as 16-bit
+    // halves by the flatten kernel; its padding is zero-filled after.
     hipStream_t st = static_cast<hipStream_t>(stream);
-    unsigned short* flat = static_cast<unsigned short*>(flat_dev);
-    FlatBatch b;
-    b.count = 0;
-    int64_t blocks = 0;
-    auto flush = [&]() -> int {
-        if (b.count == 0) return ZERO_OK;
-        b.first_block[b.count] = static_cast<int32_t>(blocks);
-        const int64_t grid = (blocks + kXcds - 1) / kXcds * kXcds;
-        hipLaunchKernelGGL(flatten_kernel, dim3(static_cast<unsigned>(grid)), dim3(kFlatThreads), 0, st,
-                           b, flat);
-        b.count = 0;
-        blocks = 0;
-        return launch_error("flatten kernel launch");
-    };
-    // One table entry per piece of at most kFlatMaxPiece elements; a
-    // piece's blocks cover its aligned body vectors, at least one block
-    // (its head and tail).
-    auto add_piece = [&](const unsigned short* src, int64_t dst, int64_t n) -> int {
-        const int64_t a0 = (dst + 7) & ~int64_t(7);
-        const int64_t body = (dst + n) / 8 * 8 > a0 ? ((dst + n) / 8 * 8 - a0) / 8 : 0;
-        int64_t nb = (body + kFlatThreads - 1) / kFlatThreads;
-        if (nb < 1) nb = 1;
-        if (b.count == kFlatBatch || blocks + nb > (int64_t(1) << 30)) {
-            int rc = flush();
-            if (rc) return rc;
-        }
-        b.src[b.count] = src;
-        b.dst[b.count] = dst;
-        b.n[b.count] = n;
-        b.first_block[b.count] = static_cast<int32_t>(blocks);
-        blocks += nb;
-        ++b.count;
-        return ZERO_OK;
-    };
-    auto add = [&](const void* src, int64_t dst, int64_t n) -> int {
-        const unsigned short* s16 = static_cast<const unsigned short*>(src);
-        for (int64_t done = 0; done < n; done += kFlatMaxPiece) {
-            const int64_t len = n - done < kFlatMaxPiece ? n - done : kFlatMaxPiece;
-            int rc = add_piece(s16 ? s16 + done : nullptr, dst + done, len);
-            if (rc) return rc;
-        }
-        return ZERO_OK;
-    };
-    int rc;
-    for (int32_t t = 0; t < n_tensors; ++t)
-        if ((rc = add(src_dev[t], slots[t].offset, slots[t].numel))) return rc;
-    if ((rc = add(nullptr, prev_end, flat_numel - prev_end))) return rc;
-    return flush();
+    const int64_t s_old = from->shard_numel, s_new = to->shard_numel;
+    for (int32_t j = 0; j < to->world_size; ++j) {
+        if (s_new == 0) break;
+        const int64_t lo = static_cast<int64_t>(j) * s_new;
+        const int64_t hi = lo + zero_partition_valid_numel(to, j);
+        const int64_t k0 = hi > lo ? lo / s_old : 0;
+        const int32_t n_pieces = hi > lo ? static_cast<int32_t>((hi - 1) / s_old - k0 + 1) : 0;
+        auto piece_lo = [&](int32_t q) { const int64_t k = k0 + q; return lo > k * s_old ? lo : k * s_old; };
+        auto piece_hi = [&](int32_t q) {
+            const int64_t k = k0 + q, e = (k + 1) * s_old;
+            return hi < e ? hi : e;
+        };
+        int rc = copy_ranges(
+            n_pieces,
+            [&](int32_t q) {
+                const int64_t k = k0 + q;
+                return reinterpret_cast<const unsigned short*>(src_dev[k] + (piece_lo(q) - k * s_old));
+            },
+            [&](int32_t q) { return 2 * (piece_lo(q) - lo); },
+            [&](int32_t q) { return 2 * (piece_hi(q) - piece_lo(q)); },
+            reinterpret_cast<unsigned short*>(dst_dev[j]), 2 * s_new, st);
+        if (rc) return rc;
+    }
+    return ZERO_OK;
 }
 
 }  // extern "C"

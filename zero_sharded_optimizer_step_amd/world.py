@@ -14,9 +14,10 @@ from typing import Optional, Sequence
 
 import torch
 
-from . import (GLOBAL_BYTES, StepArgs, zero_global_t, zero_partials_bytes, zero_partition,
-               zero_partition_valid_numel, zero_shard_accumulate, zero_shard_apply,
-               zero_shard_combine, zero_shard_reduce, zero_shard_workspace_bytes)
+from . import (GLOBAL_BYTES, StepArgs, checkpoint, zero_global_t, zero_partials_bytes,
+               zero_partition, zero_partition_valid_numel, zero_repartition,
+               zero_shard_accumulate, zero_shard_apply, zero_shard_combine, zero_shard_reduce,
+               zero_shard_workspace_bytes)
 
 
 @dataclass
@@ -114,3 +115,36 @@ class SimulatedWorld:
     def reduced_grad(self, k: int) -> torch.Tensor:
         """Rank ranks[k]'s fp32 reduced gradient from its last reduce."""
         return self.workspace[k][:self.s * 4].view(torch.float32)
+
+    # ------------------------------------------------- checkpoint and resume
+    def _all_ranks(self):
+        if self.ranks != list(range(self.world_size)):
+            raise ValueError("needs every rank of the world")
+
+    def state(self, k: int):
+        return (self.master[k], self.exp_avg[k], self.exp_avg_sq[k])
+
+    def save_checkpoint(self, directory: str, step: int, scaler=None) -> None:
+        """One shard file per rank: `step` optimizer steps applied so far."""
+        self._all_ranks()
+        torch.cuda.synchronize(self.device)
+        checkpoint.save_world(directory, self.part, [self.state(k) for k in range(self.world_size)],
+                              self.param_dtype, step, scaler)
+
+    def load_checkpoint(self, directory: str):
+        """Resume every simulated rank from a run saved under any world size;
+        returns (step, scaler) of the saved run."""
+        out = None
+        for k, r in enumerate(self.ranks):
+            out = checkpoint.load_rank_resharded(directory, self.part, r, self.state(k))
+        return out
+
+    def repartition_from(self, other: "SimulatedWorld", stream=None) -> None:
+        """Take over the optimizer state of a resident world of the same
+        numel but another partition, on the device."""
+        self._all_ranks()
+        other._all_ranks()
+        for field in range(3):
+            zero_repartition(other.part, [other.state(k)[field] for k in range(other.world_size)],
+                             self.part, [self.state(k)[field] for k in range(self.world_size)],
+                             stream)
