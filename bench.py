@@ -39,10 +39,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="shard13b", choices=["shard13b", "ragged"],
+    ap.add_argument("--workload", default="shard13b",
+                    choices=["shard13b", "ragged", "repartition"],
                     help="shard13b: rank 0 of the 13B/8 flat model (the headline); "
                          "ragged: 2000 tensors flattened bucket by bucket, then the step of "
-                         "all 8 ranks")
+                         "all 8 ranks; repartition: the ragged model's optimizer state moved "
+                         "from 8 ranks to 3 on the device, and one rank's checkpoint file "
+                         "written and read back")
     ap.add_argument("--micro-batches", type=int, default=1,
                     help="shard13b: gradient-accumulation window K; each step reduces K "
                          "micro-batches (the first sets the fp32 slice, the others add to it) "
@@ -298,6 +301,70 @@ def report_ragged(args, r, W):
     print(json.dumps(out), flush=True)
 
 
+def run_repartition(args, torch, Z, W):
+    """Elastic resume of the ragged model's optimizer state (2.18e9 params):
+    all three fp32 arrays moved from 8 ranks to 3 on the device (one step =
+    three zero_repartition calls), and rank 0's checkpoint file written and
+    read back through pinned staging (host-bound; reported, not the roofline)."""
+    import tempfile
+    from zero_sharded_optimizer_step_amd import checkpoint as C
+    from zero_sharded_optimizer_step_amd.world import SimulatedWorld
+    P = W.RAGGED_2000.numel
+    src = SimulatedWorld(P, 8, n_replicas=1, alignment=128, grad_dtype=torch.bfloat16)
+    dst = SimulatedWorld(P, 3, n_replicas=1, alignment=128, grad_dtype=torch.bfloat16)
+    for w in (src, dst):
+        w.grads = []
+        w.workspace = []
+    for k in range(8):
+        for f, t in enumerate(src.state(k)):
+            W.flat_normal(t, k * src.s, P, 1.0, ("bench-repart", f))
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        dst.repartition_from(src, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        dst.repartition_from(src, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    # 3 arrays: every real element read once and written once, the new padding zeroed
+    nbytes = 3 * (4 * P + 4 * dst.padded)
+    # one rank's file: 3 x 273M fp32 written, then read back into a new rank
+    d = tempfile.mkdtemp(prefix="zero_ckpt_")
+    path = C.rank_path(d, 0)
+    t0 = time.perf_counter()
+    C.save_rank(path, src.part, 0, src.state(0), torch.bfloat16, 1)
+    t_save = time.perf_counter() - t0
+    fbytes = os.path.getsize(path)
+    t0 = time.perf_counter()
+    with open(path, "rb") as f:
+        f.seek(C.HEADER_BYTES)
+        for t in src.state(0):
+            C._read_fp32(f, t[:src.valid[0]], C._staging(t.device, src.valid[0]))
+    torch.cuda.synchronize()
+    t_load = time.perf_counter() - t0
+    os.remove(path)
+    os.rmdir(d)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": P / (ms * 1e-3), "unit": "params/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "optimizer state of %d params re-partitioned from 8 ranks to 3 "
+                               "(master, exp_avg, exp_avg_sq)" % P, "params": P},
+        "hbm_gbps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS, "bytes_per_step": nbytes,
+        "roofline": {"bound": "hbm", "kernel": "flatten_kernel (range copies of zero_repartition)",
+                     "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None},
+        "checkpoint_file": {"bytes": fbytes, "save_s": t_save, "save_gbps": fbytes / t_save / 1e9,
+                            "load_s": t_load, "load_gbps": fbytes / t_load / 1e9,
+                            "where": "temporary directory on the host"},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def calibrate_copy(torch, n):
     """Plain copies of a known size, for scaling the HBM byte counters."""
     nbytes = 4 << 30
@@ -329,6 +396,9 @@ def main():
         return
     if args.workload == "ragged":
         report_ragged(args, run_ragged(args, torch, Z, W), W)
+        return
+    if args.workload == "repartition":
+        run_repartition(args, torch, Z, W)
         return
     r = run_shard13b(args, torch, Z, W)
     app_gbps = r["bytes_apply"] / (r["apply_ms"] * 1e-3) / 1e9
