@@ -306,6 +306,55 @@ int zero_loss_scaler_update(zero_loss_scaler_t* st, int32_t overflow,
                             int32_t* skip_step);
 
 /* ------------------------------------------------------------------------
+ * Optimizer step offloaded to the host CPU.  [P1] §1.2.3 and §3.1
+ * configuration (offload_optimizer: device cpu, pin_memory true), §6
+ * (ZeRO-3 with CPU offload fits 200B parameters on 8 A100s); [P3] real-world
+ * implementations (ZeRO-Offload pushes optimizer state to CPU memory).
+ *
+ * The rank's fp32 master weights and both moments live in host memory
+ * (pinned memory is strongly recommended: it makes the copies DMA).  Pass 1
+ * and the combine still run on the GPU (zero_shard_reduce /
+ * zero_shard_accumulate, zero_shard_combine); this call replaces
+ * zero_shard_apply.  It reads the combine's result; if the step overflowed
+ * it touches nothing.  Otherwise it streams the fp32 reduced gradient to
+ * the host chunk by chunk, applies the same fp32 AdamW update as the GPU
+ * pass (identical operations in identical order, so identical bits) on
+ * the host's threads, and streams the cast parameters back into the rank's
+ * slice of the device's full parameter buffer.  Device-to-host copies, host
+ * arithmetic and host-to-device copies of neighbouring chunks overlap.
+ * The call returns when everything is done (it waits for `stream`).
+ */
+typedef struct {
+    void*   grad_stage[2];    /* host, chunk_elems * 4 bytes each (pinned)   */
+    void*   param_stage[2];   /* host, chunk_elems * 2 bytes each (pinned)   */
+    int64_t chunk_elems;      /* > 0, a multiple of 8                        */
+    int32_t n_threads;        /* host threads for the update; 0: all cores   */
+    int32_t reserved;
+} zero_offload_staging_t;
+
+/* a: as for zero_shard_apply (and checked the same way), except that
+ * master, exp_avg and exp_avg_sq are HOST pointers (fp32[shard_numel],
+ * updated in place); the replica pointers are checked but not read.  global_dev: the combine's zero_global_t (device).  info, if
+ * not NULL, receives it.  Errors: as zero_shard_apply; a NULL or short
+ * staging buffer, chunk_elems not a positive multiple of 8 -> ZERO_EINVAL;
+ * a HIP failure -> ZERO_EDEVICE. */
+int zero_offload_apply(const zero_step_args* a, const void* global_dev,
+                       const zero_offload_staging_t* staging, zero_step_info* info,
+                       void* stream);
+
+/* The host AdamW of zero_offload_apply on n elements, all pointers HOST:
+ * for i < n, g' = g[i] * coef, then the update of zero_shard_apply on
+ * master, exp_avg, exp_avg_sq (fp32, in place), and, if params_out is not
+ * NULL, params_out[i] = round-to-nearest-even of the new master in
+ * param_dtype.  Hyper-parameters as in zero_step_args; step is t >= 1.
+ * n_threads 0 uses every hardware thread.  Errors: n < 0, a NULL array
+ * when n > 0, bad dtype or hyper-parameters -> ZERO_EINVAL.  Host only. */
+int zero_host_adamw(int64_t n, const float* g, float coef, float* master, float* exp_avg,
+                    float* exp_avg_sq, void* params_out, int32_t param_dtype, double lr,
+                    double beta1, double beta2, double eps, double weight_decay,
+                    int64_t step, int32_t n_threads);
+
+/* ------------------------------------------------------------------------
  * Sharded checkpoint and resume.  [P2] practice notes: a sharded run must be
  * saved through the engine (engine.save_checkpoint()), because a plain
  * torch.save of the state dict loses the shard information.  Each rank

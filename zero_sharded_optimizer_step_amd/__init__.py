@@ -16,8 +16,8 @@ from . import _abi
 from ._abi import (ZERO_BF16, ZERO_CKPT_MAGIC, ZERO_CKPT_VERSION, ZERO_EALIGN, ZERO_EDEVICE,
                    ZERO_EINVAL, ZERO_ESIZE, ZERO_FP16, ZERO_MAX_REPLICAS, ZERO_OK, ZeroError,
                    check, lib, zero_bucket_t, zero_ckpt_header_t, zero_global_t,
-                   zero_loss_scaler_t, zero_partition_t, zero_step_args, zero_step_info,
-                   zero_tensor_slot_t)
+                   zero_loss_scaler_t, zero_offload_staging_t, zero_partition_t,
+                   zero_step_args, zero_step_info, zero_tensor_slot_t)
 
 __all__ = [
     "ZERO_OK", "ZERO_EINVAL", "ZERO_EALIGN", "ZERO_ESIZE", "ZERO_EDEVICE",
@@ -27,7 +27,8 @@ __all__ = [
     "zero_partials_bytes", "zero_shard_reduce", "zero_shard_accumulate", "zero_shard_combine",
     "zero_shard_apply", "zero_shard_step", "zero_loss_scaler_init",
     "zero_loss_scaler_update", "zero_ckpt_header_make", "zero_ckpt_header_check",
-    "zero_repartition", "StepArgs", "dtype_code", "GLOBAL_BYTES",
+    "zero_repartition", "zero_offload_apply", "zero_host_adamw", "OffloadStaging",
+    "StepArgs", "dtype_code", "GLOBAL_BYTES",
 ]
 
 GLOBAL_BYTES = ctypes.sizeof(zero_global_t)
@@ -268,3 +269,49 @@ def zero_repartition(from_part: zero_partition_t, srcs: Sequence, to_part: zero_
         raise ValueError("one tensor per rank of each partition")
     check(lib().zero_repartition(ctypes.byref(from_part), sp, ctypes.byref(to_part), dp,
                                  _stream(stream)), "zero_repartition")
+
+
+# ------------------------------------------------------- optimizer offload
+class OffloadStaging:
+    """Two pinned host buffers per direction for zero_offload_apply."""
+
+    def __init__(self, chunk_elems: int = 1 << 25, n_threads: int = 0):
+        torch = _torch()
+        self.grad = [torch.empty(chunk_elems, dtype=torch.float32, pin_memory=True)
+                     for _ in range(2)]
+        self.param = [torch.empty(chunk_elems, dtype=torch.int16, pin_memory=True)
+                      for _ in range(2)]
+        self.c = zero_offload_staging_t()
+        for i in range(2):
+            self.c.grad_stage[i] = self.grad[i].data_ptr()
+            self.c.param_stage[i] = self.param[i].data_ptr()
+        self.c.chunk_elems = chunk_elems
+        self.c.n_threads = n_threads
+
+
+def zero_offload_apply(args, global_buf, staging: OffloadStaging, want_info: bool = False,
+                       stream=None) -> Optional[zero_step_info]:
+    """Pass 2 on the host: args.master / exp_avg / exp_avg_sq are host (pinned)
+    tensors; waits for the stream."""
+    info = zero_step_info() if want_info else None
+    check(lib().zero_offload_apply(ctypes.byref(_args(args)), _dptr(global_buf),
+                                   ctypes.byref(staging.c),
+                                   ctypes.byref(info) if info is not None else None,
+                                   _stream(stream)), "zero_offload_apply")
+    return info
+
+
+def zero_host_adamw(g, coef: float, master, exp_avg, exp_avg_sq, params_out=None,
+                    param_dtype=ZERO_BF16, lr: float = 6e-5, beta1: float = 0.9,
+                    beta2: float = 0.999, eps: float = 1e-8, weight_decay: float = 0.01,
+                    step: int = 1, n_threads: int = 0) -> None:
+    """The offloaded update on host arrays (anything with data_ptr(), or
+    numpy arrays via their ctypes data pointer)."""
+    def ptr(x):
+        if x is None:
+            return None
+        return x.data_ptr() if hasattr(x, "data_ptr") else x.ctypes.data
+    n = g.numel() if hasattr(g, "numel") and callable(g.numel) else g.size
+    check(lib().zero_host_adamw(n, ptr(g), coef, ptr(master), ptr(exp_avg), ptr(exp_avg_sq),
+                                ptr(params_out), dtype_code(param_dtype), lr, beta1, beta2, eps,
+                                weight_decay, step, n_threads), "zero_host_adamw")

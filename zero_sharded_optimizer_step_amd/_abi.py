@@ -77,6 +77,11 @@ class zero_ckpt_header_t(ctypes.Structure):
 
 assert ctypes.sizeof(zero_ckpt_header_t) == 128
 
+class zero_offload_staging_t(ctypes.Structure):
+    _fields_ = [("grad_stage", vp * 2), ("param_stage", vp * 2), ("chunk_elems", i64),
+                ("n_threads", i32), ("reserved", i32)]
+
+
 _PROTOTYPES = {
     "zero_last_error": (ctypes.c_char_p, []),
     "zero_partition": (ctypes.c_int, [i64, i32, i32, ctypes.POINTER(zero_partition_t)]),
@@ -106,6 +111,11 @@ _PROTOTYPES = {
                                               ctypes.POINTER(zero_partition_t)]),
     "zero_repartition": (ctypes.c_int, [ctypes.POINTER(zero_partition_t), ctypes.POINTER(vp),
                                         ctypes.POINTER(zero_partition_t), ctypes.POINTER(vp), vp]),
+    "zero_offload_apply": (ctypes.c_int, [ctypes.POINTER(zero_step_args), vp,
+                                          ctypes.POINTER(zero_offload_staging_t),
+                                          ctypes.POINTER(zero_step_info), vp]),
+    "zero_host_adamw": (ctypes.c_int, [i64, vp, f32, vp, vp, vp, vp, i32, f64, f64, f64, f64,
+                                       f64, i64, i32]),
 }
 
 _lib = None

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libzero_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["zero_host.cpp", "zero_kernels.hip"]
+SOURCES = ["zero_host.cpp", "zero_offload.cpp", "zero_kernels.hip"]
 ARCH = "gfx950"
 
 

@@ -23,6 +23,21 @@ void clear_error() { g_error[0] = '\0'; }
 
 static bool finite_positive(double x) { return std::isfinite(x) && x > 0.0; }
 
+AdamConsts adam_consts(double lr, double beta1, double beta2, double eps, double weight_decay,
+                       int64_t step) {
+    AdamConsts k;
+    const double t = static_cast<double>(step);
+    k.decay = static_cast<float>(1.0 - lr * weight_decay);
+    k.b1 = static_cast<float>(beta1);
+    k.c1 = static_cast<float>(1.0 - beta1);
+    k.b2 = static_cast<float>(beta2);
+    k.c2 = static_cast<float>(1.0 - beta2);
+    k.step_size = static_cast<float>(lr / (1.0 - std::pow(beta1, t)));
+    k.inv_sqrt_bc2 = static_cast<float>(1.0 / std::sqrt(1.0 - std::pow(beta2, t)));
+    k.eps = static_cast<float>(eps);
+    return k;
+}
+
 int validate_step_args(const zero_step_args* a) {
     if (!a) return fail(ZERO_EINVAL, "args is NULL");
     if (a->world_size < 1) return fail(ZERO_EINVAL, "world_size %d < 1", a->world_size);

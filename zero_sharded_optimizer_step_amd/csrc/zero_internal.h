@@ -88,4 +88,18 @@ inline size_t ws_global_offset(int64_t shard_numel) {
 // Checks every field of a step's arguments (see zero_shard_step).
 int validate_step_args(const zero_step_args* a);
 
+// AdamW's per-step fp32 constants, each computed in fp64 from the step's
+// hyper-parameters and rounded once; the GPU pass and the host (offloaded)
+// pass both use exactly these.
+struct AdamConsts {
+    float decay;          // 1 - lr * wd
+    float b1, c1;         // beta1, 1 - beta1
+    float b2, c2;         // beta2, 1 - beta2
+    float step_size;      // lr / (1 - beta1^t)
+    float inv_sqrt_bc2;   // 1 / sqrt(1 - beta2^t)
+    float eps;
+};
+AdamConsts adam_consts(double lr, double beta1, double beta2, double eps, double weight_decay,
+                       int64_t step);
+
 }  // namespace zero

@@ -250,15 +250,6 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 // AdamW ([P1] §3.1) on the rank's fp32 masters and moments ([P3] FAQ), only
 // when no replica overflowed, then the cast of the new masters into the
 // rank's slice of the full low-precision buffer ([P1] §2.1 all-gather).
-struct AdamConsts {
-    float decay;          // 1 - lr * wd
-    float b1, c1;         // beta1, 1 - beta1
-    float b2, c2;         // beta2, 1 - beta2
-    float step_size;      // lr / (1 - beta1^t)
-    float inv_sqrt_bc2;   // 1 / sqrt(1 - beta2^t)
-    float eps;
-};
-
 // One element, in fp32 with one rounding per operation (no contraction):
 //   m' = b1 m + c1 g;  v' = b2 v + c2 g^2;  d = sqrt(v') / sqrt(1 - b2^t) + eps;
 //   p' = p (1 - lr wd) - lr / (1 - b1^t) * m' / d.
@@ -471,16 +462,7 @@ int launch_combine(const void* partials, int n_slots, double peer_ss, int peer_o
 }
 
 int launch_apply(const zero_step_args* a, const void* global, hipStream_t st) {
-    AdamConsts k;
-    const double t = static_cast<double>(a->step);
-    k.decay = static_cast<float>(1.0 - a->lr * a->weight_decay);
-    k.b1 = static_cast<float>(a->beta1);
-    k.c1 = static_cast<float>(1.0 - a->beta1);
-    k.b2 = static_cast<float>(a->beta2);
-    k.c2 = static_cast<float>(1.0 - a->beta2);
-    k.step_size = static_cast<float>(a->lr / (1.0 - std::pow(a->beta1, t)));
-    k.inv_sqrt_bc2 = static_cast<float>(1.0 / std::sqrt(1.0 - std::pow(a->beta2, t)));
-    k.eps = static_cast<float>(a->eps);
+    const AdamConsts k = adam_consts(a->lr, a->beta1, a->beta2, a->eps, a->weight_decay, a->step);
     const dim3 grid(static_cast<unsigned>(apply_blocks_for(a->valid_numel)));
     unsigned short* out = static_cast<unsigned short*>(a->full_params) +
                           static_cast<size_t>(a->rank) * static_cast<size_t>(a->shard_numel);
