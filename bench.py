@@ -40,12 +40,17 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="shard13b",
-                    choices=["shard13b", "ragged", "repartition"],
+                    choices=["shard13b", "ragged", "repartition", "offload"],
                     help="shard13b: rank 0 of the 13B/8 flat model (the headline); "
                          "ragged: 2000 tensors flattened bucket by bucket, then the step of "
                          "all 8 ranks; repartition: the ragged model's optimizer state moved "
                          "from 8 ranks to 3 on the device, and one rank's checkpoint file "
-                         "written and read back")
+                         "written and read back; offload: the 13B/8 shard with its optimizer "
+                         "state in pinned host memory (pass 1 on the GPU, AdamW on the host)")
+    ap.add_argument("--host-threads", type=int, default=0,
+                    help="offload: host threads for the update (0: all)")
+    ap.add_argument("--chunk", type=int, default=1 << 25,
+                    help="offload: elements per transfer chunk")
     ap.add_argument("--micro-batches", type=int, default=1,
                     help="shard13b: gradient-accumulation window K; each step reduces K "
                          "micro-batches (the first sets the fp32 slice, the others add to it) "
@@ -365,6 +370,75 @@ def run_repartition(args, torch, Z, W):
     print(json.dumps(out), flush=True)
 
 
+def run_offload(args, torch, Z, W):
+    """The 13B/8 shard with its fp32 master and moments in pinned host memory:
+    pass 1 and the combine on the GPU, then zero_offload_apply (gradient
+    down, host AdamW, parameters up, pipelined by chunk)."""
+    import multiprocessing
+    w = W.SHARD_13B_OF_8
+    part = Z.zero_partition(w.numel, w.world_size, w.alignment)
+    s = part.shard_numel
+    valid = Z.zero_partition_valid_numel(part, 0)
+    log("offload: generating 8 replicas and pinning 3 x %d fp32 of host state" % s)
+    grads = []
+    for i in range(w.world_size):
+        g = torch.empty(s, dtype=torch.bfloat16, device="cuda")
+        W.flat_normal(g, 0, w.numel, w.grad_sigma, W.grad_key(w, 0, 0, i))
+        grads.append(g)
+    master = torch.empty(s, dtype=torch.float32, pin_memory=True)
+    tmp = torch.empty(min(s, W.CHUNK), dtype=torch.float32, device="cuda")
+    for a in range(0, s, tmp.numel()):
+        b = min(s, a + tmp.numel())
+        W.flat_normal(tmp[:b - a], a, w.numel, w.master_sigma, W.master_key(w, 0))
+        master[a:b].copy_(tmp[:b - a])
+    del tmp
+    m = torch.zeros(s, dtype=torch.float32, pin_memory=True)
+    v = torch.zeros(s, dtype=torch.float32, pin_memory=True)
+    full = torch.zeros(part.padded_numel, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(Z.zero_shard_workspace_bytes(s), dtype=torch.uint8, device="cuda")
+    partials = torch.zeros(Z.zero_partials_bytes(1), dtype=torch.uint8, device="cuda")
+    glob = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    staging = Z.OffloadStaging(args.chunk, args.host_threads)
+    stream = torch.cuda.current_stream()
+
+    def step(t):
+        a = Z.StepArgs(world_size=w.world_size, rank=0, shard_numel=s, valid_numel=valid,
+                       replica_grads=grads, master=master, exp_avg=m, exp_avg_sq=v,
+                       full_params=full, workspace=ws, lr=w.lr, weight_decay=w.weight_decay,
+                       step=t, max_grad_norm=w.max_grad_norm)
+        Z.zero_shard_reduce(a, 0, partials, stream)
+        Z.zero_shard_combine(partials, 1, w.max_grad_norm, glob, stream)
+        return Z.zero_offload_apply(a, glob, staging, want_info=True, stream=stream)
+
+    t = 1
+    for _ in range(args.warmup):
+        step(t)
+        t += 1
+    torch.cuda.synchronize()
+    K = args.steps
+    t0 = time.perf_counter()
+    for _ in range(K):
+        info = step(t)
+        t += 1
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / K
+    pcie = valid * (4 + 2)
+    host_bytes = valid * (12 + 12 + 4 + 2)     # state read + written, staged gradient, cast
+    threads = args.host_threads or multiprocessing.cpu_count()
+    out = {
+        "metric": METRIC, "value": valid / sec, "unit": "params/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": sec * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name + ", optimizer state offloaded to pinned host memory",
+                   "shard_numel": s, "chunk_elems": args.chunk, "host_threads": threads},
+        "pcie_gbps": pcie / sec / 1e9, "host_memory_gbps": host_bytes / sec / 1e9,
+        "bytes_over_link_per_step": pcie,
+        "roofline": None,
+        "step_check": {"norm": info.norm, "clipped": info.clipped, "overflow": info.overflow},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def calibrate_copy(torch, n):
     """Plain copies of a known size, for scaling the HBM byte counters."""
     nbytes = 4 << 30
@@ -399,6 +473,9 @@ def main():
         return
     if args.workload == "repartition":
         run_repartition(args, torch, Z, W)
+        return
+    if args.workload == "offload":
+        run_offload(args, torch, Z, W)
         return
     r = run_shard13b(args, torch, Z, W)
     app_gbps = r["bytes_apply"] / (r["apply_ms"] * 1e-3) / 1e9

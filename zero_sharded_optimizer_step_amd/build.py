@@ -4,6 +4,8 @@
 
 Flags: -O3; no floating-point contraction (the kernels write their fused
 multiply-adds explicitly, so every other operation is rounded as written);
+no errno from math calls (lets the host update's square roots vectorize;
+results are unchanged);
 packed fp32 instructions disabled; IEEE division and square root (hipcc's
 default) and denormals kept (no flush-to-zero, no fast-math).
 """
@@ -34,6 +36,7 @@ def hipcc() -> str:
 
 def compile_flags() -> list[str]:
     return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
+            "-fno-math-errno",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-Wall", "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
 

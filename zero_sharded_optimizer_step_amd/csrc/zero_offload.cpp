@@ -34,8 +34,9 @@ inline uint32_t bits_of(float x) {
 // should; NaN is kept quiet.
 inline uint16_t to_bf16(float x) {
     const uint32_t u = bits_of(x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
-    return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t quiet = (u >> 16) | 0x0040u;
+    return static_cast<uint16_t>((u & 0x7fffffffu) > 0x7f800000u ? quiet : rounded);
 }
 
 // IEEE binary16 (5 exponent bits, bias 15, 10 fraction bits).
