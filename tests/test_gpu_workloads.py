@@ -235,3 +235,55 @@ def test_ragged_bucketed_workload():
         assert torch.equal(full[lo:lo + n], world.master[r][:n].to(torch.bfloat16).view(torch.int16))
         assert bool((full[lo + n:lo + s] == parity.CANARY).all()), "padding written, rank %d" % r
     say("ragged workload matches: norm %.6f (oracle %.6f)" % (res.norm, onorm))
+
+
+def test_shard_beyond_2_pow_31_elements():
+    """One rank whose shard holds more than 2^31 elements (64-bit indexing in
+    every kernel), 2 bf16 replicas, a ragged tail."""
+    P = (1 << 31) + (1 << 20) + 5
+    R = 2
+    say("shard of %d elements, %d replicas" % (P, R))
+    world = SimulatedWorld(P, 1, n_replicas=R, alignment=8, grad_dtype=torch.bfloat16)
+    s = world.s
+    gkey = lambda i: ("big", i)
+    for i in range(R):
+        W.flat_normal(world.grads[i], 0, P, 1e-3, gkey(i))
+    W.flat_normal(world.master[0], 0, P, 0.02, ("big-master",))
+    world.full_params.view(torch.int16).fill_(parity.CANARY)
+    rng = np.random.default_rng(8)
+    sample = np.unique(np.concatenate([
+        parity.structural_sample(P, rng, n_random=1 << 15),
+        (1 << 31) + np.arange(-4, 5, dtype=np.int64), np.arange(P - 7, P, dtype=np.int64)]))
+    inv = oracle.inv_scale(1.0)
+    on = parity.oracle_norm_and_sample(R, 0, P, P, 1e-3, gkey, torch.bfloat16, sample, inv,
+                                       log=say)
+    applies, onorm, ocoef = oracle.clip(on.sumsq, 1.0)
+    o_g, _, _ = oracle.reduce(on.codes, oracle.BF16, inv)
+    o_p = parity.gather_generated(sample, 0, P, 0.02, ("big-master",), torch.float32, P).copy()
+    o_m = np.zeros(sample.size, np.float32)
+    o_v = np.zeros(sample.size, np.float32)
+    oracle.adamw(o_g, o_p, o_m, o_v, ocoef, 6e-5, 0.9, 0.999, 1e-8, 0.01, 1)
+    say("step")
+    world.step(Hyper(), 1)
+    res = world.result()
+    assert res.overflow == 0 and bool(res.clipped) == applies
+    assert abs(res.norm - onorm) <= parity.RTOL_NORM * onorm, (res.norm, onorm)
+    parity.assert_bitwise("reduced grad (sample)", parity.take(world.reduced_grad(0), sample)
+                          .numpy(), o_g)
+    parity.assert_rel("master (sample)", parity.take(world.master[0], sample).numpy(), o_p,
+                      parity.RTOL_STATE)
+    parity.assert_rel("exp_avg (sample)", parity.take(world.exp_avg[0], sample).numpy(), o_m,
+                      parity.RTOL_STATE)
+    parity.assert_rel("exp_avg_sq (sample)", parity.take(world.exp_avg_sq[0], sample).numpy(),
+                      o_v, parity.RTOL_STATE)
+    full = world.full_params.view(torch.int16)
+    parity.assert_cast("cast (sample)", parity.take(full, sample).numpy().view(np.uint16),
+                       oracle.f32_to_bf16(o_p))
+    g = world.reduced_grad(0)
+    for a, b in _chunked(P):
+        acc = world.grads[0][a:b].float()
+        acc += world.grads[1][a:b].float()
+        assert torch.equal(acc, g[a:b]), "reduced gradient differs in [%d, %d)" % (a, b)
+        assert torch.equal(full[a:b], world.master[0][a:b].to(torch.bfloat16).view(torch.int16))
+    assert bool((full[P:s] == parity.CANARY).all())
+    say("shard beyond 2^31 matches: norm %.6f" % res.norm)
