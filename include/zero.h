@@ -184,6 +184,12 @@ typedef struct {
     double loss_scale;        /* S > 0: gradients hold S * dL/dw           */
     double grad_predivide;    /* D > 0: the sum is divided by S*D          */
     double max_grad_norm;     /* <= 0 disables clipping                    */
+    /* ZeRO-3 ([P1] §1.2.3, [P2] stage table): the rank keeps only its own
+     * shard of the low-precision parameters.  When not NULL the cast goes
+     * to param_shard[0, valid_numel) (device, 16-byte aligned) and
+     * full_params is not used (may be NULL); zero_gather_params collects a
+     * layer's parameters from all ranks' shards before its forward.       */
+    void* param_shard;
 } zero_step_args;
 
 /* Result of the cross-rank combine, 32 bytes in device memory. */
@@ -304,6 +310,26 @@ int zero_loss_scaler_init(int32_t initial_scale_power, int32_t loss_scale_window
 
 int zero_loss_scaler_update(zero_loss_scaler_t* st, int32_t overflow,
                             int32_t* skip_step);
+
+/* ------------------------------------------------------------------------
+ * ZeRO-3 parameter gather.  [P1] §1.2.3 (parameters themselves are
+ * partitioned; sub_group_size, stage3_prefetch_bucket_size), [P2] (before a
+ * layer's forward an all-gather fetches its parameters, which are freed
+ * after), [P3] technical insight (the all-gather assembles the layer's full
+ * parameters on every GPU, then the slices a GPU does not own are dropped).
+ *
+ * Copies flat parameters [lo, hi) of partition *p into dst[0, hi - lo)
+ * (device, 16-byte aligned) from the ranks' shards: shards is a host array
+ * of p->world_size device pointers, entry r holding rank r's shard of
+ * 16-bit parameters (at least its valid elements; r * shard_numel is its
+ * first flat element).  Only the shards [lo, hi) meets are read.  On one
+ * GPU the shards may be slices of one buffer; across GPUs they would be
+ * peer-mapped pointers.  Bit copy: dtype is checked, values are not read.
+ * Errors: NULL arguments, lo < 0, hi < lo, hi > numel, bad dtype, a NULL
+ * shard that [lo, hi) meets -> ZERO_EINVAL; misaligned dst or shard ->
+ * ZERO_EALIGN; launch -> ZERO_EDEVICE. */
+int zero_gather_params(const zero_partition_t* p, const void* const* shards, int32_t dtype,
+                       int64_t lo, int64_t hi, void* dst, void* stream);
 
 /* ------------------------------------------------------------------------
  * Optimizer step offloaded to the host CPU.  [P1] §1.2.3 and §3.1

@@ -253,6 +253,16 @@ def repartition(slices, numel: int, from_world: int, from_align: int, to_world: 
     return out
 
 
+def gather(slices, numel: int, world: int, align: int, lo: int, hi: int):
+    """ZeRO-3 all-gather of flat parameters [lo, hi) ("ZeRO 和分片优化器",
+    technical insight): the ranks' real elements concatenated in rank order,
+    sliced."""
+    _, _, valid = partition(numel, world, align)
+    flat = np.concatenate([np.asarray(slices[r][:valid[r]]) for r in range(world)] +
+                          [np.zeros(0, np.asarray(slices[0]).dtype)])
+    return flat[lo:hi].copy()
+
+
 # ------------------------------------------------------------------ scaler
 class LossScaler:
     """Dynamic loss scaler (reading; parity unpinned by the pages)."""

@@ -123,3 +123,12 @@ def test_files_from_different_runs_are_rejected(tmp_path):
         f.truncate(200)
     with pytest.raises(Z.ZeroError):
         C.read_header(C.rank_path(str(tmp_path), 0))
+
+
+# ------------------------------------------------------------ ZeRO-3 gather
+def test_oracle_gather_hand_example():
+    shards = [np.array([0, 1, 2, 3], np.uint16), np.array([4, 5, 6, 7], np.uint16),
+              np.array([8, 9, 0xAAAA, 0xAAAA], np.uint16)]     # 10 params, N=3, A=2
+    assert oracle.gather(shards, 10, 3, 2, 3, 9).tolist() == [3, 4, 5, 6, 7, 8]
+    assert oracle.gather(shards, 10, 3, 2, 0, 10).tolist() == list(range(10))
+    assert oracle.gather(shards, 10, 3, 2, 5, 5).size == 0

@@ -1,0 +1,97 @@
+"""GPU tests of ZeRO-3 parameter handling, through the C ABI: the cast into
+each rank's own parameter shard, the gather of any flat range from the
+shards (against the oracle's concatenate-and-slice), and the prefetching
+layer walk over the encoder-layer workload with a small live bound."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+import zero_sharded_optimizer_step_amd as Z
+from zero_sharded_optimizer_step_amd import workloads as W
+from zero_sharded_optimizer_step_amd.world import Hyper, SimulatedWorld
+from zero_sharded_optimizer_step_amd.zero3 import LayerGatherer
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def test_cast_into_own_shards_equals_full_buffer():
+    P, N = 300_007, 4
+    say("ZeRO-3 cast into shards")
+    w1 = SimulatedWorld(P, N, alignment=128, grad_dtype=torch.bfloat16)
+    w2 = SimulatedWorld(P, N, alignment=128, grad_dtype=torch.bfloat16)
+    shards = [torch.full((w2.s,), parity.CANARY, dtype=torch.int16, device="cuda")
+              for _ in range(N)]
+    for w in (w1, w2):
+        for i in range(N):
+            W.flat_normal(w.grads[i], 0, P, 1e-2, ("z3", i))
+        for k in range(N):
+            W.flat_normal(w.master[k], k * w.s, P, 0.02, ("z3m",))
+    hp = Hyper()
+    w1.step(hp, 1)
+    args = [w2.rank_args(k, hp, 1) for k in range(N)]
+    for k, a in enumerate(args):
+        a.full_params = None
+        a.param_shard = shards[k].view(torch.bfloat16)
+        Z.zero_shard_reduce(a, k, w2.partials)
+    Z.zero_shard_combine(w2.partials, N, hp.max_grad_norm, w2.global_buf)
+    for a in args:
+        Z.zero_shard_apply(a, w2.global_buf)
+    full = parity.u16(w1.full_params)
+    for k in range(N):
+        got = parity.u16(shards[k])
+        n = w1.valid[k]
+        parity.assert_bitwise("rank %d shard" % k, got[:n], full[k * w1.s:k * w1.s + n])
+        assert (got[n:] == parity.CANARY).all()
+
+
+@pytest.mark.parametrize("P,N,A", [(1_000_003, 8, 128), (77, 4, 8), (5_000_011, 3, 1)])
+def test_gather_ranges_match_oracle(P, N, A):
+    say("gather P=%d N=%d A=%d" % (P, N, A))
+    part = Z.zero_partition(P, N, A)
+    s = part.shard_numel
+    shards = [torch.randint(-32768, 32767, (s,), dtype=torch.int16, device="cuda")
+              for _ in range(N)]
+    host = [parity.u16(x) for x in shards]
+    rng = np.random.default_rng(P)
+    ranges = [(0, P), (0, 0), (P, P), (s - 3, s + 5), (min(s + 1, P), P)]
+    ranges += [tuple(sorted(int(x) for x in rng.integers(0, P + 1, 2))) for _ in range(20)]
+    for lo, hi in ranges:
+        lo, hi = min(lo, P), min(hi, P)
+        dst = torch.full((hi - lo + 16,), 0x1357, dtype=torch.int16, device="cuda")
+        Z.zero_gather_params(part, [x.view(torch.bfloat16) for x in shards], torch.bfloat16,
+                             lo, hi, dst.view(torch.bfloat16))
+        got = parity.u16(dst)
+        parity.assert_bitwise("gather [%d, %d)" % (lo, hi), got[:hi - lo],
+                              oracle.gather(host, P, N, A, lo, hi))
+        assert (got[hi - lo:] == 0x1357).all(), "wrote past the range"
+    with pytest.raises(Z.ZeroError):
+        Z.zero_gather_params(part, shards, torch.bfloat16, 0, P + 1, dst)
+
+
+@pytest.mark.parametrize("bucket,max_live", [(1 << 22, 1 << 25), (1 << 25, 1 << 25),
+                                             (1, 1 << 24)])
+def test_layer_walk_with_prefetch(bucket, max_live):
+    w = W.ENCODER_4096
+    say("layer walk: bucket %d, max live %d" % (bucket, max_live))
+    part = Z.zero_partition(w.numel, w.world_size, 128)
+    s = part.shard_numel
+    shards = [torch.randint(-32768, 32767, (s,), dtype=torch.int16, device="cuda")
+              .view(torch.bfloat16) for _ in range(w.world_size)]
+    host = [parity.u16(x) for x in shards]
+    g = LayerGatherer(part, shards, w.tensor_sizes, bucket, max_live)
+    seen = []
+    for t, params in g.forward():
+        off = sum(w.tensor_sizes[:t])
+        # some work on the caller's stream between layers
+        _ = params.float().sum()
+        parity.assert_bitwise("layer %d" % t, parity.u16(params),
+                              oracle.gather(host, w.numel, w.world_size, 128, off,
+                                            off + w.tensor_sizes[t]))
+        seen.append(t)
+    assert seen == list(range(len(w.tensor_sizes)))

@@ -27,7 +27,8 @@ __all__ = [
     "zero_partials_bytes", "zero_shard_reduce", "zero_shard_accumulate", "zero_shard_combine",
     "zero_shard_apply", "zero_shard_step", "zero_loss_scaler_init",
     "zero_loss_scaler_update", "zero_ckpt_header_make", "zero_ckpt_header_check",
-    "zero_repartition", "zero_offload_apply", "zero_host_adamw", "OffloadStaging",
+    "zero_repartition", "zero_gather_params", "zero_offload_apply", "zero_host_adamw",
+    "OffloadStaging",
     "StepArgs", "dtype_code", "GLOBAL_BYTES",
 ]
 
@@ -170,6 +171,7 @@ class StepArgs:
     grad_dtype: Optional[int] = None
     param_dtype: Optional[int] = None
     accumulate: bool = False
+    param_shard: object = None          # ZeRO-3: the rank's own parameter shard
 
     def c_args(self) -> zero_step_args:
         reps = list(self.replica_grads)
@@ -181,7 +183,8 @@ class StepArgs:
         a.valid_numel = self.valid_numel
         a.grad_dtype = dtype_code(self.grad_dtype if self.grad_dtype is not None else reps[0].dtype)
         a.param_dtype = dtype_code(self.param_dtype if self.param_dtype is not None
-                                   else self.full_params.dtype)
+                                   else (self.full_params if self.full_params is not None
+                                         else self.param_shard).dtype)
         a.n_replicas = len(reps)
         a.accumulate = 1 if self.accumulate else 0
         a.replica_grad = ctypes.cast(self._ptrs, ctypes.POINTER(_abi.vp))
@@ -189,6 +192,7 @@ class StepArgs:
         a.exp_avg = _dptr(self.exp_avg)
         a.exp_avg_sq = _dptr(self.exp_avg_sq)
         a.full_params = _dptr(self.full_params)
+        a.param_shard = _dptr(self.param_shard)
         a.workspace = _dptr(self.workspace)
         a.workspace_bytes = 0 if self.workspace is None else \
             self.workspace.numel() * self.workspace.element_size()
@@ -315,3 +319,15 @@ def zero_host_adamw(g, coef: float, master, exp_avg, exp_avg_sq, params_out=None
     check(lib().zero_host_adamw(n, ptr(g), coef, ptr(master), ptr(exp_avg), ptr(exp_avg_sq),
                                 ptr(params_out), dtype_code(param_dtype), lr, beta1, beta2, eps,
                                 weight_decay, step, n_threads), "zero_host_adamw")
+
+
+# ------------------------------------------------------ ZeRO-3 gathering
+def zero_gather_params(part: zero_partition_t, shards: Sequence, dtype, lo: int, hi: int, dst,
+                       stream=None) -> None:
+    """Copy flat parameters [lo, hi) into dst from the ranks' shards (one
+    device tensor per rank)."""
+    if len(shards) != part.world_size:
+        raise ValueError("one shard per rank")
+    sp = (_abi.vp * len(shards))(*[_dptr(t) for t in shards])
+    check(lib().zero_gather_params(ctypes.byref(part), sp, dtype_code(dtype), lo, hi, _dptr(dst),
+                                   _stream(stream)), "zero_gather_params")

@@ -47,7 +47,7 @@ class zero_step_args(ctypes.Structure):
                 ("full_params", vp), ("workspace", vp), ("workspace_bytes", sz),
                 ("lr", f64), ("beta1", f64), ("beta2", f64), ("eps", f64),
                 ("weight_decay", f64), ("step", i64), ("loss_scale", f64),
-                ("grad_predivide", f64), ("max_grad_norm", f64)]
+                ("grad_predivide", f64), ("max_grad_norm", f64), ("param_shard", vp)]
 
 
 class zero_global_t(ctypes.Structure):
@@ -111,6 +111,8 @@ _PROTOTYPES = {
                                               ctypes.POINTER(zero_partition_t)]),
     "zero_repartition": (ctypes.c_int, [ctypes.POINTER(zero_partition_t), ctypes.POINTER(vp),
                                         ctypes.POINTER(zero_partition_t), ctypes.POINTER(vp), vp]),
+    "zero_gather_params": (ctypes.c_int, [ctypes.POINTER(zero_partition_t), ctypes.POINTER(vp),
+                                          i32, i64, i64, vp, vp]),
     "zero_offload_apply": (ctypes.c_int, [ctypes.POINTER(zero_step_args), vp,
                                           ctypes.POINTER(zero_offload_staging_t),
                                           ctypes.POINTER(zero_step_info), vp]),

@@ -74,7 +74,8 @@ int validate_step_args(const zero_step_args* a) {
     // A rank with no real elements reads and writes no element, so its data
     // pointers may be NULL (empty tensors).
     if (a->valid_numel > 0) {
-        if (!a->replica_grad || !a->master || !a->exp_avg || !a->exp_avg_sq || !a->full_params)
+        if (!a->replica_grad || !a->master || !a->exp_avg || !a->exp_avg_sq ||
+            (!a->full_params && !a->param_shard))
             return fail(ZERO_EINVAL, "a required pointer is NULL");
         for (int i = 0; i < a->n_replicas; ++i) {
             if (!a->replica_grad[i]) return fail(ZERO_EINVAL, "replica_grad[%d] is NULL", i);
@@ -82,7 +83,7 @@ int validate_step_args(const zero_step_args* a) {
                 return fail(ZERO_EALIGN, "replica_grad[%d] is not 16-byte aligned", i);
         }
         if (!aligned16(a->master) || !aligned16(a->exp_avg) || !aligned16(a->exp_avg_sq) ||
-            !aligned16(a->full_params))
+            !aligned16(a->full_params) || !aligned16(a->param_shard))
             return fail(ZERO_EALIGN, "a state or parameter pointer is not 16-byte aligned");
     }
     // Start of this rank's slice of the full buffer: shard_numel is a

@@ -85,6 +85,14 @@ inline size_t ws_global_offset(int64_t shard_numel) {
     return ws_slot_offset(shard_numel) + round_up(kSlotBytes, 256);
 }
 
+// Where a rank's cast parameters go: its ZeRO-3 shard when given, else
+// its slice of the full buffer.
+inline unsigned short* param_out(const zero_step_args* a) {
+    if (a->param_shard) return static_cast<unsigned short*>(a->param_shard);
+    return static_cast<unsigned short*>(a->full_params) +
+           static_cast<size_t>(a->rank) * static_cast<size_t>(a->shard_numel);
+}
+
 // Checks every field of a step's arguments (see zero_shard_step).
 int validate_step_args(const zero_step_args* a);
 

@@ -464,8 +464,7 @@ int launch_combine(const void* partials, int n_slots, double peer_ss, int peer_o
 int launch_apply(const zero_step_args* a, const void* global, hipStream_t st) {
     const AdamConsts k = adam_consts(a->lr, a->beta1, a->beta2, a->eps, a->weight_decay, a->step);
     const dim3 grid(static_cast<unsigned>(apply_blocks_for(a->valid_numel)));
-    unsigned short* out = static_cast<unsigned short*>(a->full_params) +
-                          static_cast<size_t>(a->rank) * static_cast<size_t>(a->shard_numel);
+    unsigned short* out = param_out(a);
     const zero_global_t* gl = static_cast<const zero_global_t*>(global);
     const float* g = static_cast<const float*>(a->workspace);
     if (a->param_dtype == ZERO_BF16)
@@ -639,6 +638,37 @@ int zero_bucket_flatten(const zero_tensor_slot_t* slots, int32_t n_tensors, cons
         n_tensors, [&](int32_t t) { return static_cast<const unsigned short*>(src_dev[t]); },
         [&](int32_t t) { return slots[t].offset; }, [&](int32_t t) { return slots[t].numel; },
         static_cast<unsigned short*>(flat_dev), flat_numel, static_cast<hipStream_t>(stream));
+}
+
+int zero_gather_params(const zero_partition_t* p, const void* const* shards, int32_t dtype,
+                       int64_t lo, int64_t hi, void* dst, void* stream) {
+    clear_error();
+    if (!p || !shards || !dst) return fail(ZERO_EINVAL, "a required pointer is NULL");
+    if (dtype != ZERO_FP16 && dtype != ZERO_BF16)
+        return fail(ZERO_EINVAL, "dtype %d is not ZERO_FP16 or ZERO_BF16", dtype);
+    if (p->world_size < 1 || p->shard_numel * p->world_size < p->numel)
+        return fail(ZERO_EINVAL, "the partition is invalid (use zero_partition)");
+    if (lo < 0 || hi < lo || hi > p->numel)
+        return fail(ZERO_EINVAL, "range [%lld, %lld) outside [0, %lld)", (long long)lo,
+                    (long long)hi, (long long)p->numel);
+    if (!aligned16(dst)) return fail(ZERO_EALIGN, "dst is not 16-byte aligned");
+    if (hi == lo) return ZERO_OK;
+    const int64_t s = p->shard_numel, k0 = lo / s;
+    const int32_t n = static_cast<int32_t>((hi - 1) / s - k0 + 1);
+    for (int32_t q = 0; q < n; ++q) {
+        if (!shards[k0 + q]) return fail(ZERO_EINVAL, "shards[%lld] is NULL", (long long)(k0 + q));
+        if (reinterpret_cast<uintptr_t>(shards[k0 + q]) & 1u)
+            return fail(ZERO_EALIGN, "shards[%lld] is not 2-byte aligned", (long long)(k0 + q));
+    }
+    auto a_of = [&](int32_t q) { const int64_t k = k0 + q; return lo > k * s ? lo : k * s; };
+    auto b_of = [&](int32_t q) { const int64_t e = (k0 + q + 1) * s; return hi < e ? hi : e; };
+    return copy_ranges(
+        n,
+        [&](int32_t q) {
+            return static_cast<const unsigned short*>(shards[k0 + q]) + (a_of(q) - (k0 + q) * s);
+        },
+        [&](int32_t q) { return a_of(q) - lo; }, [&](int32_t q) { return b_of(q) - a_of(q); },
+        static_cast<unsigned short*>(dst), hi - lo, static_cast<hipStream_t>(stream));
 }
 
 int zero_repartition(const zero_partition_t* from, const float* const* src_dev,

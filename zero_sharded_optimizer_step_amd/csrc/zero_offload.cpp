@@ -171,8 +171,7 @@ int zero_offload_apply(const zero_step_args* a, const void* global_dev,
     const int64_t n = a->valid_numel, C = stg->chunk_elems;
     const int64_t n_chunks = (n + C - 1) / C;
     const float* g_dev = static_cast<const float*>(a->workspace);
-    uint16_t* out_dev = static_cast<uint16_t*>(a->full_params) +
-                        static_cast<size_t>(a->rank) * static_cast<size_t>(a->shard_numel);
+    uint16_t* out_dev = param_out(a);
     // Gradients come down on the caller's stream (after pass 1); parameters
     // go up on a second stream so the two directions of the link overlap.
     hipStream_t up = nullptr;
