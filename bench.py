@@ -40,13 +40,15 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="shard13b",
-                    choices=["shard13b", "ragged", "repartition", "offload"],
+                    choices=["shard13b", "ragged", "repartition", "offload", "zero3"],
                     help="shard13b: rank 0 of the 13B/8 flat model (the headline); "
                          "ragged: 2000 tensors flattened bucket by bucket, then the step of "
                          "all 8 ranks; repartition: the ragged model's optimizer state moved "
                          "from 8 ranks to 3 on the device, and one rank's checkpoint file "
                          "written and read back; offload: the 13B/8 shard with its optimizer "
-                         "state in pinned host memory (pass 1 on the GPU, AdamW on the host)")
+                         "state in pinned host memory (pass 1 on the GPU, AdamW on the host); "
+                         "zero3: the 13B model's bf16 parameters gathered layer by layer "
+                         "(40 layers) from 8 rank shards with prefetch")
     ap.add_argument("--host-threads", type=int, default=0,
                     help="offload: host threads for the update (0: all)")
     ap.add_argument("--chunk", type=int, default=1 << 25,
@@ -439,6 +441,58 @@ def run_offload(args, torch, Z, W):
     print(json.dumps(out), flush=True)
 
 
+def run_zero3(args, torch, Z, W):
+    """ZeRO-3 forward-pass gathering on the 13B/8 model: its bf16 parameters
+    sit as 8 rank shards (one 26 GB buffer); one step walks 40 equal layers
+    in order, each gathered from the shards on a side stream, prefetched
+    within a live bound of two layers.  Bytes: every parameter read from its
+    shard and written to its layer buffer, 4 B."""
+    from zero_sharded_optimizer_step_amd.zero3 import LayerGatherer
+    w = W.SHARD_13B_OF_8
+    part = Z.zero_partition(w.numel, w.world_size, w.alignment)
+    s = part.shard_numel
+    full = torch.empty(part.padded_numel, dtype=torch.bfloat16, device="cuda")
+    W.flat_normal(full, 0, w.numel, 0.02, ("bench-zero3",))
+    shards = [full[r * s:(r + 1) * s] for r in range(w.world_size)]
+    L = 40
+    sizes = [w.numel // L] * L
+    sizes[-1] += w.numel - sum(sizes)
+    g = LayerGatherer(part, shards, sizes, int(2e8), 2 * max(sizes))
+    stream = torch.cuda.current_stream()
+
+    def walk():
+        n = 0
+        for _, params in g.forward(stream):
+            n += params.numel()
+        return n
+
+    for _ in range(args.warmup):
+        walk()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        assert walk() == w.numel
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = 4 * w.numel
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": w.numel / (ms * 1e-3), "unit": "params/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "13B bf16 parameters as 8 rank shards, gathered as 40 layers with "
+                               "prefetch (live bound: 2 layers)", "params": w.numel,
+                   "layers": L},
+        "hbm_gbps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS, "bytes_per_step": nbytes,
+        "roofline": {"bound": "hbm", "kernel": "flatten_kernel (range copies of zero_gather_params)",
+                     "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def calibrate_copy(torch, n):
     """Plain copies of a known size, for scaling the HBM byte counters."""
     nbytes = 4 << 30
@@ -476,6 +530,9 @@ def main():
         return
     if args.workload == "offload":
         run_offload(args, torch, Z, W)
+        return
+    if args.workload == "zero3":
+        run_zero3(args, torch, Z, W)
         return
     r = run_shard13b(args, torch, Z, W)
     app_gbps = r["bytes_apply"] / (r["apply_ms"] * 1e-3) / 1e9
