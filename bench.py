@@ -58,7 +58,7 @@ def parse():
                          "micro-batches (the first sets the fp32 slice, the others add to it) "
                          "before the combine and AdamW")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=1 << 28,
+    ap.add_argument("--cpu-sample", type=int, default=1 << 29,
                     help="elements of the shard the CPU oracle is timed on")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="only run N torch copies of 4 GiB (counter calibration)")
