@@ -4,7 +4,8 @@
 
 Default workload: a 13B-parameter flat model over 8 data-parallel ranks;
 this GPU is rank 0 and owns a 1,625,000,064-element shard.  Eight bf16
-replica gradient slices, fp32 master weights and Adam moments, and the
+replica gradient slices, fp32 master weights and Adam moments (two sets,
+alternated step by step: pass 2 reads one and writes the other), and the
 13,000,000,512-element bf16 full parameter buffer sit in HBM before timing
 starts.  One step = replica reduce (+ unscale, inf/nan flag, partial norm),
 combine (norm, clip factor), AdamW + cast into the rank's slice of the full
@@ -57,6 +58,10 @@ def parse():
                     help="shard13b: gradient-accumulation window K; each step reduces K "
                          "micro-batches (the first sets the fp32 slice, the others add to it) "
                          "before the combine and AdamW")
+    ap.add_argument("--state-buffers", type=int, default=2, choices=[1, 2],
+                    help="shard13b: 2 keeps two fp32 state sets and alternates them, so "
+                         "pass 2 reads one and writes the other (the default); 1 updates "
+                         "one set in place")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 29,
                     help="elements of the shard the CPU oracle is timed on")
@@ -86,7 +91,7 @@ def log(msg):
 
 
 # ------------------------------------------------------------------ workloads
-def setup_shard13b(torch, Z, W):
+def setup_shard13b(torch, Z, W, state_buffers=1):
     w = W.SHARD_13B_OF_8
     part = Z.zero_partition(w.numel, w.world_size, w.alignment)
     s = part.shard_numel
@@ -103,27 +108,37 @@ def setup_shard13b(torch, Z, W):
     W.flat_normal(master, 0, w.numel, w.master_sigma, W.master_key(w, 0))
     m = torch.zeros(s, dtype=torch.float32, device=dev)
     v = torch.zeros(s, dtype=torch.float32, device=dev)
+    # the second state set of the ping-pong layout
+    alt = None
+    if state_buffers == 2:
+        alt = tuple(torch.zeros(s, dtype=torch.float32, device=dev) for _ in range(3))
     full = torch.zeros(part.padded_numel, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(Z.zero_shard_workspace_bytes(s), dtype=torch.uint8, device=dev)
     partials = torch.zeros(Z.zero_partials_bytes(1), dtype=torch.uint8, device=dev)
     glob = torch.zeros(256, dtype=torch.uint8, device=dev)
-    return dict(w=w, s=s, valid=valid, grads=grads, master=master, m=m, v=v, full=full, ws=ws,
-                partials=partials, glob=glob, nrep=w.world_size)
+    return dict(w=w, s=s, valid=valid, grads=grads, master=master, m=m, v=v, alt=alt, full=full,
+                ws=ws, partials=partials, glob=glob, nrep=w.world_size)
 
 
 def run_shard13b(args, torch, Z, W):
-    st = setup_shard13b(torch, Z, W)
+    st = setup_shard13b(torch, Z, W, args.state_buffers)
     w, s, valid = st["w"], st["s"], st["valid"]
     torch.cuda.synchronize()
 
     MB = args.micro_batches
+    sets = [(st["master"], st["m"], st["v"])] + ([st["alt"]] if st["alt"] else [])
 
     def step_args(t, accumulate=False):
-        return Z.StepArgs(world_size=w.world_size, rank=0, shard_numel=s, valid_numel=valid,
-                          replica_grads=st["grads"], master=st["master"], exp_avg=st["m"],
-                          exp_avg_sq=st["v"], full_params=st["full"], workspace=st["ws"],
-                          lr=w.lr, weight_decay=w.weight_decay, step=t,
-                          max_grad_norm=w.max_grad_norm, accumulate=accumulate)
+        # ping-pong: step t reads set (t - 1) % 2 and writes the other one
+        src = sets[(t - 1) % len(sets)]
+        a = Z.StepArgs(world_size=w.world_size, rank=0, shard_numel=s, valid_numel=valid,
+                       replica_grads=st["grads"], master=src[0], exp_avg=src[1],
+                       exp_avg_sq=src[2], full_params=st["full"], workspace=st["ws"],
+                       lr=w.lr, weight_decay=w.weight_decay, step=t,
+                       max_grad_norm=w.max_grad_norm, accumulate=accumulate)
+        if len(sets) == 2:
+            a.master_out, a.exp_avg_out, a.exp_avg_sq_out = sets[t % 2]
+        return a
 
     def fused_step(t):
         for j in range(MB - 1):
@@ -553,6 +568,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": W.SHARD_13B_OF_8.name, "shard_numel": r["st"]["s"],
                    "world_size": 8, "replicas": 8, "micro_batches": args.micro_batches,
+                   "state_buffers": args.state_buffers,
                    "grad_dtype": "bf16", "param_dtype": "bf16",
                    "lr": 6e-5, "weight_decay": 0.01, "max_grad_norm": 1.0},
         "hbm_gbps": step_gbps,

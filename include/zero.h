@@ -190,6 +190,15 @@ typedef struct {
      * full_params is not used (may be NULL); zero_gather_params collects a
      * layer's parameters from all ranks' shards before its forward.       */
     void* param_shard;
+    /* Optional second set of state buffers (device, fp32[shard_numel], 16-byte
+     * aligned, not overlapping master / exp_avg / exp_avg_sq): when all three
+     * are set, pass 2 reads the state from master, exp_avg, exp_avg_sq and
+     * writes the new state here instead of in place; a caller alternating
+     * two sets ("ping-pong") saves the in-place read-modify-write.  All NULL:
+     * in place.  Not used by zero_offload_apply (must be NULL there).      */
+    float* master_out;
+    float* exp_avg_out;
+    float* exp_avg_sq_out;
 } zero_step_args;
 
 /* Result of the cross-rank combine, 32 bytes in device memory. */

@@ -249,3 +249,19 @@ def test_accumulate_flag_must_be_zero_or_one():
     for rc in (Z.lib().zero_shard_step(ctypes.byref(c), 0.0, 0, None, None),
                Z.lib().zero_shard_accumulate(ctypes.byref(c), None)):
         assert rc == Z.ZERO_EINVAL and "accumulate" in Z.zero_last_error()
+
+
+def test_output_state_pointers_are_checked():
+    c = good_args().c_args()
+    c.master_out = 0x800000
+    rc = Z.lib().zero_shard_step(ctypes.byref(c), 0.0, 0, None, None)
+    assert rc == Z.ZERO_EINVAL and "together" in Z.zero_last_error()
+    c.exp_avg_out, c.exp_avg_sq_out = 0x900000, 0xA00008
+    assert Z.lib().zero_shard_step(ctypes.byref(c), 0.0, 0, None, None) == Z.ZERO_EALIGN
+    c.exp_avg_sq_out = c.exp_avg_sq
+    assert Z.lib().zero_shard_step(ctypes.byref(c), 0.0, 0, None, None) == Z.ZERO_EINVAL
+    c.exp_avg_sq_out = 0xA00000
+    st = Z.zero_offload_staging_t()
+    assert Z.lib().zero_offload_apply(ctypes.byref(c), 0x1000, ctypes.byref(st), None,
+                                      None) == Z.ZERO_EINVAL
+    assert "in place" in Z.zero_last_error()

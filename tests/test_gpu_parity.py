@@ -319,3 +319,31 @@ def test_accumulate_then_fused_step_equals_split_calls():
     for a, b in ((w1.master[0], w2.master[0]), (w1.exp_avg[0], w2.exp_avg[0]),
                  (w1.reduced_grad(0), w2.reduced_grad(0))):
         parity.assert_bitwise("fused vs split", parity.f32(a[:numel]), parity.f32(b[:numel]))
+
+
+def test_ping_pong_state_equals_in_place():
+    # Two state sets alternated step by step give the same bits as one set
+    # updated in place.
+    say("ping-pong state")
+    numel, K = 250_007, 4
+    hp = Hyper()
+    w1 = SimulatedWorld(numel, 1, n_replicas=8, alignment=128, grad_dtype=BF16)
+    w2 = SimulatedWorld(numel, 1, n_replicas=8, alignment=128, grad_dtype=BF16)
+    second = [torch.full((w2.s,), 9.0, device="cuda") for _ in range(3)]
+    for w in (w1, w2):
+        W.flat_normal(w.master[0], 0, numel, 0.02, ("ppm",))
+    sets = [list(w2.state(0)), second]
+    for t in range(1, K + 1):
+        for w in (w1, w2):
+            for i in range(8):
+                W.flat_normal(w.grads[i], 0, numel, 1e-2, ("pp", t, i))
+        w1.step(hp, t)
+        a = w2.rank_args(0, hp, t)
+        src, dst = sets[(t - 1) % 2], sets[t % 2]
+        a.master, a.exp_avg, a.exp_avg_sq = src
+        a.master_out, a.exp_avg_out, a.exp_avg_sq_out = dst
+        Z.zero_shard_step(a)
+    final = sets[K % 2]
+    for got, ref in zip(final, w1.state(0)):
+        parity.assert_bitwise("ping-pong state", parity.f32(got[:numel]), parity.f32(ref[:numel]))
+    parity.assert_bitwise("ping-pong params", parity.u16(w2.full_params), parity.u16(w1.full_params))

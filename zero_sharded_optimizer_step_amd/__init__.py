@@ -172,6 +172,9 @@ class StepArgs:
     param_dtype: Optional[int] = None
     accumulate: bool = False
     param_shard: object = None          # ZeRO-3: the rank's own parameter shard
+    master_out: object = None           # optional second state set (ping-pong)
+    exp_avg_out: object = None
+    exp_avg_sq_out: object = None
 
     def c_args(self) -> zero_step_args:
         reps = list(self.replica_grads)
@@ -193,6 +196,9 @@ class StepArgs:
         a.exp_avg_sq = _dptr(self.exp_avg_sq)
         a.full_params = _dptr(self.full_params)
         a.param_shard = _dptr(self.param_shard)
+        a.master_out = _dptr(self.master_out)
+        a.exp_avg_out = _dptr(self.exp_avg_out)
+        a.exp_avg_sq_out = _dptr(self.exp_avg_sq_out)
         a.workspace = _dptr(self.workspace)
         a.workspace_bytes = 0 if self.workspace is None else \
             self.workspace.numel() * self.workspace.element_size()

@@ -47,7 +47,8 @@ class zero_step_args(ctypes.Structure):
                 ("full_params", vp), ("workspace", vp), ("workspace_bytes", sz),
                 ("lr", f64), ("beta1", f64), ("beta2", f64), ("eps", f64),
                 ("weight_decay", f64), ("step", i64), ("loss_scale", f64),
-                ("grad_predivide", f64), ("max_grad_norm", f64), ("param_shard", vp)]
+                ("grad_predivide", f64), ("max_grad_norm", f64), ("param_shard", vp),
+                ("master_out", vp), ("exp_avg_out", vp), ("exp_avg_sq_out", vp)]
 
 
 class zero_global_t(ctypes.Structure):

@@ -86,6 +86,18 @@ int validate_step_args(const zero_step_args* a) {
             !aligned16(a->full_params) || !aligned16(a->param_shard))
             return fail(ZERO_EALIGN, "a state or parameter pointer is not 16-byte aligned");
     }
+    const int n_out = (a->master_out != nullptr) + (a->exp_avg_out != nullptr) +
+                      (a->exp_avg_sq_out != nullptr);
+    if (n_out != 0 && n_out != 3)
+        return fail(ZERO_EINVAL, "master_out, exp_avg_out and exp_avg_sq_out are set together");
+    if (n_out == 3) {
+        if (!aligned16(a->master_out) || !aligned16(a->exp_avg_out) || !aligned16(a->exp_avg_sq_out))
+            return fail(ZERO_EALIGN, "an output state pointer is not 16-byte aligned");
+        if (a->master_out == a->master || a->exp_avg_out == a->exp_avg ||
+            a->exp_avg_sq_out == a->exp_avg_sq)
+            return fail(ZERO_EINVAL, "output state must not be the input state (leave it NULL "
+                                     "to update in place)");
+    }
     // Start of this rank's slice of the full buffer: shard_numel is a
     // multiple of 8, so 2-byte elements keep 16-byte alignment.
     if (a->workspace_bytes < zero_shard_workspace_bytes(a->shard_numel))

@@ -261,12 +261,20 @@ __device__ __forceinline__ void adamw1(float g, float& p, float& m, float& v, co
 }
 
 // coef is 1 when clipping does not apply; multiplying by it is then exact.
-template <int PT>
+// In place (p2 == p, m2 == m, v2 == v) or, with OOP, from one set of state
+// buffers into another; the loads are all issued before the stores either
+// way.
+template <int PT, bool OOP>
 __global__ __launch_bounds__(kApplyThreads) void apply_kernel(
-    const float* __restrict__ g, float* __restrict__ p, float* __restrict__ m, float* __restrict__ v,
+    const float* g, const float* p, const float* m, const float* v, float* p2, float* m2, float* v2,
     unsigned short* __restrict__ out, int64_t n_valid, const zero_global_t* __restrict__ glob,
     AdamConsts k) {
     if (glob->overflow) return;                    // skipped step: touch nothing
+    if constexpr (!OOP) {
+        p2 = const_cast<float*>(p);
+        m2 = const_cast<float*>(m);
+        v2 = const_cast<float*>(v);
+    }
     const float coef = glob->coef;
     const int64_t q = xcd_block(blockIdx.x, gridDim.x) * kApplyThreads + threadIdx.x;
     const int64_t full = n_valid / kQuad;
@@ -281,9 +289,9 @@ __global__ __launch_bounds__(kApplyThreads) void apply_kernel(
             adamw1(gq[e] * coef, pe, me, ve, k);
             pq[e] = pe; mq[e] = me; vq[e] = ve;
         }
-        reinterpret_cast<f32x4*>(p)[q] = pq;
-        reinterpret_cast<f32x4*>(m)[q] = mq;
-        reinterpret_cast<f32x4*>(v)[q] = vq;
+        reinterpret_cast<f32x4*>(p2)[q] = pq;
+        reinterpret_cast<f32x4*>(m2)[q] = mq;
+        reinterpret_cast<f32x4*>(v2)[q] = vq;
         u32x2 o;
         o.x = pack2<PT>(pq.x, pq.y);
         o.y = pack2<PT>(pq.z, pq.w);
@@ -292,7 +300,7 @@ __global__ __launch_bounds__(kApplyThreads) void apply_kernel(
         for (int64_t j = q * kQuad; j < n_valid; ++j) {
             float pj = p[j], mj = m[j], vj = v[j];
             adamw1(g[j] * coef, pj, mj, vj, k);
-            p[j] = pj; m[j] = mj; v[j] = vj;
+            p2[j] = pj; m2[j] = mj; v2[j] = vj;
             out[j] = pack1<PT>(pj);
         }
     }
@@ -467,12 +475,19 @@ int launch_apply(const zero_step_args* a, const void* global, hipStream_t st) {
     unsigned short* out = param_out(a);
     const zero_global_t* gl = static_cast<const zero_global_t*>(global);
     const float* g = static_cast<const float*>(a->workspace);
-    if (a->param_dtype == ZERO_BF16)
-        hipLaunchKernelGGL(apply_kernel<ZERO_BF16>, grid, dim3(kApplyThreads), 0, st, g, a->master,
-                           a->exp_avg, a->exp_avg_sq, out, a->valid_numel, gl, k);
-    else
-        hipLaunchKernelGGL(apply_kernel<ZERO_FP16>, grid, dim3(kApplyThreads), 0, st, g, a->master,
-                           a->exp_avg, a->exp_avg_sq, out, a->valid_numel, gl, k);
+    const bool oop = a->master_out != nullptr;
+    float* p2 = oop ? a->master_out : a->master;
+    float* m2 = oop ? a->exp_avg_out : a->exp_avg;
+    float* v2 = oop ? a->exp_avg_sq_out : a->exp_avg_sq;
+#define ZERO_APPLY(PT, OOP)                                                                         \
+    hipLaunchKernelGGL((apply_kernel<PT, OOP>), grid, dim3(kApplyThreads), 0, st, g, a->master,      \
+                       a->exp_avg, a->exp_avg_sq, p2, m2, v2, out, a->valid_numel, gl, k)
+    if (a->param_dtype == ZERO_BF16) {
+        if (oop) ZERO_APPLY(ZERO_BF16, true); else ZERO_APPLY(ZERO_BF16, false);
+    } else {
+        if (oop) ZERO_APPLY(ZERO_FP16, true); else ZERO_APPLY(ZERO_FP16, false);
+    }
+#undef ZERO_APPLY
     return launch_error("apply kernel launch");
 }
 

@@ -151,6 +151,8 @@ int zero_offload_apply(const zero_step_args* a, const void* global_dev,
     if (rc) return rc;
     if (!global_dev) return fail(ZERO_EINVAL, "global_dev is NULL");
     if (!aligned16(global_dev)) return fail(ZERO_EALIGN, "global_dev is not 16-byte aligned");
+    if (a->master_out || a->exp_avg_out || a->exp_avg_sq_out)
+        return fail(ZERO_EINVAL, "the offloaded step updates the host state in place");
     if (!stg) return fail(ZERO_EINVAL, "staging is NULL");
     if (stg->chunk_elems < 1 || stg->chunk_elems % 8 != 0)
         return fail(ZERO_EINVAL, "chunk_elems %lld is not a positive multiple of 8",
