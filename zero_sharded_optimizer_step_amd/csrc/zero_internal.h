@@ -24,11 +24,13 @@ inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // consecutive elements and launch one thread per quad (no grid-stride
 // loop): blocks are dispatched in order, so the set of addresses in flight
 // stays a compact window of every stream, which keeps HBM pages open.  The
-// block count is a multiple of 8 and dispatch-order block b is mapped to
-// logical block (b % 8) * (blocks / 8) + b / 8: the hardware deals blocks to
-// the 8 XCDs round robin, so each XCD walks its own contiguous eighth of the
-// shard.  Everything depends only on valid_numel, so the per-block partial
-// sums, and hence the norm, are identical from run to run.
+// hardware deals dispatch-order blocks to the 8 XCDs round robin; the
+// kernels remap them so that each XCD takes runs of `group` consecutive
+// logical blocks (256 for large grids, measured best; the whole eighth of
+// the grid for small ones), which keeps every XCD on contiguous memory
+// while all of them advance through the shard together.  Everything
+// depends only on valid_numel, so the per-block partial sums, and hence the
+// norm, are identical from run to run.
 constexpr int kQuad = 4;
 // shard_numel must be a multiple of this, so that every rank's slice of the
 // full 16-bit parameter buffer starts on a 16-byte boundary.
@@ -56,15 +58,27 @@ constexpr size_t kSlotBytes = sizeof(SlotHeader) + kFoldBlocks * sizeof(Partial)
 // Quads (the last one possibly partial) of n elements.
 inline int64_t quads_of(int64_t n) { return (n + kQuad - 1) / kQuad; }
 
-// Blocks of `threads` threads covering quads_of(n) quads, at least one,
-// rounded up to a multiple of kXcds.
-inline int64_t grid_for(int64_t n, int threads) {
+// A launch: `blocks` (a multiple of kXcds * group) of which the first
+// `needed` hold work, remapped in XCD runs of `group` logical blocks.
+struct Grid {
+    int64_t blocks;
+    int32_t group;
+};
+constexpr int64_t kXcdGroup = 256;
+
+// Blocks of `threads` threads covering quads_of(n) quads, at least one.
+inline Grid grid_for(int64_t n, int threads) {
     int64_t b = (quads_of(n) + threads - 1) / threads;
     if (b < 1) b = 1;
-    return (b + kXcds - 1) / kXcds * kXcds;
+    if (b >= kXcds * kXcdGroup) {
+        const int64_t unit = kXcds * kXcdGroup;
+        return Grid{(b + unit - 1) / unit * unit, static_cast<int32_t>(kXcdGroup)};
+    }
+    const int64_t nb = (b + kXcds - 1) / kXcds * kXcds;
+    return Grid{nb, static_cast<int32_t>(nb / kXcds)};
 }
-inline int64_t reduce_blocks_for(int64_t n) { return grid_for(n, kReduceThreads); }
-inline int64_t apply_blocks_for(int64_t n) { return grid_for(n, kApplyThreads); }
+inline int64_t reduce_blocks_for(int64_t n) { return grid_for(n, kReduceThreads).blocks; }
+inline int64_t apply_blocks_for(int64_t n) { return grid_for(n, kApplyThreads).blocks; }
 inline int fold_blocks_for(int64_t reduce_blocks) {
     return static_cast<int>(reduce_blocks < kFoldBlocks ? reduce_blocks : kFoldBlocks);
 }

@@ -35,11 +35,13 @@ struct ReplicaPtrs {
     const u32x2* p[ZERO_MAX_REPLICAS];
 };
 
-// Logical block of dispatch-order block b in a grid of nb (a multiple of
-// kXcds) blocks: XCD b % 8 takes the contiguous run of logical blocks
-// [(b % 8) * nb / 8, (b % 8 + 1) * nb / 8).
-__device__ __forceinline__ int64_t xcd_block(int64_t b, int64_t nb) {
-    return (b % kXcds) * (nb / kXcds) + b / kXcds;
+// Logical block of dispatch-order block b (which the hardware sends to XCD
+// b % 8) in a grid that is a multiple of 8 * group blocks: XCD x takes
+// logical blocks [k * 8 * group + x * group, ... + group) for k = 0, 1, ...
+// With group = grid / 8 that is one contiguous eighth of the grid per XCD.
+__device__ __forceinline__ int64_t xcd_block(uint32_t b, uint32_t group) {
+    const uint32_t x = b % kXcds, j = b / kXcds;
+    return static_cast<int64_t>(j / group) * (kXcds * group) + x * group + j % group;
 }
 
 // ---------------------------------------------------------------- formats
@@ -138,8 +140,8 @@ __device__ __forceinline__ void sum_quad(const ReplicaPtrs& reps, int nrep, int6
 template <int DT, int NR, bool ACC>
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(
     ReplicaPtrs reps, int nrep, int64_t n_valid, float inv_scale, float* __restrict__ g,
-    Partial* __restrict__ partials) {
-    const int64_t blk = xcd_block(blockIdx.x, gridDim.x);
+    Partial* __restrict__ partials, uint32_t group) {
+    const int64_t blk = xcd_block(blockIdx.x, group);
     const int64_t q = blk * kReduceThreads + threadIdx.x;
     const int64_t full = n_valid / kQuad;              // complete quads
     double ss = 0.0;
@@ -158,7 +160,8 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(
             ss += static_cast<double>(gk) * static_cast<double>(gk);
             o[k] = gk;
         }
-        reinterpret_cast<f32x4*>(g)[q] = o;
+        // streamed out: the next read is a whole pass away
+        __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(g) + q);
     } else if (q == full) {
         // Ragged tail: the 0-3 elements after the last complete quad.
         for (int64_t i = q * kQuad; i < n_valid; ++i) {
@@ -268,7 +271,7 @@ template <int PT, bool OOP>
 __global__ __launch_bounds__(kApplyThreads) void apply_kernel(
     const float* g, const float* p, const float* m, const float* v, float* p2, float* m2, float* v2,
     unsigned short* __restrict__ out, int64_t n_valid, const zero_global_t* __restrict__ glob,
-    AdamConsts k) {
+    AdamConsts k, uint32_t group) {
     if (glob->overflow) return;                    // skipped step: touch nothing
     if constexpr (!OOP) {
         p2 = const_cast<float*>(p);
@@ -276,7 +279,7 @@ __global__ __launch_bounds__(kApplyThreads) void apply_kernel(
         v2 = const_cast<float*>(v);
     }
     const float coef = glob->coef;
-    const int64_t q = xcd_block(blockIdx.x, gridDim.x) * kApplyThreads + threadIdx.x;
+    const int64_t q = xcd_block(blockIdx.x, group) * kApplyThreads + threadIdx.x;
     const int64_t full = n_valid / kQuad;
     if (q < full) {
         f32x4 gq = reinterpret_cast<const f32x4*>(g)[q];
@@ -289,13 +292,14 @@ __global__ __launch_bounds__(kApplyThreads) void apply_kernel(
             adamw1(gq[e] * coef, pe, me, ve, k);
             pq[e] = pe; mq[e] = me; vq[e] = ve;
         }
-        reinterpret_cast<f32x4*>(p2)[q] = pq;
-        reinterpret_cast<f32x4*>(m2)[q] = mq;
-        reinterpret_cast<f32x4*>(v2)[q] = vq;
+        // streamed out: nothing reads these again in this step
+        __builtin_nontemporal_store(pq, reinterpret_cast<f32x4*>(p2) + q);
+        __builtin_nontemporal_store(mq, reinterpret_cast<f32x4*>(m2) + q);
+        __builtin_nontemporal_store(vq, reinterpret_cast<f32x4*>(v2) + q);
         u32x2 o;
         o.x = pack2<PT>(pq.x, pq.y);
         o.y = pack2<PT>(pq.z, pq.w);
-        reinterpret_cast<u32x2*>(out)[q] = o;
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(out) + q);
     } else if (q == full) {
         for (int64_t j = q * kQuad; j < n_valid; ++j) {
             float pj = p[j], mj = m[j], vj = v[j];
@@ -354,7 +358,7 @@ __device__ __forceinline__ u32x4 shift_pick(const u32x4 lo, const u32x4 hi, int 
 }
 
 __global__ __launch_bounds__(kFlatThreads) void flatten_kernel(FlatBatch b, unsigned short* __restrict__ flat) {
-    const int64_t blk = xcd_block(blockIdx.x, gridDim.x);
+    const int64_t blk = xcd_block(blockIdx.x, gridDim.x / kXcds);
     if (blk >= b.first_block[b.count]) return;       // grid rounded up to the XCD count
     // Which table entry owns this block: binary search over the prefix.
     int lo = 0, hi = b.count - 1;
@@ -414,18 +418,20 @@ int launch_error(const char* what) {
 template <int DT, bool ACC>
 void launch_reduce_dt(const ReplicaPtrs& reps, int nrep, int64_t n_valid, float inv, float* g,
                       Partial* parts, hipStream_t st) {
-    const dim3 grid(static_cast<unsigned>(reduce_blocks_for(n_valid)));
+    const Grid gr = grid_for(n_valid, kReduceThreads);
+    const dim3 grid(static_cast<unsigned>(gr.blocks));
+    const uint32_t group = static_cast<uint32_t>(gr.group);
 #define ZERO_REDUCE_CASE(NR)                                                                   \
     case NR:                                                                                   \
         hipLaunchKernelGGL((reduce_kernel<DT, NR, ACC>), grid, dim3(kReduceThreads), 0, st, reps, \
-                           nrep, n_valid, inv, g, parts);                                      \
+                           nrep, n_valid, inv, g, parts, group);                               \
         break;
     switch (nrep) {
         ZERO_REDUCE_CASE(1) ZERO_REDUCE_CASE(2) ZERO_REDUCE_CASE(3) ZERO_REDUCE_CASE(4)
         ZERO_REDUCE_CASE(5) ZERO_REDUCE_CASE(6) ZERO_REDUCE_CASE(7) ZERO_REDUCE_CASE(8)
         default:
             hipLaunchKernelGGL((reduce_kernel<DT, 0, ACC>), grid, dim3(kReduceThreads), 0, st, reps,
-                               nrep, n_valid, inv, g, parts);
+                               nrep, n_valid, inv, g, parts, group);
     }
 #undef ZERO_REDUCE_CASE
 }
@@ -471,7 +477,9 @@ int launch_combine(const void* partials, int n_slots, double peer_ss, int peer_o
 
 int launch_apply(const zero_step_args* a, const void* global, hipStream_t st) {
     const AdamConsts k = adam_consts(a->lr, a->beta1, a->beta2, a->eps, a->weight_decay, a->step);
-    const dim3 grid(static_cast<unsigned>(apply_blocks_for(a->valid_numel)));
+    const Grid gr = grid_for(a->valid_numel, kApplyThreads);
+    const dim3 grid(static_cast<unsigned>(gr.blocks));
+    const uint32_t group = static_cast<uint32_t>(gr.group);
     unsigned short* out = param_out(a);
     const zero_global_t* gl = static_cast<const zero_global_t*>(global);
     const float* g = static_cast<const float*>(a->workspace);
@@ -481,7 +489,7 @@ int launch_apply(const zero_step_args* a, const void* global, hipStream_t st) {
     float* v2 = oop ? a->exp_avg_sq_out : a->exp_avg_sq;
 #define ZERO_APPLY(PT, OOP)                                                                         \
     hipLaunchKernelGGL((apply_kernel<PT, OOP>), grid, dim3(kApplyThreads), 0, st, g, a->master,      \
-                       a->exp_avg, a->exp_avg_sq, p2, m2, v2, out, a->valid_numel, gl, k)
+                       a->exp_avg, a->exp_avg_sq, p2, m2, v2, out, a->valid_numel, gl, k, group)
     if (a->param_dtype == ZERO_BF16) {
         if (oop) ZERO_APPLY(ZERO_BF16, true); else ZERO_APPLY(ZERO_BF16, false);
     } else {
