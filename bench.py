@@ -58,10 +58,10 @@ def parse():
                     help="shard13b: gradient-accumulation window K; each step reduces K "
                          "micro-batches (the first sets the fp32 slice, the others add to it) "
                          "before the combine and AdamW")
-    ap.add_argument("--state-buffers", type=int, default=2, choices=[1, 2],
-                    help="shard13b: 2 keeps two fp32 state sets and alternates them, so "
-                         "pass 2 reads one and writes the other (the default); 1 updates "
-                         "one set in place")
+    ap.add_argument("--state-buffers", type=int, default=1, choices=[1, 2],
+                    help="shard13b: 1 updates one fp32 state set in place (the default); "
+                         "2 keeps two sets and alternates them, so pass 2 reads one and "
+                         "writes the other")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 29,
                     help="elements of the shard the CPU oracle is timed on")

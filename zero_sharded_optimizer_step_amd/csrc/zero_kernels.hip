@@ -149,7 +149,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(
     if (q < full) {
         float acc[4];
         f32x4 prev;
-        if constexpr (ACC) prev = reinterpret_cast<const f32x4*>(g)[q];
+        if constexpr (ACC) prev = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g) + q);
         sum_quad<DT, NR>(reps, nrep, q, acc);
         f32x4 o;
         #pragma unroll
@@ -266,7 +266,8 @@ __device__ __forceinline__ void adamw1(float g, float& p, float& m, float& v, co
 // coef is 1 when clipping does not apply; multiplying by it is then exact.
 // In place (p2 == p, m2 == m, v2 == v) or, with OOP, from one set of state
 // buffers into another; the loads are all issued before the stores either
-// way.
+// way.  Every stream is touched once per step, so loads and stores are all
+// nontemporal.
 template <int PT, bool OOP>
 __global__ __launch_bounds__(kApplyThreads) void apply_kernel(
     const float* g, const float* p, const float* m, const float* v, float* p2, float* m2, float* v2,
@@ -282,17 +283,16 @@ __global__ __launch_bounds__(kApplyThreads) void apply_kernel(
     const int64_t q = xcd_block(blockIdx.x, group) * kApplyThreads + threadIdx.x;
     const int64_t full = n_valid / kQuad;
     if (q < full) {
-        f32x4 gq = reinterpret_cast<const f32x4*>(g)[q];
-        f32x4 pq = reinterpret_cast<const f32x4*>(p)[q];
-        f32x4 mq = reinterpret_cast<const f32x4*>(m)[q];
-        f32x4 vq = reinterpret_cast<const f32x4*>(v)[q];
+        const f32x4 gq = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g) + q);
+        f32x4 pq = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + q);
+        f32x4 mq = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(m) + q);
+        f32x4 vq = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(v) + q);
         #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float pe = pq[e], me = mq[e], ve = vq[e];
             adamw1(gq[e] * coef, pe, me, ve, k);
             pq[e] = pe; mq[e] = me; vq[e] = ve;
         }
-        // streamed out: nothing reads these again in this step
         __builtin_nontemporal_store(pq, reinterpret_cast<f32x4*>(p2) + q);
         __builtin_nontemporal_store(mq, reinterpret_cast<f32x4*>(m2) + q);
         __builtin_nontemporal_store(vq, reinterpret_cast<f32x4*>(v2) + q);
