@@ -320,7 +320,8 @@ __global__ __launch_bounds__(kApplyThreads) void apply_kernel(
 // elements before the first and after the last aligned destination vector
 // of a tensor are copied one by one by its first block.  Blocks of one
 // launch are spread over the XCDs like the step's kernels, so each XCD
-// copies a contiguous run of the batch's tensors.
+// copies a contiguous run of the batch's tensors.  The body is stored
+// nontemporally: nothing reads it again before the next pass.
 constexpr int kFlatBatch = 128;            // tensors per launch (kernel arguments)
 constexpr int kFlatThreads = 256;
 constexpr int64_t kFlatMaxPiece = int64_t(1) << 30;   // elements per table entry
@@ -379,7 +380,7 @@ __global__ __launch_bounds__(kFlatThreads) void flatten_kernel(FlatBatch b, unsi
     const int64_t nv = (a1 - a0) / 8;
     const int64_t q = jb * kFlatThreads + threadIdx.x;   // body vector of this thread
     if (src == nullptr) {
-        if (q < nv) dvec[a0 / 8 + q] = u32x4{0u, 0u, 0u, 0u};
+        if (q < nv) __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, dvec + a0 / 8 + q);
         if (jb == 0) {
             if (threadIdx.x < a0 - d0) flat[d0 + threadIdx.x] = 0;
             if (threadIdx.x >= 8 && threadIdx.x - 8 < d1 - a1) flat[a1 + threadIdx.x - 8] = 0;
@@ -397,7 +398,7 @@ __global__ __launch_bounds__(kFlatThreads) void flatten_kernel(FlatBatch b, unsi
         u32x4 o;
         if (k == 0) o = sbase[sv0 + q];
         else o = shift_pick(sbase[sv0 + q], sbase[sv0 + q + 1], k);
-        dvec[a0 / 8 + q] = o;
+        __builtin_nontemporal_store(o, dvec + a0 / 8 + q);
     }
     if (jb == 0) {
         if (threadIdx.x < a0 - d0) flat[d0 + threadIdx.x] = src[threadIdx.x];
