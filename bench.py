@@ -51,7 +51,8 @@ def parse():
                          "zero3: the 13B model's bf16 parameters gathered layer by layer "
                          "(40 layers) from 8 rank shards with prefetch")
     ap.add_argument("--host-threads", type=int, default=0,
-                    help="offload: host threads for the update (0: all)")
+                    help="offload: host threads for the update (0: the library's default, "
+                         "OMP_NUM_THREADS or the process's CPU affinity)")
     ap.add_argument("--chunk", type=int, default=1 << 25,
                     help="offload: elements per transfer chunk")
     ap.add_argument("--micro-batches", type=int, default=1,
@@ -391,7 +392,6 @@ def run_offload(args, torch, Z, W):
     """The 13B/8 shard with its fp32 master and moments in pinned host memory:
     pass 1 and the combine on the GPU, then zero_offload_apply (gradient
     down, host AdamW, parameters up, pipelined by chunk)."""
-    import multiprocessing
     w = W.SHARD_13B_OF_8
     part = Z.zero_partition(w.numel, w.world_size, w.alignment)
     s = part.shard_numel
@@ -441,7 +441,7 @@ def run_offload(args, torch, Z, W):
     sec = (time.perf_counter() - t0) / K
     pcie = valid * (4 + 2)
     host_bytes = valid * (12 + 12 + 4 + 2)     # state read + written, staged gradient, cast
-    threads = args.host_threads or multiprocessing.cpu_count()
+    threads = args.host_threads or Z.zero_host_threads()
     out = {
         "metric": METRIC, "value": valid / sec, "unit": "params/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": sec * 1e3, "higher_is_better": True,

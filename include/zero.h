@@ -363,7 +363,7 @@ typedef struct {
     void*   grad_stage[2];    /* host, chunk_elems * 4 bytes each (pinned)   */
     void*   param_stage[2];   /* host, chunk_elems * 2 bytes each (pinned)   */
     int64_t chunk_elems;      /* > 0, a multiple of 8                        */
-    int32_t n_threads;        /* host threads for the update; 0: all cores   */
+    int32_t n_threads;        /* host threads; 0: zero_host_threads()        */
     int32_t reserved;
 } zero_offload_staging_t;
 
@@ -382,12 +382,19 @@ int zero_offload_apply(const zero_step_args* a, const void* global_dev,
  * master, exp_avg, exp_avg_sq (fp32, in place), and, if params_out is not
  * NULL, params_out[i] = round-to-nearest-even of the new master in
  * param_dtype.  Hyper-parameters as in zero_step_args; step is t >= 1.
- * n_threads 0 uses every hardware thread.  Errors: n < 0, a NULL array
+ * n_threads 0 uses zero_host_threads().  Errors: n < 0, a NULL array
  * when n > 0, bad dtype or hyper-parameters -> ZERO_EINVAL.  Host only. */
 int zero_host_adamw(int64_t n, const float* g, float coef, float* master, float* exp_avg,
                     float* exp_avg_sq, void* params_out, int32_t param_dtype, double lr,
                     double beta1, double beta2, double eps, double weight_decay,
                     int64_t step, int32_t n_threads);
+
+/* The host thread count that n_threads = 0 selects: OMP_NUM_THREADS when it
+ * is set to a positive number, else the number of CPUs the calling process
+ * may run on (its affinity mask), else the hardware's thread count.  A
+ * container whose CPU share is smaller than the host sets one of the first
+ * two.  Never fails; at least 1. */
+int32_t zero_host_threads(void);
 
 /* ------------------------------------------------------------------------
  * Sharded checkpoint and resume.  [P2] practice notes: a sharded run must be

@@ -2,6 +2,8 @@
 optimizer step) against the oracle: same fp32 operations in the same order,
 so the same bits, on any thread count; and its round-to-nearest-even casts
 on midpoints, subnormals, the overflow edge and NaN."""
+import os
+
 import numpy as np
 import pytest
 
@@ -74,3 +76,20 @@ def test_host_adamw_rejects():
         Z.zero_host_adamw(g, 1.0, g.copy(), g.copy(), g.copy(), None, 7)
     with pytest.raises(Z.ZeroError):
         Z.zero_host_adamw(g, float("nan"), g.copy(), g.copy(), g.copy(), None, Z.ZERO_BF16)
+
+
+def test_host_threads_default_follows_omp_and_affinity():
+    """n_threads = 0 resolves to OMP_NUM_THREADS, else the affinity mask."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import sys; sys.path.insert(0, %r); import zero_sharded_optimizer_step_amd as Z; "
+            "print(Z.zero_host_threads())" % root)
+    env = dict(os.environ, OMP_NUM_THREADS="3")
+    out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                         check=True).stdout
+    assert int(out) == 3
+    env.pop("OMP_NUM_THREADS")
+    out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                         check=True).stdout
+    assert int(out) == len(os.sched_getaffinity(0))

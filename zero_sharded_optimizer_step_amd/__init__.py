@@ -27,7 +27,7 @@ __all__ = [
     "zero_partials_bytes", "zero_shard_reduce", "zero_shard_accumulate", "zero_shard_combine",
     "zero_shard_apply", "zero_shard_step", "zero_loss_scaler_init",
     "zero_loss_scaler_update", "zero_ckpt_header_make", "zero_ckpt_header_check",
-    "zero_repartition", "zero_gather_params", "zero_offload_apply", "zero_host_adamw",
+    "zero_repartition", "zero_gather_params", "zero_offload_apply", "zero_host_adamw", "zero_host_threads",
     "OffloadStaging",
     "StepArgs", "dtype_code", "GLOBAL_BYTES",
 ]
@@ -309,6 +309,11 @@ def zero_offload_apply(args, global_buf, staging: OffloadStaging, want_info: boo
                                    ctypes.byref(info) if info is not None else None,
                                    _stream(stream)), "zero_offload_apply")
     return info
+
+
+def zero_host_threads() -> int:
+    """Host threads the offloaded update uses when n_threads is 0."""
+    return int(lib().zero_host_threads())
 
 
 def zero_host_adamw(g, coef: float, master, exp_avg, exp_avg_sq, params_out=None,

@@ -119,6 +119,7 @@ _PROTOTYPES = {
                                           ctypes.POINTER(zero_step_info), vp]),
     "zero_host_adamw": (ctypes.c_int, [i64, vp, f32, vp, vp, vp, vp, i32, f64, f64, f64, f64,
                                        f64, i64, i32]),
+    "zero_host_threads": (i32, []),
 }
 
 _lib = None

@@ -11,8 +11,11 @@
 // written from the formats' bit layouts.
 #include <hip/hip_runtime_api.h>
 
+#include <sched.h>
+
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <thread>
 #include <vector>
@@ -90,11 +93,28 @@ void adamw_range(const HostUpdate& u, int64_t lo, int64_t hi, const float* g, fl
     }
 }
 
+// The thread count used when the caller passes 0: OMP_NUM_THREADS when it
+// is set to a positive number, else the CPUs this process may run on, else
+// the hardware's thread count.
+int default_host_threads() {
+    if (const char* env = std::getenv("OMP_NUM_THREADS")) {
+        const long v = std::strtol(env, nullptr, 10);
+        if (v > 0) return static_cast<int>(std::min<long>(v, 1024));
+    }
+    cpu_set_t set;
+    if (sched_getaffinity(0, sizeof(set), &set) == 0) {
+        const int c = CPU_COUNT(&set);
+        if (c > 0) return c;
+    }
+    const unsigned h = std::thread::hardware_concurrency();
+    return h > 0 ? static_cast<int>(h) : 1;
+}
+
 // Split [0, n) into contiguous ranges of whole 64-byte lines, one per
 // thread, and run them.
 void adamw_parallel(const HostUpdate& u, int64_t n, const float* g, float* p, float* m, float* v,
                     uint16_t* out, int n_threads) {
-    int t = n_threads > 0 ? n_threads : static_cast<int>(std::thread::hardware_concurrency());
+    int t = n_threads > 0 ? n_threads : default_host_threads();
     if (t < 1) t = 1;
     const int64_t min_per = int64_t(1) << 16;
     if (static_cast<int64_t>(t) * min_per > n) t = static_cast<int>(std::max<int64_t>(1, n / min_per));
@@ -122,6 +142,8 @@ int hip_fail(hipError_t e, const char* what) {
 using namespace zero;
 
 extern "C" {
+
+int32_t zero_host_threads(void) { return default_host_threads(); }
 
 int zero_host_adamw(int64_t n, const float* g, float coef, float* master, float* exp_avg,
                     float* exp_avg_sq, void* params_out, int32_t param_dtype, double lr,
