@@ -178,6 +178,8 @@ BAD = [
     (dict(eps=0.0), Z.ZERO_EINVAL), (dict(lr=float("nan")), Z.ZERO_EINVAL),
     (dict(max_grad_norm=float("nan")), Z.ZERO_EINVAL), (dict(grad_dtype=3), Z.ZERO_EINVAL),
     (dict(param_dtype=0), Z.ZERO_EINVAL), (dict(replica_grads=[]), Z.ZERO_EINVAL),
+    (dict(replica_grads=[FakeTensor(0x10000 * (i + 1)) for i in range(Z.ZERO_MAX_REPLICAS + 1)]),
+     Z.ZERO_EINVAL),
     (dict(master=FakeTensor(0)), Z.ZERO_EINVAL),
     (dict(master=FakeTensor(0x100004)), Z.ZERO_EALIGN),
     (dict(full_params=FakeTensor(0x400002)), Z.ZERO_EALIGN),

@@ -31,7 +31,7 @@ CASES = [
     (100_003, 8, 128, BF16, 1e-3, 1.0, 1.0, 3),
     (100_003, 8, 128, BF16, 1e-3, 1.0, 0.0, 3),     # clipping off
     (1_048_583, 4, 128, FP16, 1e-3, 2.0**12, 1e9, 2),  # clip threshold never reached
-    (3_000_001, 2, 128, BF16, 3e-2, 1.0, 1.0, 2),   # >1 grid-stride iteration per thread
+    (3_000_001, 2, 128, BF16, 3e-2, 1.0, 1.0, 2),   # 1.5M-element shards, 2 ranks
 ]
 
 
@@ -63,6 +63,18 @@ def test_more_replicas_than_ranks_and_generic_replica_count():
     say("11 replicas, 3 ranks")
     spec = parity.Spec(numel=50_001, world_size=3, n_replicas=11, alignment=8, grad_dtype=BF16,
                        grad_sigma=1e-2, steps=2, name="generic-replicas")
+    parity.run(spec)
+
+
+@pytest.mark.parametrize("nrep,dt", [(1, BF16), (5, FP16), (6, BF16), (7, FP16), (64, BF16)])
+def test_each_replica_count(nrep, dt):
+    # The reduce is compiled for 1..8 replicas and has a generic loop above;
+    # these cover the counts no other case reaches, up to the maximum.
+    say("%d replicas, 3 ranks, %s" % (nrep, str(dt)[6:]))
+    scale = 2.0**12 if dt == FP16 else 1.0
+    spec = parity.Spec(numel=30_011, world_size=3, n_replicas=nrep, alignment=8, grad_dtype=dt,
+                       grad_sigma=1e-3, steps=2, name="replicas-%d" % nrep,
+                       hp=Hyper(loss_scale=scale))
     parity.run(spec)
 
 
@@ -134,6 +146,57 @@ def test_run_to_run_bitwise_determinism():
     for x, y in zip(a[3], b[3]):
         parity.assert_bitwise("rerun", x, y)
     parity.assert_bitwise("rerun params", a[4], b[4])
+
+
+def test_concurrent_threads_and_streams_equal_one_stream():
+    # The library keeps no state between calls: four host threads, each
+    # queueing one rank's reduce and apply on its own stream at the same
+    # time, give the bits of the same step queued on one stream.
+    import threading
+    say("4 ranks on 4 threads and 4 streams")
+    worlds = [SimulatedWorld(2_000_003, 4, alignment=128, grad_dtype=BF16) for _ in range(2)]
+    for w in worlds:
+        _fill(w, 3)
+    hp = Hyper()
+    worlds[0].step(hp, 1)
+    w = worlds[1]
+    args = [w.rank_args(k, hp, 1) for k in range(4)]
+    main = torch.cuda.current_stream()
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    errors = []
+
+    def on_threads(fn):
+        def body(k):
+            try:
+                with torch.cuda.stream(streams[k]):
+                    fn(k)
+            except Exception as e:          # reported after the join
+                errors.append(e)
+        ts = [threading.Thread(target=body, args=(k,)) for k in range(4)]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+        assert not errors, errors
+
+    for st in streams:
+        st.wait_stream(main)
+    on_threads(lambda k: Z.zero_shard_reduce(args[k], k, w.partials, streams[k]))
+    for st in streams:
+        main.wait_stream(st)
+    Z.zero_shard_combine(w.partials, 4, hp.max_grad_norm, w.global_buf, main)
+    for st in streams:
+        st.wait_stream(main)
+    on_threads(lambda k: Z.zero_shard_apply(args[k], w.global_buf, streams[k]))
+    for st in streams:
+        main.wait_stream(st)
+    torch.cuda.synchronize()
+    a, b = worlds[0].result(), w.result()
+    assert (a.sumsq, a.norm, a.coef, a.overflow) == (b.sumsq, b.norm, b.coef, b.overflow)
+    for x, y in zip(worlds[0].master + worlds[0].exp_avg + worlds[0].exp_avg_sq,
+                    w.master + w.exp_avg + w.exp_avg_sq):
+        parity.assert_bitwise("state", parity.f32(y), parity.f32(x))
+    parity.assert_bitwise("params", parity.u16(w.full_params), parity.u16(worlds[0].full_params))
 
 
 def test_sharded_concatenation_equals_unsharded_on_gpu():
