@@ -97,6 +97,10 @@ def lib():
         L.oracle_reduce.restype = None
         L.oracle_reduce_accumulate.argtypes = [i32, vp, i32, i64, f32, vp, vp, vp]
         L.oracle_reduce_accumulate.restype = None
+        L.oracle_accumulate_local.argtypes = [i32, i64, vp, vp, i32]
+        L.oracle_accumulate_local.restype = None
+        L.oracle_reduce_f32.argtypes = [i32, vp, i64, f32, vp, vp, vp]
+        L.oracle_reduce_f32.restype = None
         L.oracle_clip.argtypes = [f64, f64, vp, vp]
         L.oracle_clip.restype = i32
         L.oracle_adamw.argtypes = [i64, vp, vp, vp, vp, f64, f64, f64, f64,
@@ -211,6 +215,33 @@ def reduce_accumulate(replicas, dtype: int, inv: float, g: np.ndarray, sumsq: fl
     lib().oracle_reduce_accumulate(len(reps), ctypes.addressof(arr), dtype, n, np.float32(inv),
                                    _ptr(g), ctypes.addressof(ss), ctypes.addressof(of))
     return ss.value, of.value
+
+
+def accumulate_local(micro_grads, dtype: int) -> np.ndarray:
+    """One replica's micro-batch gradients (16-bit codes, equal lengths)
+    summed into a new fp32 buffer in micro-batch order: the first sets it,
+    each later one adds."""
+    grads = [np.ascontiguousarray(x, dtype=np.uint16) for x in micro_grads]
+    n = grads[0].size
+    assert all(x.size == n for x in grads)
+    acc = np.empty(n, dtype=np.float32)
+    for j, x in enumerate(grads):
+        lib().oracle_accumulate_local(dtype, n, _ptr(x), _ptr(acc), 1 if j == 0 else 0)
+    return acc
+
+
+def reduce_f32(replicas, inv: float, sumsq: float = 0.0, overflow: int = 0):
+    """`reduce` over fp32 replica slices; return (g, sumsq, overflow)."""
+    reps = [np.ascontiguousarray(r, dtype=np.float32) for r in replicas]
+    n = reps[0].size
+    assert all(r.size == n for r in reps)
+    arr = (ctypes.c_void_p * len(reps))(*[_ptr(r) for r in reps])
+    g = np.empty(n, dtype=np.float32)
+    ss = ctypes.c_double(sumsq)
+    of = ctypes.c_int32(overflow)
+    lib().oracle_reduce_f32(len(reps), ctypes.addressof(arr), n, np.float32(inv), _ptr(g),
+                            ctypes.addressof(ss), ctypes.addressof(of))
+    return g, ss.value, of.value
 
 
 def clip(sumsq: float, max_norm: float):
@@ -363,6 +394,46 @@ def step_accumulated(micro_batches, dtype: int, numel: int, world_size: int,
                                            overflow if last else 0)
             if last:
                 sumsq, overflow = ss, of
+        grads.append(g)
+    overflow = overflow or not math.isfinite(sumsq)
+    applies, norm, coef = clip(sumsq, hp.max_grad_norm)
+    info = StepInfo(sumsq, norm, coef, applies, bool(overflow),
+                    bool(overflow), grads if keep_grads else [])
+    if overflow:
+        return info
+    for r in range(world_size):
+        lo, n = r * s, valid[r]
+        p, m, v = masters[r][:n], exp_avgs[r][:n], exp_avg_sqs[r][:n]
+        adamw(grads[r], p, m, v, coef, hp.lr, hp.beta1, hp.beta2, hp.eps,
+              hp.weight_decay, t)
+        if cast:
+            full_params[lo:lo + n] = to_low_precision(p, dtype)
+    return info
+
+
+def step_local_accumulated(micro_batches, dtype: int, numel: int, world_size: int,
+                           alignment: int, masters, exp_avgs, exp_avg_sqs, full_params,
+                           hp: Hyper, t: int, keep_grads: bool = False,
+                           cast: bool = True) -> StepInfo:
+    """One sharded step over an accumulation window of K micro-batches, with
+    the window summed before the reduce (the no_sync pattern).
+
+    micro_batches: K lists of N replica flats (as `step_accumulated` takes).
+    Each replica first sums its K micro-batch gradients into an fp32 flat
+    buffer of its own; each rank then reduces its slice of the N fp32
+    buffers, and the norm, the overflow flag, clipping, AdamW and the cast
+    follow as in `step`.
+    """
+    s, padded, valid = partition(numel, world_size, alignment)
+    inv = inv_scale(hp.loss_scale, hp.predivide)
+    n_rep = len(micro_batches[0])
+    local = [accumulate_local([flats[i][:numel] for flats in micro_batches], dtype)
+             for i in range(n_rep)]
+    sumsq, overflow = 0.0, 0
+    grads = []
+    for r in range(world_size):
+        lo, n = r * s, valid[r]
+        g, sumsq, overflow = reduce_f32([a[lo:lo + n] for a in local], inv, sumsq, overflow)
         grads.append(g)
     overflow = overflow or not math.isfinite(sumsq)
     applies, norm, coef = clip(sumsq, hp.max_grad_norm)

@@ -248,6 +248,42 @@ void oracle_reduce_accumulate(int32_t n_replicas, const uint16_t* const* replica
 }
 
 /* ------------------------------------------------------------------------ */
+/* Accumulation before the reduce ([P1] §1.2.2 no_sync pattern, §3.1
+ * gradient_accumulation_steps): a replica's micro-batch gradients are
+ * widened and summed into its own fp32 buffer in micro-batch order; the
+ * first micro-batch of a window sets the buffer.                         */
+void oracle_accumulate_local(int32_t dtype, int64_t n, const uint16_t* grad, float* acc,
+                             int32_t first)
+{
+    const float* value = (dtype == ORACLE_FP16) ? f16_value : bf16_value;
+    for (int64_t i = 0; i < n; ++i) {
+        float x = value[grad[i]];
+        acc[i] = first ? x : acc[i] + x;
+    }
+}
+
+/* The replica reduce of oracle_reduce, on fp32 replica buffers.           */
+void oracle_reduce_f32(int32_t n_replicas, const float* const* replicas, int64_t n,
+                       float inv_scale, float* g, double* sumsq, int32_t* overflow)
+{
+    double ss = *sumsq;
+    int32_t bad = *overflow;
+    for (int64_t i = 0; i < n; ++i) {
+        float acc = 0.0f;
+        for (int32_t r = 0; r < n_replicas; ++r) {
+            float x = replicas[r][i];
+            acc = (r == 0) ? x : acc + x;
+        }
+        float gi = acc * inv_scale;
+        g[i] = gi;
+        if (!isfinite(gi)) bad = 1;
+        ss += (double)gi * (double)gi;
+    }
+    *sumsq = ss;
+    *overflow = bad;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Global-norm clipping.  [P1] §6 configuration: gradient_clipping 1.0.
  * The factor max_norm / (norm + 1e-6) applies only when it is below one.  */
 int32_t oracle_clip(double sumsq, double max_norm, double* norm, double* coef)

@@ -29,6 +29,10 @@
  *   oracle_reduce_accumulate                  pinned (numpy fp32 sum over
  *                                             micro-batches, one micro-batch,
  *                                             sign of zero)
+ *   oracle_accumulate_local, oracle_reduce_f32
+ *                                             pinned (numpy fp32 sums, closed
+ *                                             form, a hand-rounded example
+ *                                             that separates the two orders)
  *   oracle_clip                               pinned (library clip, closed form)
  *   oracle_adamw                              pinned (closed form, library AdamW)
  *   oracle_scaler_*                           parity unpinned by the pages:
@@ -101,6 +105,22 @@ void oracle_reduce(int32_t n_replicas, const uint16_t* const* replicas,
 void oracle_reduce_accumulate(int32_t n_replicas, const uint16_t* const* replicas,
                               int32_t dtype, int64_t n, float inv_scale, float* g,
                               double* sumsq, int32_t* overflow);
+
+/* ---- gradient accumulation before the reduce ----------------------------- *
+ * The other reading of gradient_accumulation_steps ([P1] §3.1, §5.1), the
+ * pattern of [P1] §1.2.2's no_sync snippet: each replica keeps the
+ * gradients of its micro-batches locally, summed in an fp32 buffer of its
+ * own, and the gradients are synchronised once per window.  For i in [0, n):
+ *   acc[i] = first ? x : acc[i] + x     (fp32), x = grad[i] widened to fp32
+ * The reduce then sums the replicas' fp32 buffers with oracle_reduce_f32. */
+void oracle_accumulate_local(int32_t dtype, int64_t n, const uint16_t* grad, float* acc,
+                             int32_t first);
+
+/* oracle_reduce over fp32 replica buffers (those oracle_accumulate_local
+ * fills): the same running sum in replica order, unscale, flag and fp64 sum
+ * of squares. */
+void oracle_reduce_f32(int32_t n_replicas, const float* const* replicas, int64_t n,
+                       float inv_scale, float* g, double* sumsq, int32_t* overflow);
 
 /* ---- gradient clipping ([P1] §6 configuration: gradient_clipping 1.0) --- *
  * norm = sqrt(sumsq); coef = max_norm / (norm + 1e-6); the gradient is

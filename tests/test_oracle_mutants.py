@@ -34,6 +34,11 @@ MUTANTS = {
     "unscale_dropped": ("float gi = acc * inv_scale;\n        g[i] = gi;", "float gi = acc;\n        g[i] = gi;"),
     "accumulate_overwrites": ("float gi = g[i] + acc * inv_scale;", "float gi = acc * inv_scale;"),
     "accumulate_unscale_dropped": ("float gi = g[i] + acc * inv_scale;", "float gi = g[i] + acc;"),
+    "local_accumulate_overwrites": ("acc[i] = first ? x : acc[i] + x;", "acc[i] = x;"),
+    "local_accumulate_starts_at_zero": ("acc[i] = first ? x : acc[i] + x;",
+                                        "acc[i] = (first ? 0.0f : acc[i]) + x;"),
+    "reduce_f32_drops_first_replica": ("for (int32_t r = 0; r < n_replicas; ++r) {\n            float x = replicas[r][i];",
+                                       "for (int32_t r = 1; r < n_replicas; ++r) {\n            float x = replicas[r][i];"),
     "nan_not_flagged": ("if (!isfinite(gi)) bad = 1;", "if (isinf(gi)) bad = 1;"),
     "clip_eps_dropped": ("max_norm / (*norm + 1e-6)", "max_norm / (*norm)"),
     "partition_floor_not_ceil": ("(numel % world_size != 0 ? 1 : 0)", "0"),

@@ -423,3 +423,113 @@ def test_accumulated_step_equals_one_step_over_all_gradients_when_sums_are_exact
         for x, y in zip(xs, ys):
             assert np.array_equal(x, y)
     assert np.array_equal(a[4], b[4])
+
+
+# ------------------------------------ accumulation before the reduce (no_sync)
+@pytest.mark.parametrize("dtype", [oracle.FP16, oracle.BF16])
+def test_local_accumulation_matches_numpy_fp32_running_sum(dtype):
+    # A replica's window, widened and added in micro-batch order by numpy.
+    rng = np.random.default_rng(31)
+    K, n = 5, 3001
+    micro = [rand_codes(rng, n, dtype, sigma=10.0 ** rng.uniform(-3, 2)) for _ in range(K)]
+    acc = oracle.accumulate_local(micro, dtype)
+    ref = decode(micro[0], dtype).copy()
+    for x in micro[1:]:
+        ref = np.add(ref, decode(x, dtype), dtype=np.float32)
+    assert np.array_equal(acc, ref)
+
+
+def test_reduce_f32_matches_numpy_running_sum():
+    rng = np.random.default_rng(32)
+    N, n = 6, 2999
+    reps = [(rng.standard_normal(n) * 10.0 ** rng.uniform(-3, 3)).astype(np.float32)
+            for _ in range(N)]
+    inv = oracle.inv_scale(8.0)
+    g, ss, of = oracle.reduce_f32(reps, inv)
+    acc = reps[0].copy()
+    for r in reps[1:]:
+        acc = np.add(acc, r, dtype=np.float32)
+    ref = np.multiply(acc, inv, dtype=np.float32)
+    assert np.array_equal(g, ref) and of == 0
+    assert ss == np.cumsum(ref.astype(np.float64) ** 2)[-1]     # sequential, index order
+    bad = [r.copy() for r in reps]
+    bad[3][17] = np.nan
+    assert oracle.reduce_f32(bad, inv)[2] == 1
+
+
+def test_local_accumulation_exact_closed_form():
+    # Dyadic values whose sums are exact: N replicas, each summing K equal
+    # micro-batches, give exactly N * K * x, unscaled.
+    x = np.array([0.5, -0.25, 3.0, 1.0 / 64, -7.0, 0.0], np.float32)
+    codes = oracle.f32_to_f16(x)
+    N, K = 3, 4
+    local = [oracle.accumulate_local([codes] * K, oracle.FP16) for _ in range(N)]
+    g, _, _ = oracle.reduce_f32(local, oracle.inv_scale(2.0))
+    assert np.array_equal(g, x * np.float32(N * K / 2.0))
+
+
+def test_local_accumulation_order_differs_from_reduce_per_micro_batch():
+    # Worked by hand, bf16 inputs, scale 1, one element, 2 replicas, 2
+    # micro-batches: replica 0 sees 1 then 2^-24, replica 1 sees 0 then 2^-24.
+    # Summed locally first: replica 0 holds 1 + 2^-24, a tie between 1 and
+    # 1 + 2^-23 that rounds to the even 1; replica 1 holds 2^-24; their sum
+    # 1 + 2^-24 rounds to 1 again.  Reduced per micro-batch: 1 + 0 = 1, then
+    # 2^-24 + 2^-24 = 2^-23, and 1 + 2^-23 is exact.
+    one, tiny, zero = 0x3F80, 0x3380, 0x0000          # bf16 codes of 1, 2^-24, 0
+    assert oracle.bf16_to_f32(np.array([tiny], np.uint16))[0] == 2.0 ** -24
+    micro = [[np.array([one], np.uint16), np.array([zero], np.uint16)],
+             [np.array([tiny], np.uint16), np.array([tiny], np.uint16)]]
+
+    def run(fn):
+        z = [np.zeros(1, np.float32)]
+        info = fn(micro, oracle.BF16, 1, 1, 1, [np.zeros(1, np.float32)], z,
+                  [np.zeros(1, np.float32)], np.zeros(1, np.uint16), oracle.Hyper(), 1,
+                  keep_grads=True)
+        return info.grads[0][0]
+
+    assert run(oracle.step_local_accumulated) == np.float32(1.0)
+    assert run(oracle.step_accumulated) == np.float32(1.0 + 2.0 ** -23)
+
+
+def test_local_accumulation_sign_of_zero_and_skip():
+    neg0 = oracle.f32_to_bf16(np.array([-0.0, 1.0], np.float32))
+    acc = oracle.accumulate_local([neg0, neg0], oracle.BF16)
+    assert np.signbit(acc[0])                   # -0 + -0 = -0; the first sets, not adds
+    g, _, _ = oracle.reduce_f32([acc], oracle.inv_scale(1.0))
+    assert np.signbit(g[0]) and g[1] == 2.0
+    # a NaN in one micro-batch of one replica skips the whole window
+    P, N, A, K = 1001, 2, 8, 3
+    s, padded, valid = oracle.partition(P, N, A)
+    rng = np.random.default_rng(33)
+    micro = [[rand_codes(rng, padded, oracle.BF16, 1e-2) for _ in range(N)] for _ in range(K)]
+    micro[1][1][700] = 0x7FC0                   # bf16 NaN
+    ps = split((rng.standard_normal(padded) * 0.02).astype(np.float32), N, s)
+    before = [p.copy() for p in ps]
+    info = oracle.step_local_accumulated(micro, oracle.BF16, P, N, A, ps,
+                                         split(np.zeros(padded, np.float32), N, s),
+                                         split(np.zeros(padded, np.float32), N, s),
+                                         np.zeros(padded, np.uint16), oracle.Hyper(), 1)
+    assert info.overflow and info.skipped
+    assert all(np.array_equal(a, b) for a, b in zip(before, ps))
+
+
+def test_local_accumulation_of_one_micro_batch_is_the_plain_step():
+    # Widening is exact, so a window of one micro-batch reduces the same
+    # fp32 values in the same order as the plain step.
+    rng = np.random.default_rng(34)
+    P, N, A = 4099, 4, 128
+    s, padded, valid = oracle.partition(P, N, A)
+    flats = [rand_codes(rng, padded, oracle.FP16, 1e-3 * 2**12) for _ in range(N)]
+    master = (rng.standard_normal(padded) * 0.02).astype(np.float32)
+    hp = oracle.Hyper(loss_scale=2.0**12)
+    out = []
+    for fn, arg in ((oracle.step_local_accumulated, [flats]), (oracle.step, flats)):
+        ps, ms, vs = (split(a, N, s) for a in (master, np.zeros(padded, np.float32),
+                                                np.zeros(padded, np.float32)))
+        full = np.zeros(padded, np.uint16)
+        info = fn(arg, oracle.FP16, P, N, A, ps, ms, vs, full, hp, 1)
+        out.append((info.sumsq, ps, ms, vs, full))
+    assert out[0][0] == out[1][0]
+    for xs, ys in zip(out[0][1:4], out[1][1:4]):
+        assert all(np.array_equal(x, y) for x, y in zip(xs, ys))
+    assert np.array_equal(out[0][4], out[1][4])
