@@ -55,6 +55,10 @@ extern "C" {
  * enables either fp16 or bf16 mixed precision, never both. */
 #define ZERO_FP16 1
 #define ZERO_BF16 2
+/* fp32 replica gradients: the buffers zero_accumulate_local fills when a
+ * window of micro-batches is summed on each replica before the reduce.
+ * Valid as zero_step_args.grad_dtype only. */
+#define ZERO_FP32 3
 
 /* Largest number of data-parallel replicas one reduce can sum. */
 #define ZERO_MAX_REPLICAS 64
@@ -159,7 +163,8 @@ typedef struct {
     int32_t rank;             /* this rank, in [0, world_size)             */
     int64_t shard_numel;      /* from zero_partition                       */
     int64_t valid_numel;      /* real elements of this rank's shard        */
-    int32_t grad_dtype;       /* ZERO_FP16 or ZERO_BF16                    */
+    int32_t grad_dtype;       /* ZERO_FP16, ZERO_BF16, or ZERO_FP32 for
+                                 replicas summed by zero_accumulate_local */
     int32_t param_dtype;      /* ZERO_FP16 or ZERO_BF16                    */
     int32_t n_replicas;       /* gradients summed, 1..ZERO_MAX_REPLICAS    */
     /* 0: pass 1 sets the workspace's fp32 gradient slice to this reduce's
@@ -253,6 +258,23 @@ int zero_shard_reduce(const zero_step_args* a, int32_t slot,
  * flag, clipping and AdamW act on the accumulated slice.  The loss scale
  * must stay the same within a window.  Errors: as zero_shard_step. */
 int zero_shard_accumulate(const zero_step_args* a, void* stream);
+
+/* Gradient accumulation before the reduce: the other reading of
+ * gradient_accumulation_steps ([P1] §3.1, §5.1), the pattern of [P1]
+ * §1.2.2's no_sync snippet, where each replica keeps its micro-batch
+ * gradients locally and the replicas are synchronised once per window.
+ * Each replica sums its window into an fp32 buffer of its own:
+ *   acc[i] = first ? x : acc[i] + x,   x = grad[i] widened to fp32 (exact)
+ * for i in [0, n), in micro-batch order.  The step then reduces the
+ * replicas' fp32 buffers: zero_step_args.grad_dtype = ZERO_FP32 with
+ * replica_grad pointing at this rank's slice of each replica's acc.  The
+ * loss scale must stay the same within a window; it is undone once, in the
+ * reduce.  grad: device, n values of grad_dtype (ZERO_FP16 or ZERO_BF16);
+ * acc: device fp32[n]; both 16-byte aligned and not overlapping; first is 0
+ * or 1.  Asynchronous on `stream`.  Errors: n < 0, a NULL pointer when
+ * n > 0, a bad dtype or first -> ZERO_EINVAL; misalignment -> ZERO_EALIGN. */
+int zero_accumulate_local(const void* grad, int32_t grad_dtype, float* acc, int64_t n,
+                          int32_t first, void* stream);
 
 /* Combine slots [0, n_slots) of partials_dev in a fixed order into one
  * zero_global_t at global_dev (device): the global sum of squares and norm,

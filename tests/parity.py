@@ -108,6 +108,9 @@ class Spec:
     poison: Optional[List[Optional[W.Poison]]] = None
     micro_batches: int = 1                 # gradient-accumulation window
     poison_micro: int = 0                  # micro-batch the poison lands in
+    # sum each replica's window in fp32 before one reduce (no_sync pattern)
+    # instead of reducing every micro-batch into the rank's slice
+    local_accumulation: bool = False
     name: str = "case"
     seed: int = 0
 
@@ -128,8 +131,13 @@ def run(spec: Spec, device="cuda", check_every_step: bool = True,
     """Run spec.steps steps on both sides and compare them."""
     nrep = spec.n_replicas or spec.world_size
     pdt = spec.param_dtype or spec.grad_dtype
-    world = SimulatedWorld(spec.numel, spec.world_size, nrep, spec.alignment, spec.grad_dtype,
-                           pdt, device)
+    local = spec.local_accumulation
+    world = SimulatedWorld(spec.numel, spec.world_size, nrep, spec.alignment,
+                           torch.float32 if local else spec.grad_dtype, pdt, device)
+    # local accumulation: the micro-batch gradients live in their own 16-bit
+    # buffers and world.grads are the replicas' fp32 window sums
+    mbuf = [torch.zeros_like(g, dtype=spec.grad_dtype) for g in world.grads] if local else \
+        world.grads
     s, P = world.s, spec.numel
     odt = oracle_dtype(spec.grad_dtype)
     podt = oracle_dtype(pdt)
@@ -164,22 +172,32 @@ def run(spec: Spec, device="cuda", check_every_step: bool = True,
             for i in range(nrep):
                 key = ("grad", spec.name, spec.seed, step, i) if K == 1 else \
                     ("grad", spec.name, spec.seed, step, i, j)
-                W.flat_normal(world.grads[i], world.lo, P, spec.grad_sigma, key, scale=scale)
+                W.flat_normal(mbuf[i], world.lo, P, spec.grad_sigma, key, scale=scale)
             if spec.poison and spec.poison[step] is not None and spec.poison_micro == j:
-                W.plant(world.grads[spec.poison[step].replica], spec.poison[step])
-            micro.append([u16(gbuf) for gbuf in world.grads])     # generator output
-            if j < K - 1:
+                W.plant(mbuf[spec.poison[step].replica], spec.poison[step])
+            micro.append([u16(gbuf) for gbuf in mbuf])     # generator output
+            if local:
+                world.accumulate_local(mbuf, first=j == 0)
+                if j == K - 1:
+                    world.step(hp, t_lib)
+            elif j < K - 1:
                 world.accumulate(hp, first=j == 0)
             else:
                 world.step(hp, t_lib, accumulate=K > 1)
+        if local:
+            # the device's fp32 window sums against the oracle's, bit for bit
+            for i in range(nrep):
+                ref = oracle.accumulate_local([mb[i][:P - world.lo] for mb in micro], odt)
+                assert_bitwise("step %d replica %d window sum" % (step, i),
+                               f32(world.grads[i][:P - world.lo]), ref)
         res = world.result()
         last = step == spec.steps - 1
         compare = check_every_step or last
         # Every step overwrites all real elements of the full buffer, so the
         # oracle casts only on the steps whose result is compared.
-        info = oracle.step_accumulated(micro, odt, P, spec.world_size, spec.alignment, o_master,
-                                       o_m, o_v, o_full, o_hp, t_orc, keep_grads=compare,
-                                       cast=compare)
+        ostep = oracle.step_local_accumulated if local else oracle.step_accumulated
+        info = ostep(micro, odt, P, spec.world_size, spec.alignment, o_master,
+                     o_m, o_v, o_full, o_hp, t_orc, keep_grads=compare, cast=compare)
         if compare and info.overflow and t_orc > 1:
             # a skipped step leaves the last applied step's cast in place
             s_, _, valid_ = oracle.partition(P, spec.world_size, spec.alignment)

@@ -176,7 +176,7 @@ BAD = [
     (dict(loss_scale=0.0), Z.ZERO_EINVAL), (dict(grad_predivide=-1.0), Z.ZERO_EINVAL),
     (dict(beta1=1.0), Z.ZERO_EINVAL), (dict(beta2=-0.1), Z.ZERO_EINVAL),
     (dict(eps=0.0), Z.ZERO_EINVAL), (dict(lr=float("nan")), Z.ZERO_EINVAL),
-    (dict(max_grad_norm=float("nan")), Z.ZERO_EINVAL), (dict(grad_dtype=3), Z.ZERO_EINVAL),
+    (dict(max_grad_norm=float("nan")), Z.ZERO_EINVAL), (dict(grad_dtype=4), Z.ZERO_EINVAL),
     (dict(param_dtype=0), Z.ZERO_EINVAL), (dict(replica_grads=[]), Z.ZERO_EINVAL),
     (dict(replica_grads=[FakeTensor(0x10000 * (i + 1)) for i in range(Z.ZERO_MAX_REPLICAS + 1)]),
      Z.ZERO_EINVAL),
@@ -267,3 +267,34 @@ def test_output_state_pointers_are_checked():
     assert Z.lib().zero_offload_apply(ctypes.byref(c), 0x1000, ctypes.byref(st), None,
                                       None) == Z.ZERO_EINVAL
     assert "in place" in Z.zero_last_error()
+
+
+def test_accumulate_local_rejects_bad_arguments_before_any_work():
+    # Fake device addresses: every call must fail in the host checks.
+    L = Z.lib()
+    g, acc = 0x100000, 0x200000
+    cases = [
+        ((g, Z.ZERO_BF16, acc, -1, 1), Z.ZERO_EINVAL),          # n < 0
+        ((g, Z.ZERO_FP32, acc, 64, 1), Z.ZERO_EINVAL),          # fp32 is not a micro-batch format
+        ((g, 0, acc, 64, 1), Z.ZERO_EINVAL),
+        ((g, Z.ZERO_BF16, acc, 64, 2), Z.ZERO_EINVAL),          # first not 0 or 1
+        ((None, Z.ZERO_BF16, acc, 64, 1), Z.ZERO_EINVAL),
+        ((g, Z.ZERO_BF16, None, 64, 0), Z.ZERO_EINVAL),
+        ((g + 2, Z.ZERO_BF16, acc, 64, 1), Z.ZERO_EALIGN),
+        ((g, Z.ZERO_BF16, acc + 4, 64, 1), Z.ZERO_EALIGN),
+        ((acc + 64, Z.ZERO_FP16, acc, 64, 1), Z.ZERO_EINVAL),   # overlapping
+    ]
+    for args, code in cases:
+        assert L.zero_accumulate_local(*args, None) == code, args
+        assert Z.zero_last_error()
+    assert L.zero_accumulate_local(None, Z.ZERO_BF16, None, 0, 1, None) == Z.ZERO_OK   # empty
+
+
+def test_step_accepts_fp32_replicas_only_as_gradients():
+    import torch
+    a = good_args(replica_grads=[FakeTensor(0x10000 * (i + 1), dtype=torch.float32)
+                                 for i in range(4)], grad_dtype=None)
+    assert a.c_args().grad_dtype == Z.ZERO_FP32
+    bad = good_args(param_dtype=Z.ZERO_FP32)
+    with pytest.raises(Z.ZeroError):
+        Z.zero_shard_step(bad, stream=0)

@@ -358,6 +358,60 @@ def test_accumulation_poison_in_any_micro_batch_skips(micro):
     assert rep.skipped == 1
 
 
+LOCAL_CASES = [
+    # (numel, world, alignment, dtype, sigma, loss_scale, micro_batches, replicas)
+    (5, 4, 8, BF16, 1e-2, 1.0, 2, 4),              # empty ranks, tail only
+    (40_001, 3, 8, FP16, 1e-3, 2.0**12, 4, 3),
+    (100_003, 4, 128, BF16, 1e-3, 1.0, 3, 4),
+    (1_000_003, 8, 128, BF16, 3e-2, 1.0, 2, 8),
+    (77_777, 2, 128, FP16, 1e-3, 2.0**10, 3, 11),  # generic replica loop
+]
+
+
+@pytest.mark.parametrize("case", LOCAL_CASES,
+                         ids=["P%d-N%d-%s-K%d-R%d" % (c[0], c[1], str(c[3])[6:], c[6], c[7])
+                              for c in LOCAL_CASES])
+def test_local_accumulation_matches_oracle(case):
+    # Each replica sums its window in fp32 (zero_accumulate_local), then one
+    # reduce of the fp32 sums (grad_dtype ZERO_FP32); the window sums, the
+    # reduced slices, the state and the cast are compared with the oracle.
+    numel, world, align, dt, sigma, scale, K, R = case
+    say("local accumulation %s" % (case,))
+    spec = parity.Spec(numel=numel, world_size=world, n_replicas=R, alignment=align,
+                       grad_dtype=dt, grad_sigma=sigma, steps=2, micro_batches=K,
+                       local_accumulation=True, name="local-%d-%d-%d" % (numel, world, K),
+                       hp=Hyper(loss_scale=scale))
+    rep = parity.run(spec)
+    say("norm rel err %.2e, bitwise state %.6f" % (rep.norm_rel_err, rep.state_bitwise))
+
+
+@pytest.mark.parametrize("micro", [0, 2])
+def test_local_accumulation_poison_in_any_micro_batch_skips(micro):
+    say("local accumulation, poison in micro-batch %d" % micro)
+    sched = [None, W.Poison(1, 1, 777, 1), None]
+    spec = parity.Spec(numel=20_011, world_size=4, alignment=8, grad_dtype=FP16,
+                       grad_sigma=1e-3, steps=3, poison=sched, poison_micro=micro,
+                       micro_batches=3, local_accumulation=True, dynamic_scale=True,
+                       scaler_args=(10, 2, 1, 1.0), name="local-poison")
+    rep = parity.run(spec)
+    assert rep.skipped == 1
+
+
+def test_accumulate_local_edges():
+    # Ragged lengths end in a scalar tail; nothing past n is written.
+    say("zero_accumulate_local edges")
+    import oracle
+    for n in (1, 3, 4, 5, 1023, 4099):
+        g1 = torch.randn(n + 8, device="cuda").to(BF16)
+        g2 = torch.randn(n + 8, device="cuda").to(BF16)
+        acc = torch.full((n + 8,), 5.0, device="cuda")
+        Z.zero_accumulate_local(g1, acc, True, n=n)
+        Z.zero_accumulate_local(g2, acc, False, n=n)
+        ref = oracle.accumulate_local([parity.u16(g1[:n]), parity.u16(g2[:n])], oracle.BF16)
+        parity.assert_bitwise("n=%d" % n, parity.f32(acc[:n]), ref)
+        assert bool((acc[n:] == 5.0).all()), "wrote past n"
+
+
 def test_accumulate_then_fused_step_equals_split_calls():
     say("zero_shard_accumulate + zero_shard_step vs the split world")
     numel, K = 123_457, 3

@@ -14,17 +14,19 @@ from typing import Optional, Sequence
 
 from . import _abi
 from ._abi import (ZERO_BF16, ZERO_CKPT_MAGIC, ZERO_CKPT_VERSION, ZERO_EALIGN, ZERO_EDEVICE,
-                   ZERO_EINVAL, ZERO_ESIZE, ZERO_FP16, ZERO_MAX_REPLICAS, ZERO_OK, ZeroError,
+                   ZERO_EINVAL, ZERO_ESIZE, ZERO_FP16, ZERO_FP32, ZERO_MAX_REPLICAS, ZERO_OK,
+                   ZeroError,
                    check, lib, zero_bucket_t, zero_ckpt_header_t, zero_global_t,
                    zero_loss_scaler_t, zero_offload_staging_t, zero_partition_t,
                    zero_step_args, zero_step_info, zero_tensor_slot_t)
 
 __all__ = [
     "ZERO_OK", "ZERO_EINVAL", "ZERO_EALIGN", "ZERO_ESIZE", "ZERO_EDEVICE",
-    "ZERO_FP16", "ZERO_BF16", "ZERO_MAX_REPLICAS", "ZeroError", "lib",
+    "ZERO_FP16", "ZERO_BF16", "ZERO_FP32", "ZERO_MAX_REPLICAS", "ZeroError", "lib",
     "zero_last_error", "zero_partition", "zero_partition_valid_numel",
     "zero_bucket_plan", "zero_bucket_flatten", "zero_shard_workspace_bytes",
-    "zero_partials_bytes", "zero_shard_reduce", "zero_shard_accumulate", "zero_shard_combine",
+    "zero_partials_bytes", "zero_shard_reduce", "zero_shard_accumulate",
+    "zero_accumulate_local", "zero_shard_combine",
     "zero_shard_apply", "zero_shard_step", "zero_loss_scaler_init",
     "zero_loss_scaler_update", "zero_ckpt_header_make", "zero_ckpt_header_check",
     "zero_repartition", "zero_gather_params", "zero_offload_apply", "zero_host_adamw", "zero_host_threads",
@@ -41,7 +43,8 @@ def _torch():
 
 
 def dtype_code(dtype) -> int:
-    """ZERO_FP16 / ZERO_BF16 for a torch dtype (or pass an int through)."""
+    """ZERO_FP16 / ZERO_BF16 / ZERO_FP32 for a torch dtype (or pass an int
+    through).  ZERO_FP32 is accepted only as a replica gradient format."""
     if isinstance(dtype, int):
         return dtype
     torch = _torch()
@@ -49,7 +52,9 @@ def dtype_code(dtype) -> int:
         return ZERO_FP16
     if dtype == torch.bfloat16:
         return ZERO_BF16
-    raise ValueError("only float16 and bfloat16 are supported, got %s" % dtype)
+    if dtype == torch.float32:
+        return ZERO_FP32
+    raise ValueError("only float16, bfloat16 and float32 are supported, got %s" % dtype)
 
 
 def _stream(stream) -> Optional[int]:
@@ -226,6 +231,17 @@ def zero_shard_accumulate(args, stream=None) -> None:
     of an accumulation window; args.accumulate selects set or add)."""
     check(lib().zero_shard_accumulate(ctypes.byref(_args(args)), _stream(stream)),
           "zero_shard_accumulate")
+
+
+def zero_accumulate_local(grad, acc, first: bool, n: Optional[int] = None,
+                          stream=None) -> None:
+    """Gradient accumulation before the reduce: acc[:n] (fp32) is set to
+    (first) or incremented by grad[:n] widened to fp32.  n defaults to
+    grad.numel()."""
+    n = grad.numel() if n is None else n
+    check(lib().zero_accumulate_local(_dptr(grad), dtype_code(grad.dtype), _dptr(acc), n,
+                                      1 if first else 0, _stream(stream)),
+          "zero_accumulate_local")
 
 
 def zero_shard_combine(partials, n_slots: int, max_grad_norm: float, global_buf,

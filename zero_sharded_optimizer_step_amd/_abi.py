@@ -19,6 +19,7 @@ ZERO_ESIZE = -3
 ZERO_EDEVICE = -4
 ZERO_FP16 = 1
 ZERO_BF16 = 2
+ZERO_FP32 = 3
 ZERO_MAX_REPLICAS = 64
 
 i32, i64, f32, f64, vp, sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
@@ -120,6 +121,7 @@ _PROTOTYPES = {
     "zero_host_adamw": (ctypes.c_int, [i64, vp, f32, vp, vp, vp, vp, i32, f64, f64, f64, f64,
                                        f64, i64, i32]),
     "zero_host_threads": (i32, []),
+    "zero_accumulate_local": (ctypes.c_int, [vp, i32, vp, i64, i32, vp]),
 }
 
 _lib = None

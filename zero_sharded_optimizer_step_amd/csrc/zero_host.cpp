@@ -49,8 +49,9 @@ int validate_step_args(const zero_step_args* a) {
     if (a->valid_numel < 0 || a->valid_numel > a->shard_numel)
         return fail(ZERO_EINVAL, "valid_numel %lld outside [0, shard_numel=%lld]",
                     (long long)a->valid_numel, (long long)a->shard_numel);
-    if (a->grad_dtype != ZERO_FP16 && a->grad_dtype != ZERO_BF16)
-        return fail(ZERO_EINVAL, "grad_dtype %d is not ZERO_FP16 or ZERO_BF16", a->grad_dtype);
+    if (a->grad_dtype != ZERO_FP16 && a->grad_dtype != ZERO_BF16 && a->grad_dtype != ZERO_FP32)
+        return fail(ZERO_EINVAL, "grad_dtype %d is not ZERO_FP16, ZERO_BF16 or ZERO_FP32",
+                    a->grad_dtype);
     if (a->param_dtype != ZERO_FP16 && a->param_dtype != ZERO_BF16)
         return fail(ZERO_EINVAL, "param_dtype %d is not ZERO_FP16 or ZERO_BF16", a->param_dtype);
     if (a->n_replicas < 1 || a->n_replicas > ZERO_MAX_REPLICAS)

@@ -31,8 +31,9 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
+// Replica slices: 16-bit codes (ZERO_FP16, ZERO_BF16) or fp32 (ZERO_FP32).
 struct ReplicaPtrs {
-    const u32x2* p[ZERO_MAX_REPLICAS];
+    const void* p[ZERO_MAX_REPLICAS];
 };
 
 // Logical block of dispatch-order block b (which the hardware sends to XCD
@@ -78,6 +79,29 @@ __device__ __forceinline__ unsigned short pack1(float a) {
 
 __device__ __forceinline__ bool finite(float x) { return __builtin_isfinite(x); }
 
+// One quad of a replica slice: 8 bytes of 16-bit codes, or 16 bytes of fp32.
+template <int DT> struct QuadOf { typedef u32x2 T; };
+template <> struct QuadOf<ZERO_FP32> { typedef f32x4 T; };
+
+template <int DT>
+__device__ __forceinline__ typename QuadOf<DT>::T load_quad(const void* base, int64_t q) {
+    return __builtin_nontemporal_load(static_cast<const typename QuadOf<DT>::T*>(base) + q);
+}
+template <int DT>
+__device__ __forceinline__ void widen4(const typename QuadOf<DT>::T v, float o[4]) {
+    if constexpr (DT == ZERO_FP32) {
+        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    } else {
+        decode4<DT>(v, o);
+    }
+}
+// Element i of a replica slice, widened to fp32 (exact).
+template <int DT>
+__device__ __forceinline__ float elem(const void* base, int64_t i) {
+    if constexpr (DT == ZERO_FP32) return static_cast<const float*>(base)[i];
+    else return lo_to_f32<DT>(static_cast<const unsigned short*>(base)[i]);
+}
+
 // ------------------------------------------------------- block reduction
 // Fixed shuffle pattern and fixed wave order: the block's result depends
 // only on which values its threads hold, never on timing.  Thread 0 ends
@@ -113,22 +137,22 @@ __device__ __forceinline__ void block_reduce(double& ss, int& bad) {
 template <int DT, int NR>
 __device__ __forceinline__ void sum_quad(const ReplicaPtrs& reps, int nrep, int64_t q, float acc[4]) {
     if constexpr (NR > 0) {
-        u32x2 x[NR];
+        typename QuadOf<DT>::T x[NR];
         #pragma unroll
-        for (int r = 0; r < NR; ++r) x[r] = __builtin_nontemporal_load(reps.p[r] + q);
-        decode4<DT>(x[0], acc);
+        for (int r = 0; r < NR; ++r) x[r] = load_quad<DT>(reps.p[r], q);
+        widen4<DT>(x[0], acc);
         #pragma unroll
         for (int r = 1; r < NR; ++r) {
             float y[4];
-            decode4<DT>(x[r], y);
+            widen4<DT>(x[r], y);
             #pragma unroll
             for (int k = 0; k < 4; ++k) acc[k] = acc[k] + y[k];
         }
     } else {
-        decode4<DT>(__builtin_nontemporal_load(reps.p[0] + q), acc);
+        widen4<DT>(load_quad<DT>(reps.p[0], q), acc);
         for (int r = 1; r < nrep; ++r) {
             float y[4];
-            decode4<DT>(__builtin_nontemporal_load(reps.p[r] + q), y);
+            widen4<DT>(load_quad<DT>(reps.p[r], q), y);
             #pragma unroll
             for (int k = 0; k < 4; ++k) acc[k] = acc[k] + y[k];
         }
@@ -167,8 +191,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(
         for (int64_t i = q * kQuad; i < n_valid; ++i) {
             float acc = 0.0f;
             for (int r = 0; r < nrep; ++r) {
-                const unsigned short* base = reinterpret_cast<const unsigned short*>(reps.p[r]);
-                const float x = lo_to_f32<DT>(base[i]);
+                const float x = elem<DT>(reps.p[r], i);
                 acc = (r == 0) ? x : acc + x;
             }
             float gi = acc * inv_scale;
@@ -183,6 +206,38 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(
         partials[blk].sumsq = ss;
         partials[blk].flag = bad;
         partials[blk].pad = 0;
+    }
+}
+
+// ============================================ accumulation before the reduce
+// [P1] §1.2.2 (no_sync) and §3.1 (gradient_accumulation_steps): a replica
+// sums its micro-batch gradients into an fp32 buffer of its own before the
+// replicas are reduced once.  acc = grad widened (FIRST) or acc + grad
+// widened; each stream is touched once, so loads and stores are
+// nontemporal.
+template <int DT, bool FIRST>
+__global__ __launch_bounds__(kReduceThreads) void accumulate_local_kernel(
+    const u32x2* __restrict__ grad, float* __restrict__ acc, int64_t n, uint32_t group) {
+    const int64_t q = xcd_block(blockIdx.x, group) * kReduceThreads + threadIdx.x;
+    const int64_t full = n / kQuad;
+    if (q < full) {
+        float x[4];
+        decode4<DT>(__builtin_nontemporal_load(grad + q), x);
+        f32x4 o;
+        if constexpr (FIRST) {
+            o = f32x4{x[0], x[1], x[2], x[3]};
+        } else {
+            const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(acc) + q);
+            #pragma unroll
+            for (int k = 0; k < 4; ++k) o[k] = a[k] + x[k];
+        }
+        __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(acc) + q);
+    } else if (q == full) {
+        const unsigned short* g16 = reinterpret_cast<const unsigned short*>(grad);
+        for (int64_t i = q * kQuad; i < n; ++i) {
+            const float x = lo_to_f32<DT>(g16[i]);
+            acc[i] = FIRST ? x : acc[i] + x;
+        }
     }
 }
 
@@ -441,19 +496,24 @@ void launch_reduce_dt(const ReplicaPtrs& reps, int nrep, int64_t n_valid, float 
 int launch_pass1(const zero_step_args* a, hipStream_t st) {
     ReplicaPtrs reps;
     for (int r = 0; r < ZERO_MAX_REPLICAS; ++r)
-        reps.p[r] = r < a->n_replicas ? static_cast<const u32x2*>(a->replica_grad[r]) : nullptr;
+        reps.p[r] = r < a->n_replicas ? a->replica_grad[r] : nullptr;
     const float inv = static_cast<float>(1.0 / (a->loss_scale * a->grad_predivide));
     unsigned char* ws = static_cast<unsigned char*>(a->workspace);
     float* g = reinterpret_cast<float*>(ws);
     Partial* parts = reinterpret_cast<Partial*>(ws + ws_blocks_offset(a->shard_numel));
-    const bool bf = a->grad_dtype == ZERO_BF16;
-    if (a->accumulate) {
-        if (bf) launch_reduce_dt<ZERO_BF16, true>(reps, a->n_replicas, a->valid_numel, inv, g, parts, st);
-        else launch_reduce_dt<ZERO_FP16, true>(reps, a->n_replicas, a->valid_numel, inv, g, parts, st);
-    } else {
-        if (bf) launch_reduce_dt<ZERO_BF16, false>(reps, a->n_replicas, a->valid_numel, inv, g, parts, st);
-        else launch_reduce_dt<ZERO_FP16, false>(reps, a->n_replicas, a->valid_numel, inv, g, parts, st);
+#define ZERO_PASS1(DT)                                                                          \
+    do {                                                                                        \
+        if (a->accumulate)                                                                      \
+            launch_reduce_dt<DT, true>(reps, a->n_replicas, a->valid_numel, inv, g, parts, st);  \
+        else                                                                                    \
+            launch_reduce_dt<DT, false>(reps, a->n_replicas, a->valid_numel, inv, g, parts, st); \
+    } while (0)
+    switch (a->grad_dtype) {
+        case ZERO_BF16: ZERO_PASS1(ZERO_BF16); break;
+        case ZERO_FP16: ZERO_PASS1(ZERO_FP16); break;
+        default: ZERO_PASS1(ZERO_FP32); break;
     }
+#undef ZERO_PASS1
     return launch_error("reduce kernel launch");
 }
 
@@ -592,6 +652,36 @@ int zero_shard_accumulate(const zero_step_args* a, void* stream) {
     int rc = validate_step_args(a);
     if (rc) return rc;
     return launch_pass1(a, static_cast<hipStream_t>(stream));
+}
+
+int zero_accumulate_local(const void* grad, int32_t grad_dtype, float* acc, int64_t n,
+                          int32_t first, void* stream) {
+    clear_error();
+    if (n < 0) return fail(ZERO_EINVAL, "n %lld < 0", (long long)n);
+    if (grad_dtype != ZERO_FP16 && grad_dtype != ZERO_BF16)
+        return fail(ZERO_EINVAL, "grad_dtype %d is not ZERO_FP16 or ZERO_BF16", grad_dtype);
+    if (first != 0 && first != 1) return fail(ZERO_EINVAL, "first %d is not 0 or 1", first);
+    if (n == 0) return ZERO_OK;
+    if (!grad || !acc) return fail(ZERO_EINVAL, "grad or acc is NULL");
+    if (!aligned16(grad) || !aligned16(acc))
+        return fail(ZERO_EALIGN, "grad or acc is not 16-byte aligned");
+    const unsigned char* g0 = static_cast<const unsigned char*>(grad);
+    const unsigned char* a0 = reinterpret_cast<const unsigned char*>(acc);
+    if (g0 < a0 + 4 * n && a0 < g0 + 2 * n) return fail(ZERO_EINVAL, "grad and acc overlap");
+    const Grid gr = grid_for(n, kReduceThreads);
+    const dim3 grid(static_cast<unsigned>(gr.blocks));
+    const uint32_t group = static_cast<uint32_t>(gr.group);
+    const u32x2* g = static_cast<const u32x2*>(grad);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+#define ZERO_ACC_LOCAL(DT, FIRST) \
+    hipLaunchKernelGGL((accumulate_local_kernel<DT, FIRST>), grid, dim3(kReduceThreads), 0, st, g, acc, n, group)
+    if (grad_dtype == ZERO_BF16) {
+        if (first) ZERO_ACC_LOCAL(ZERO_BF16, true); else ZERO_ACC_LOCAL(ZERO_BF16, false);
+    } else {
+        if (first) ZERO_ACC_LOCAL(ZERO_FP16, true); else ZERO_ACC_LOCAL(ZERO_FP16, false);
+    }
+#undef ZERO_ACC_LOCAL
+    return launch_error("accumulate kernel launch");
 }
 
 int zero_shard_combine(const void* partials_dev, int32_t n_slots, double max_grad_norm,

@@ -15,9 +15,9 @@ from typing import Optional, Sequence
 import torch
 
 from . import (GLOBAL_BYTES, StepArgs, checkpoint, zero_global_t, zero_partials_bytes,
-               zero_partition, zero_partition_valid_numel, zero_repartition,
-               zero_shard_accumulate, zero_shard_apply, zero_shard_combine, zero_shard_reduce,
-               zero_shard_workspace_bytes)
+               zero_accumulate_local, zero_partition, zero_partition_valid_numel,
+               zero_repartition, zero_shard_accumulate, zero_shard_apply, zero_shard_combine,
+               zero_shard_reduce, zero_shard_workspace_bytes)
 
 
 @dataclass
@@ -94,6 +94,16 @@ class SimulatedWorld:
         ones add to them)."""
         for k in range(len(self.ranks)):
             zero_shard_accumulate(self.rank_args(k, hp, 1, accumulate=not first), stream)
+
+    def accumulate_local(self, micro_grads, first: bool, stream=None) -> None:
+        """Accumulation before the reduce (grads must be fp32): replica i's
+        micro-batch gradient micro_grads[i] (16-bit, same range as grads[i])
+        is widened into grads[i], which `first` sets and later calls add to.
+        The window's step then reduces the fp32 sums."""
+        if self.grad_dtype != torch.float32:
+            raise ValueError("accumulate_local needs a world with float32 replica buffers")
+        for i, g in enumerate(micro_grads):
+            zero_accumulate_local(g, self.grads[i], first, stream=stream)
 
     def step(self, hp: Hyper, t: int, stream=None, accumulate: bool = False) -> None:
         """Queue one optimizer step of every simulated rank (no host wait).
