@@ -59,6 +59,11 @@ def parse():
                     help="shard13b: gradient-accumulation window K; each step reduces K "
                          "micro-batches (the first sets the fp32 slice, the others add to it) "
                          "before the combine and AdamW")
+    ap.add_argument("--accumulation", default="reduced", choices=["reduced", "local"],
+                    help="shard13b with --micro-batches K > 1: 'reduced' reduces every "
+                         "micro-batch into the rank's fp32 slice (the default); 'local' "
+                         "sums the rank's own full gradient over the window in fp32 first "
+                         "(zero_accumulate_local) and reduces the replicas' fp32 sums once")
     ap.add_argument("--state-buffers", type=int, default=1, choices=[1, 2],
                     help="shard13b: 1 updates one fp32 state set in place (the default); "
                          "2 keeps two sets and alternates them, so pass 2 reads one and "
@@ -200,6 +205,99 @@ def run_shard13b(args, torch, Z, W):
                bytes_apply=bytes_apply, norm=info.norm, clipped=info.clipped,
                overflow=info.overflow, grads=st["grads"], master0=None, st=st)
     return res
+
+
+def run_shard13b_local(args, torch, Z, W):
+    """The 13B/8 rank with gradient accumulation before the reduce.  Per
+    step: K passes of zero_accumulate_local over the rank's own full flat
+    gradient (13e9 elements, bf16 into an fp32 sum), then one reduce of its
+    shard over the 8 replicas' fp32 sums (its own, plus 7 resident fp32
+    slices standing in for the peers'), combine and AdamW."""
+    w = W.SHARD_13B_OF_8
+    part = Z.zero_partition(w.numel, w.world_size, w.alignment)
+    s, P, K = part.shard_numel, part.padded_numel, args.micro_batches
+    valid = Z.zero_partition_valid_numel(part, 0)
+    dev = "cuda"
+    log("local accumulation: %d bf16 gradient + fp32 sum, 7 fp32 peer slices" % P)
+    own = torch.empty(P, dtype=torch.bfloat16, device=dev)
+    W.flat_normal(own, 0, w.numel, w.grad_sigma, W.grad_key(w, 0, 0, 0))
+    acc = torch.empty(P, dtype=torch.float32, device=dev)
+    peers = []
+    for i in range(1, w.world_size):
+        x = torch.empty(s, dtype=torch.float32, device=dev)
+        W.flat_normal(x, 0, w.numel, w.grad_sigma * K, W.grad_key(w, 0, 0, i))
+        peers.append(x)
+    master = torch.empty(s, dtype=torch.float32, device=dev)
+    W.flat_normal(master, 0, w.numel, w.master_sigma, W.master_key(w, 0))
+    m = torch.zeros(s, dtype=torch.float32, device=dev)
+    v = torch.zeros(s, dtype=torch.float32, device=dev)
+    full = torch.zeros(P, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(Z.zero_shard_workspace_bytes(s), dtype=torch.uint8, device=dev)
+    partials = torch.zeros(Z.zero_partials_bytes(1), dtype=torch.uint8, device=dev)
+    glob = torch.zeros(256, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step_args(t):
+        return Z.StepArgs(world_size=w.world_size, rank=0, shard_numel=s, valid_numel=valid,
+                          replica_grads=[acc[:s]] + peers, master=master, exp_avg=m,
+                          exp_avg_sq=v, full_params=full, workspace=ws, lr=w.lr,
+                          weight_decay=w.weight_decay, step=t, max_grad_norm=w.max_grad_norm)
+
+    t = 1
+    for _ in range(args.warmup):
+        for j in range(K):
+            Z.zero_accumulate_local(own, acc, j == 0, stream=stream)
+        Z.zero_shard_step(step_args(t), stream=stream)
+        t += 1
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(K + 3)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        e = ev[k]
+        e[0].record(stream)
+        for j in range(K):
+            Z.zero_accumulate_local(own, acc, j == 0, stream=stream)
+            e[1 + j].record(stream)
+        a = step_args(t)
+        Z.zero_shard_reduce(a, 0, partials, stream)
+        Z.zero_shard_combine(partials, 1, w.max_grad_norm, glob, stream)
+        e[K + 1].record(stream)
+        Z.zero_shard_apply(a, glob, stream)
+        e[K + 2].record(stream)
+        t += 1
+    torch.cuda.synchronize()
+    n = args.steps
+    ms = ev[0][0].elapsed_time(ev[-1][K + 2]) / n
+    first_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / n
+    add_ms = (sum(e[1].elapsed_time(e[K]) for e in ev) / n / (K - 1)) if K > 1 else None
+    red_ms = sum(e[K].elapsed_time(e[K + 1]) for e in ev) / n
+    app_ms = sum(e[K + 1].elapsed_time(e[K + 2]) for e in ev) / n
+    info = Z.zero_shard_step(step_args(t), want_info=True)
+    b_first, b_add = P * 6, P * 10
+    b_acc = b_first + (K - 1) * b_add
+    b_red, b_app = valid * (w.world_size * 4 + 4), valid * 30
+    b_step = b_acc + b_red + b_app
+    dom_ms, dom_b, dom_name = (add_ms, b_add, "accumulate_local_kernel (add)") if K > 1 else \
+        (first_ms, b_first, "accumulate_local_kernel (set)")
+    achieved = dom_b / (dom_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": valid / (ms * 1e-3), "unit": "params/s", "n_gpus": 1,
+        "steps": n, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name + ", gradient accumulation before the reduce",
+                   "micro_batches": K, "shard_numel": s, "full_gradient_numel": P,
+                   "world_size": 8, "replicas": 8, "grad_dtype": "bf16 (fp32 window sums)",
+                   "param_dtype": "bf16"},
+        "hbm_gbps": b_step / (ms * 1e-3) / 1e9, "hbm_frac": b_step / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "bytes_per_step": b_step,
+        "kernels_ms": {"accumulate_set": first_ms, "accumulate_add": add_ms,
+                       "reduce_fp32_and_fold_and_combine": red_ms, "apply": app_ms},
+        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": None},
+        "reduce_gbps": b_red / (red_ms * 1e-3) / 1e9, "apply_gbps": b_app / (app_ms * 1e-3) / 1e9,
+        "step_check": {"norm": info.norm, "clipped": info.clipped, "overflow": info.overflow},
+    }
+    print(json.dumps(out), flush=True)
 
 
 def cpu_baseline_shard13b(args, torch, W, st):
@@ -548,6 +646,11 @@ def main():
         return
     if args.workload == "zero3":
         run_zero3(args, torch, Z, W)
+        return
+    if args.accumulation == "local":
+        if args.micro_batches < 1:
+            raise SystemExit("--accumulation local needs --micro-batches >= 1")
+        run_shard13b_local(args, torch, Z, W)
         return
     r = run_shard13b(args, torch, Z, W)
     app_gbps = r["bytes_apply"] / (r["apply_ms"] * 1e-3) / 1e9
