@@ -220,7 +220,9 @@ typedef zero_global_t zero_step_info;
 
 /* Bytes of workspace a rank needs: the fp32 reduced gradient of its shard
  * (shard_numel * 4, rounded up to 256), one 16-byte partial sum of squares
- * and flag per 1024 elements of the reduce pass, one partials slot (see
+ * and flag per block of the reduce pass (1024 elements each; the block
+ * count is rounded up to a multiple of 8, or of 2048 for large shards, so
+ * that every XCD gets whole runs), one partials slot (see
  * zero_partials_bytes) and one zero_global_t.  Host only. */
 size_t zero_shard_workspace_bytes(int64_t shard_numel);
 
