@@ -339,16 +339,58 @@ def take(t: torch.Tensor, idx: np.ndarray) -> torch.Tensor:
 
 def structural_sample(n: int, rng: np.random.Generator, n_random: int = 1 << 16) -> np.ndarray:
     """Sorted unique indices in [0, n): both ends, both kernels' block and
-    XCD-range boundaries, and n_random uniform draws."""
+    XCD-range boundaries (an eighth of the grid per XCD, or runs of 256
+    blocks on large grids), and n_random uniform draws."""
     picks = [np.arange(min(n, 8)), np.arange(max(n - 8, 0), n)]
     for per_block in (1024, 256):                      # reduce / apply elements per block
         blocks = -(-(-(-n // 4)) // (per_block // 4))  # blocks needed
         blocks = -(-blocks // 8) * 8
         per_xcd = blocks // 8
         edges = np.arange(1, 8, dtype=np.int64) * per_xcd * per_block
-        picks.append(edges)
-        picks.append(edges - 1)
+        runs = 256 * per_block                         # one XCD run on large grids
+        run_edges = np.concatenate([np.arange(1, 17, dtype=np.int64),
+                                    rng.integers(1, max(n // runs, 2), 64, dtype=np.int64)])
+        for e in (edges, run_edges * runs):
+            picks.append(e)
+            picks.append(e - 1)
         picks.append(rng.integers(1, max(blocks, 2), 64, dtype=np.int64) * per_block)
     picks.append(rng.integers(0, max(n, 1), n_random, dtype=np.int64))
     s = np.unique(np.concatenate([np.asarray(p, np.int64) for p in picks]))
     return s[(s >= 0) & (s < n)]
+
+
+_SHARD13B = None
+
+
+def shard13b_reference(log: Optional[Callable[[str], None]] = None) -> dict:
+    """The oracle's side of rank 0 of the 13B/8 workload with the bench's
+    inputs, computed once per process: the norm and overflow flag over every
+    element (inputs regenerated chunk by chunk), and, at a structural sample
+    of the shard, the reduced gradient and the state after AdamW steps 1 and
+    2 on the same gradients (as the bench repeats them)."""
+    global _SHARD13B
+    if _SHARD13B is not None:
+        return _SHARD13B
+    w = W.SHARD_13B_OF_8
+    part = Z.zero_partition(w.numel, w.world_size, w.alignment)
+    n = Z.zero_partition_valid_numel(part, 0)
+    gkey = lambda i: W.grad_key(w, 0, 0, i)
+    sample = structural_sample(n, np.random.default_rng(5))
+    inv = oracle.inv_scale(1.0)
+    on = oracle_norm_and_sample(w.world_size, 0, n, w.numel, w.grad_sigma, gkey, torch.bfloat16,
+                                sample, inv, log=log)
+    applies, onorm, ocoef = oracle.clip(on.sumsq, w.max_grad_norm)
+    o_g, _, _ = oracle.reduce(on.codes, oracle.BF16, inv)
+    p = gather_generated(sample, 0, w.numel, w.master_sigma, W.master_key(w, 0), torch.float32,
+                         n).copy()
+    m = np.zeros(sample.size, np.float32)
+    v = np.zeros(sample.size, np.float32)
+    hp = Hyper(lr=w.lr, weight_decay=w.weight_decay, max_grad_norm=w.max_grad_norm)
+    states = []
+    for t in (1, 2):
+        oracle.adamw(o_g, p, m, v, ocoef, hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, t)
+        states.append((p.copy(), m.copy(), v.copy()))
+    _SHARD13B = dict(w=w, part=part, s=part.shard_numel, n=n, gkey=gkey, sample=sample, inv=inv,
+                     overflow=on.overflow, sumsq=on.sumsq, applies=applies, norm=onorm,
+                     coef=ocoef, g=o_g, states=states, hp=hp)
+    return _SHARD13B

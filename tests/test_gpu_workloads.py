@@ -98,20 +98,12 @@ def test_13b_shard_in_bench_configuration():
                           weight_decay=hp.weight_decay, step=t, max_grad_norm=hp.max_grad_norm,
                           grad_dtype=torch.bfloat16, param_dtype=torch.bfloat16)
 
-    # the oracle's norm over every element, from regenerated inputs
-    rng = np.random.default_rng(5)
-    sample = parity.structural_sample(n, rng)
-    say("oracle: reduce over %d elements x %d replicas, %d sampled" % (n, nrep, sample.size))
-    inv = oracle.inv_scale(1.0)
-    on = parity.oracle_norm_and_sample(nrep, 0, n, w.numel, w.grad_sigma, gkey, torch.bfloat16,
-                                       sample, inv, log=say)
-    assert on.overflow == 0
-    applies, onorm, ocoef = oracle.clip(on.sumsq, hp.max_grad_norm)
-    o_g, _, _ = oracle.reduce(on.codes, oracle.BF16, inv)
-    o_p = parity.gather_generated(sample, 0, w.numel, w.master_sigma, W.master_key(w, 0),
-                                  torch.float32, n).copy()
-    o_m = np.zeros(sample.size, np.float32)
-    o_v = np.zeros(sample.size, np.float32)
+    # the oracle's norm over every element, from regenerated inputs, and
+    # its AdamW on a sample
+    oref = parity.shard13b_reference(log=say)
+    sample, inv = oref["sample"], oref["inv"]
+    assert oref["overflow"] == 0
+    applies, onorm, o_g = oref["applies"], oref["norm"], oref["g"]
 
     # step 1, the fused entry point (the bench's kernels and grids)
     say("step 1")
@@ -136,8 +128,7 @@ def test_13b_shard_in_bench_configuration():
             say("step 2 (same gradients, as the bench repeats)")
             info2 = Z.zero_shard_step(args(2), want_info=True)
             assert info2.overflow == 0 and info2.norm == info.norm
-        oracle.adamw(o_g, o_p, o_m, o_v, ocoef, hp.lr, hp.beta1, hp.beta2, hp.eps,
-                     hp.weight_decay, t)
+        o_p, o_m, o_v = oref["states"][t - 1]
         for name, dev_t, ref in (("master", master, o_p), ("exp_avg", m, o_m),
                                  ("exp_avg_sq", v, o_v)):
             parity.assert_rel("step %d %s (sample)" % (t, name), parity.take(dev_t, sample).numpy(),
@@ -152,6 +143,8 @@ def test_13b_shard_in_bench_configuration():
     for a, b in _chunked(part.padded_numel - s, 1 << 30):
         assert bool((full[s + a:s + b] == parity.CANARY).all()), "write outside the slice"
     say("13B/8 shard matches: norm %.6f (oracle %.6f), coef %.9g" % (info.norm, onorm, info.coef))
+    del grads, master, m, v, full, ws
+    torch.cuda.empty_cache()
 
 
 # -------------------------------------------------------- ragged, bucketed
