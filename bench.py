@@ -621,9 +621,8 @@ def calibrate_copy(torch, n):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(each rank's step is local; see the sharding notes). Run with --gpus 1.",
-              file=sys.stderr)
+        print("bench.py measures one GPU: it times one rank's step on its own device and "
+              "has no multi-GPU launcher. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
