@@ -31,7 +31,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "ZeRO shard step: params updated/s + achieved HBM GB/s (% of 8 TB/s peak)"
-KERNEL_SRC = os.path.join(ROOT, "zero_sharded_optimizer_step_amd", "csrc", "zero_kernels.hip")
+# the sources that decide the kernels' code and launch geometry
+KERNEL_SRCS = [os.path.join(ROOT, "zero_sharded_optimizer_step_amd", "csrc", f)
+               for f in ("zero_kernels.hip", "zero_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_shard13b.json")
 
 
@@ -77,7 +79,10 @@ def parse():
 
 
 def kernel_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):

@@ -18,3 +18,19 @@ def test_plain_c_caller(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "all checks passed" in r.stdout
+
+
+def test_launch_grids_are_xcd_bijections(tmp_path):
+    """tests/c/grid_check.cpp, built with g++ against the library's internal
+    header: for the workloads' shard sizes and the edges of the grid
+    rounding, every launch covers its work, the XCD remap is a bijection
+    onto the grid, each XCD gets runs of consecutive logical blocks, and the
+    padding stays under one round."""
+    exe = str(tmp_path / "grid_check")
+    subprocess.run(["g++", "-std=c++17", "-O2", "-Wall", "-Werror",
+                    "-I", os.path.join(ROOT, "include"),
+                    "-I", os.path.join(ROOT, "zero_sharded_optimizer_step_amd", "csrc"),
+                    os.path.join(ROOT, "tests", "c", "grid_check.cpp"), "-o", exe], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "all checks passed" in r.stdout

@@ -77,6 +77,16 @@ inline Grid grid_for(int64_t n, int threads) {
     const int64_t nb = (b + kXcds - 1) / kXcds * kXcds;
     return Grid{nb, static_cast<int32_t>(nb / kXcds)};
 }
+// Logical block of dispatch-order block b (which the hardware sends to XCD
+// b % kXcds) in a grid that is a multiple of kXcds * group blocks: XCD x
+// takes logical blocks [k * kXcds * group + x * group, ... + group) for
+// k = 0, 1, ...  With group = grid / kXcds that is one contiguous share of
+// the grid per XCD.  constexpr, so the kernels and the host-side check of
+// the launch grids use the same code.
+constexpr int64_t xcd_logical_block(uint32_t b, uint32_t group) {
+    return static_cast<int64_t>((b / kXcds) / group) * (kXcds * group) + (b % kXcds) * group +
+           (b / kXcds) % group;
+}
 inline int64_t reduce_blocks_for(int64_t n) { return grid_for(n, kReduceThreads).blocks; }
 inline int64_t apply_blocks_for(int64_t n) { return grid_for(n, kApplyThreads).blocks; }
 inline int fold_blocks_for(int64_t reduce_blocks) {

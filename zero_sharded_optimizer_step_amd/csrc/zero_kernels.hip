@@ -36,13 +36,9 @@ struct ReplicaPtrs {
     const void* p[ZERO_MAX_REPLICAS];
 };
 
-// Logical block of dispatch-order block b (which the hardware sends to XCD
-// b % 8) in a grid that is a multiple of 8 * group blocks: XCD x takes
-// logical blocks [k * 8 * group + x * group, ... + group) for k = 0, 1, ...
-// With group = grid / 8 that is one contiguous eighth of the grid per XCD.
+// This block's logical index under the XCD remap (zero_internal.h).
 __device__ __forceinline__ int64_t xcd_block(uint32_t b, uint32_t group) {
-    const uint32_t x = b % kXcds, j = b / kXcds;
-    return static_cast<int64_t>(j / group) * (kXcds * group) + x * group + j % group;
+    return xcd_logical_block(b, group);
 }
 
 // ---------------------------------------------------------------- formats
