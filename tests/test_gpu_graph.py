@@ -60,3 +60,70 @@ def test_captured_step_replays_equal_eager_steps():
                                   parity.f32(eager.state(0)[f][:numel]))
         parity.assert_bitwise("replay %d params" % rep, parity.u16(graph_w.full_params),
                               parity.u16(eager.full_params))
+
+
+@pytest.mark.parametrize("mode", ["reduced", "local"])
+def test_captured_accumulation_window_replays_equal_eager(mode):
+    # A whole window of K = 3 micro-batches captured once: either pass 1 per
+    # micro-batch into the rank's slice (zero_shard_accumulate, then the
+    # step with accumulate = 1), or the fp32 window sums of every replica
+    # (zero_accumulate_local) and a step over them.  Each replay runs on new
+    # micro-batch gradients and must equal the eager window bit for bit.
+    numel, R, K = 300_007, 4, 3
+    print("graph capture of an accumulation window (%s)" % mode, flush=True)
+    hp = Hyper()
+    local = mode == "local"
+    gdt = torch.float32 if local else torch.bfloat16
+    eager = SimulatedWorld(numel, 1, n_replicas=R, alignment=128, grad_dtype=gdt,
+                           param_dtype=torch.bfloat16)
+    graph_w = SimulatedWorld(numel, 1, n_replicas=R, alignment=128, grad_dtype=gdt,
+                             param_dtype=torch.bfloat16)
+    # the captured window reads its micro-batches from fixed buffers
+    micro = [[torch.zeros(graph_w.padded, dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+             for _ in range(K)]
+    emicro = [[torch.zeros_like(x) for x in mb] for mb in micro]
+
+    def window(w, mbufs, stream=None):
+        for j in range(K):
+            if local:
+                w.accumulate_local(mbufs[j], first=j == 0, stream=stream)
+            else:
+                for i in range(R):
+                    w.grads[i].copy_(mbufs[j][i])
+                if j < K - 1:
+                    w.accumulate(hp, first=j == 0, stream=stream)
+        if local:
+            Z.zero_shard_step(w.rank_args(0, hp, 1), stream=stream)
+        else:
+            Z.zero_shard_step(w.rank_args(0, hp, 1, accumulate=True), stream=stream)
+
+    def reset():
+        for w in (eager, graph_w):
+            W.flat_normal(w.master[0], 0, numel, 0.02, ("graph-acc-m",))
+            w.exp_avg[0].zero_()
+            w.exp_avg_sq[0].zero_()
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                   # warm up on a side stream
+        window(graph_w, micro, stream=s)
+    torch.cuda.synchronize()
+    reset()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        window(graph_w, micro)
+    for rep in range(3):
+        for j in range(K):
+            for i in range(R):
+                W.flat_normal(emicro[j][i], 0, numel, 1e-3, ("graph-acc", rep, j, i))
+                micro[j][i].copy_(emicro[j][i])
+        window(eager, emicro)
+        g.replay()
+        _ = torch.ones(1000, device="cuda").sum().item()      # eager work and a sync between
+        for f, name in enumerate(("master", "exp_avg", "exp_avg_sq")):
+            parity.assert_bitwise("%s replay %d %s" % (mode, rep, name),
+                                  parity.f32(graph_w.state(0)[f][:numel]),
+                                  parity.f32(eager.state(0)[f][:numel]))
+        parity.assert_bitwise("%s replay %d params" % (mode, rep), parity.u16(graph_w.full_params),
+                              parity.u16(eager.full_params))
