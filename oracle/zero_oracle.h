@@ -24,7 +24,11 @@
  * computed in fp64 and rounded once where it enters fp32 arithmetic.
  * Parity status of each function:
  *   oracle_partition, oracle_bucket_plan      pinned (brute force, page numbers)
- *   oracle_*_to_f32, oracle_f32_to_*          pinned (exhaustive / library)
+ *   oracle_*_to_f32, oracle_f32_to_*          pinned (decoders exhaustive against
+ *                                             numpy / torch; encoders exhaustive
+ *                                             over all 2^32 fp32 patterns against
+ *                                             an integer reference written from
+ *                                             the IEEE-754 definition)
  *   oracle_reduce                             pinned (identity, N*g, fsum)
  *   oracle_reduce_accumulate                  pinned (numpy fp32 sum over
  *                                             micro-batches, one micro-batch,
