@@ -1,4 +1,5 @@
-"""The device cast over every fp32 bit pattern, through the C ABI.
+"""The device cast over every fp32 bit pattern, and the device decode of
+every 16-bit code, through the C ABI.
 
 A step with lr = 0, weight decay 0 and zero gradients leaves every master
 unchanged (p * 1 - 0 * 0), so the parameters it writes are the cast alone.
@@ -48,3 +49,22 @@ def test_device_cast_of_every_fp32_pattern(pdt):
         del pat, x, got, ref, nan, same
     del world
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+def test_device_decode_of_every_16_bit_code(dt):
+    # One replica holding every code, reduced at scale 1: the fp32 slice is
+    # each code widened, exactly (NaN codes widen to NaN), and the flag is
+    # raised by the inf and NaN codes.
+    n = 1 << 16
+    print("device decode, every %s code" % dt, flush=True)
+    world = SimulatedWorld(n, 1, n_replicas=1, alignment=8, grad_dtype=dt)
+    codes = torch.arange(n, dtype=torch.int32, device="cuda").to(torch.int16)
+    world.grads[0].view(torch.int16).copy_(codes)
+    world.step(Hyper(), 1)
+    assert world.result().overflow
+    g = world.reduced_grad(0)[:n]
+    ref = codes.view(dt).float()
+    nan = torch.isnan(ref)
+    assert torch.equal(g[~nan].view(torch.int32), ref[~nan].view(torch.int32))
+    assert bool(torch.isnan(g[nan]).all())
