@@ -464,3 +464,47 @@ def test_ping_pong_state_equals_in_place():
     for got, ref in zip(final, w1.state(0)):
         parity.assert_bitwise("ping-pong state", parity.f32(got[:numel]), parity.f32(ref[:numel]))
     parity.assert_bitwise("ping-pong params", parity.u16(w2.full_params), parity.u16(w1.full_params))
+
+
+def test_adamw_on_ieee_edge_values_matches_oracle():
+    # Every combination of master, m and v drawn from signed zeros,
+    # subnormals, the smallest normal, ordinary values, the largest finite
+    # value, infinities and NaN, under finite gradients from tiny to near the
+    # bf16 maximum (clipping off, so nothing rescales them).  The device's
+    # division, square root and subnormal handling must give the oracle's
+    # bits; a NaN must be a NaN on both sides.
+    import itertools
+    import oracle
+    say("AdamW on IEEE edge values")
+    S = np.array([0.0, -0.0, 1.4e-45, -1.4e-45, 1e-40, 1.17549435e-38, 1e-20, 0.02, -0.5, 3.0,
+                  1e20, 3.4028235e38, -3.4028235e38, np.inf, -np.inf, np.nan], np.float32)
+    G = np.array([0.0, -0.0, 1e-40, 0.5, -3.0, 1e30, 3.38e38, -1e-3], np.float32)
+    combos = np.array(list(itertools.product(range(S.size), repeat=3)), np.int64)
+    n = combos.shape[0] * G.size
+    p0 = np.tile(S[combos[:, 0]], G.size)
+    m0 = np.tile(S[combos[:, 1]], G.size)
+    v0 = np.tile(S[combos[:, 2]], G.size)
+    gcodes = np.repeat(oracle.f32_to_bf16(G), combos.shape[0])
+    g = oracle.bf16_to_f32(gcodes)
+    hp = Hyper(max_grad_norm=0.0)
+    world = SimulatedWorld(n, 1, n_replicas=1, alignment=8, grad_dtype=BF16)
+    world.grads[0].view(torch.int16)[:n].copy_(torch.from_numpy(gcodes.view(np.int16)))
+    for dev, host in ((world.master[0], p0), (world.exp_avg[0], m0), (world.exp_avg_sq[0], v0)):
+        dev[:n].copy_(torch.from_numpy(host))
+    p, m, v = p0.copy(), m0.copy(), v0.copy()
+    for t in (1, 3):
+        world.step(hp, t)
+        res = world.result()
+        assert not res.overflow and not res.clipped
+        oracle.adamw(g, p, m, v, 1.0, hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, t)
+        for name, dev, ref in (("master", world.master[0], p), ("exp_avg", world.exp_avg[0], m),
+                               ("exp_avg_sq", world.exp_avg_sq[0], v)):
+            got = parity.f32(dev)[:n]
+            nan = np.isnan(ref)
+            assert np.array_equal(np.isnan(got), nan), "%s: NaN positions differ (t=%d)" % (name, t)
+            parity.assert_bitwise("t=%d %s" % (t, name), got[~nan], ref[~nan])
+        cast = parity.u16(world.full_params)[:n]
+        want = oracle.f32_to_bf16(p)
+        cnan = np.isnan(oracle.bf16_to_f32(want))
+        assert np.array_equal(np.isnan(oracle.bf16_to_f32(cast)), cnan)
+        parity.assert_bitwise("t=%d cast" % t, cast[~cnan], want[~cnan])
