@@ -93,3 +93,34 @@ def test_host_threads_default_follows_omp_and_affinity():
     out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
                          check=True).stdout
     assert int(out) == len(os.sched_getaffinity(0))
+
+
+@pytest.mark.parametrize("dtype", [Z.ZERO_BF16, Z.ZERO_FP16])
+def test_host_adamw_on_ieee_edge_values(dtype):
+    # The offloaded update on every combination of master, m and v drawn
+    # from signed zeros, subnormals, extremes, infinities and NaN, under
+    # gradients from 0 to 3e38: the oracle's bits, NaN for NaN.
+    import itertools
+    S = np.array([0.0, -0.0, 1.4e-45, -1.4e-45, 1e-40, 1.17549435e-38, 1e-20, 0.02, -0.5, 3.0,
+                  1e20, 3.4028235e38, -3.4028235e38, np.inf, -np.inf, np.nan], np.float32)
+    G = np.array([0.0, -0.0, 1e-40, 0.5, -3.0, 1e30, 3e38, -1e-3], np.float32)
+    combos = np.array(list(itertools.product(range(S.size), repeat=3)), np.int64)
+    p = np.tile(S[combos[:, 0]], G.size)
+    m = np.tile(S[combos[:, 1]], G.size)
+    v = np.tile(S[combos[:, 2]], G.size)
+    g = np.repeat(G, combos.shape[0])
+    op, om, ov = p.copy(), m.copy(), v.copy()
+    out = np.empty(p.size, np.uint16)
+    for t in (1, 3):
+        Z.zero_host_adamw(g, 1.0, p, m, v, out, dtype, step=t, n_threads=3)
+        oracle.adamw(g, op, om, ov, 1.0, 6e-5, 0.9, 0.999, 1e-8, 0.01, t)
+        for name, a, b in (("master", p, op), ("exp_avg", m, om), ("exp_avg_sq", v, ov)):
+            nan = np.isnan(b)
+            assert np.array_equal(np.isnan(a), nan), (name, t)
+            assert np.array_equal(a[~nan].view(np.uint32), b[~nan].view(np.uint32)), (name, t)
+        enc, dec = ((oracle.f32_to_bf16, oracle.bf16_to_f32) if dtype == Z.ZERO_BF16
+                    else (oracle.f32_to_f16, oracle.f16_to_f32))
+        ref = enc(op)
+        cnan = np.isnan(dec(ref))
+        assert np.array_equal(np.isnan(dec(out)), cnan)
+        assert np.array_equal(out[~cnan], ref[~cnan]), t
