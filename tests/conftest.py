@@ -10,3 +10,16 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line(
         "markers", "gpu: needs an MI355X (gfx950) GPU; parity against the CPU oracle")
+
+
+def pytest_runtest_teardown(item, nextitem):
+    """After each GPU test, hand the device memory torch has cached back, so
+    the full-size tests (60-175 GB each) start from an empty pool."""
+    if item.get_closest_marker("gpu") is None:
+        return
+    import gc
+    gc.collect()
+    torch = sys.modules.get("torch")
+    if torch is not None and torch.cuda.is_available():
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
