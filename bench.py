@@ -326,7 +326,19 @@ def cpu_baseline_shard13b(args, torch, W, st):
     dt = time.perf_counter() - t0
     return dict(value=n / dt, unit="params/s", cores=1, kind="oracle",
                 sample="first %d elements of rank 0's shard (8 bf16 replicas): reduce, clip, "
-                       "AdamW, bf16 cast; one host thread, %.1f s" % (n, dt))
+                       "AdamW, bf16 cast; one host thread of %s (%d CPUs available), %.1f s"
+                       % (n, host_cpu(), len(os.sched_getaffinity(0)), dt))
+
+
+def host_cpu() -> str:
+    """The host's CPU model, from /proc/cpuinfo."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "an unknown CPU"
 
 
 def run_ragged(args, torch, Z, W):
