@@ -34,6 +34,8 @@
  *   - Element counts are 64-bit; shards beyond 2^32 elements are fine.
  *   - Calls keep no state between them; concurrent calls on different
  *     buffers are safe.  Calls that write the same buffers race.
+ *   - A call's inputs and outputs must not overlap, unless the call says
+ *     that it updates a buffer in place.
  */
 #ifndef ZERO_H
 #define ZERO_H
@@ -141,8 +143,9 @@ int zero_bucket_plan(const int64_t* tensor_numel, int32_t n_tensors,
  * have non-decreasing, non-overlapping ranges inside [0, flat_numel);
  * src_dev is a host array of device pointers.  A bucket at a time may be
  * flattened by passing its slots and flat_numel = bucket end (no padding
- * is then written).  Bit copy: dtype (ZERO_FP16 / ZERO_BF16) is checked,
- * the values are not interpreted.
+ * is then written).  The sources must not overlap flat_dev.  Bit copy:
+ * dtype (ZERO_FP16 / ZERO_BF16) is checked, the values are not
+ * interpreted.
  * Errors: NULL pointers, bad dtype, slots out of order or out of range ->
  * ZERO_EINVAL; flat_dev misaligned -> ZERO_EALIGN; launch -> ZERO_EDEVICE.
  */
@@ -357,7 +360,8 @@ int zero_loss_scaler_update(zero_loss_scaler_t* st, int32_t overflow,
  * 16-bit parameters (at least its valid elements; r * shard_numel is its
  * first flat element).  Only the shards [lo, hi) meets are read.  On one
  * GPU the shards may be slices of one buffer; across GPUs they would be
- * peer-mapped pointers.  Bit copy: dtype is checked, values are not read.
+ * peer-mapped pointers.  dst must not overlap the shards.  Bit copy: dtype
+ * is checked, values are not read.
  * Errors: NULL arguments, lo < 0, hi < lo, hi > numel, bad dtype, a NULL
  * shard that [lo, hi) meets -> ZERO_EINVAL; misaligned dst or shard ->
  * ZERO_EALIGN; launch -> ZERO_EDEVICE. */
