@@ -287,6 +287,21 @@ def test_flatten_edge_cases():
     _flatten_case([8] * 130 + [13] * 131, True)             # more than one launch batch
 
 
+def test_flatten_large_tables_with_crowded_slots():
+    # Tables of more than 16 entries use the coarse index of the launch's
+    # blocks; here big tensors sit between runs of one-block tensors, so
+    # single slots hold many entries, and tables of 17, 128 and 129 entries
+    # cross the switch and the launch batch.
+    say("flatten: crowded coarse-index slots")
+    crowd = []
+    for k in range(6):
+        crowd += [2_000_003 + 97 * k] + [1 + (j % 9) for j in range(20)]
+    _flatten_case(crowd, True, seed=1)
+    _flatten_case([300] * 17, True, seed=2)
+    _flatten_case([1] * 100 + [3_000_001] + [5] * 27, True, seed=3)
+    _flatten_case([7] * 64 + [1_000_000] + [7] * 64, False, seed=4)
+
+
 def test_flatten_per_bucket():
     say("flatten bucket by bucket")
     rng = np.random.default_rng(4)

@@ -377,13 +377,24 @@ constexpr int kFlatBatch = 128;            // tensors per launch (kernel argumen
 constexpr int kFlatThreads = 256;
 constexpr int64_t kFlatMaxPiece = int64_t(1) << 30;   // elements per table entry
 
+// Each block finds its table entry before it can issue a load, and blocks
+// live about a microsecond, so the lookup must stay short: a binary search
+// over at most kFlatDirect entries, or over the entries of one slot of a
+// coarse index (slot i = blocks [i << shift, (i + 1) << shift)) for larger
+// tables.  All of it is read with scalar loads from the kernel arguments.
+constexpr int kFlatSlots = 32;
+constexpr int kFlatDirect = 16;
+
 struct FlatBatch {
     const unsigned short* src[kFlatBatch];   // nullptr: write zeros
     int64_t dst[kFlatBatch];                 // first flat element
     int64_t n[kFlatBatch];
     int32_t first_block[kFlatBatch + 1];     // prefix of blocks per entry
     int32_t count;
+    int32_t slot_shift;
+    int32_t slot_entry[kFlatSlots + 1];      // entry owning block i << shift; then count - 1
 };
+static_assert(sizeof(FlatBatch) <= 4000, "the table travels as kernel arguments");
 
 // Elements k..k+7 of the 16 packed in (lo, hi), k uniform in 1..7.
 __device__ __forceinline__ u32x4 shift_pick(const u32x4 lo, const u32x4 hi, int k) {
@@ -412,8 +423,14 @@ __device__ __forceinline__ u32x4 shift_pick(const u32x4 lo, const u32x4 hi, int 
 __global__ __launch_bounds__(kFlatThreads) void flatten_kernel(FlatBatch b, unsigned short* __restrict__ flat) {
     const int64_t blk = xcd_block(blockIdx.x, gridDim.x / kXcds);
     if (blk >= b.first_block[b.count]) return;       // grid rounded up to the XCD count
-    // Which table entry owns this block: binary search over the prefix.
+    // Which table entry owns this block: a binary search over the prefix,
+    // narrowed by the coarse index when the table is large.
     int lo = 0, hi = b.count - 1;
+    if (hi >= kFlatDirect) {
+        const int slot = static_cast<int>(blk >> b.slot_shift);
+        lo = b.slot_entry[slot];
+        hi = b.slot_entry[slot + 1];
+    }
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (b.first_block[mid] <= blk) lo = mid; else hi = mid - 1;
@@ -568,6 +585,19 @@ int copy_ranges(int32_t n, Src src_of, Dst dst_of, Len len_of, unsigned short* f
     auto flush = [&]() -> int {
         if (b.count == 0) return ZERO_OK;
         b.first_block[b.count] = static_cast<int32_t>(blocks);
+        // The coarse index: at most kFlatSlots slots of 2^shift blocks, each
+        // naming the entry that owns its first block.
+        int shift = 0;
+        while (((blocks - 1) >> shift) >= kFlatSlots) ++shift;
+        const int slots = static_cast<int>((blocks - 1) >> shift) + 1;
+        b.slot_shift = shift;
+        int owner = 0;
+        for (int i = 0; i < slots; ++i) {
+            const int64_t first = static_cast<int64_t>(i) << shift;
+            while (owner + 1 < b.count && b.first_block[owner + 1] <= first) ++owner;
+            b.slot_entry[i] = owner;
+        }
+        b.slot_entry[slots] = b.count - 1;
         const int64_t grid = (blocks + kXcds - 1) / kXcds * kXcds;
         hipLaunchKernelGGL(flatten_kernel, dim3(static_cast<unsigned>(grid)), dim3(kFlatThreads), 0, st,
                            b, flat);
