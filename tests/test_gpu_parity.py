@@ -302,6 +302,33 @@ def test_flatten_large_tables_with_crowded_slots():
     _flatten_case([7] * 64 + [1_000_000] + [7] * 64, False, seed=4)
 
 
+def test_flatten_destinations_beyond_2_pow_32_elements():
+    # Slots whose destinations cross 2^32 elements, with gaps between them.
+    # A launch's table counts destinations from its first one in 32 bits,
+    # so the launcher must start a new batch before that would overflow.
+    say("flatten: destinations beyond 2^32 elements")
+    n32 = 1 << 32
+    specs = [(0, 1000), (1000, 5), (n32 - 3, 100), (n32 + 1000, 7), (n32 + 1007, 33)]
+    flat_numel = n32 + 4096
+    flat = torch.full((flat_numel + 64,), 0x1357, dtype=torch.int16, device="cuda")
+    rng = np.random.default_rng(12)
+    srcs = [torch.from_numpy(rng.integers(0, 65536, n + 3, dtype=np.uint64).astype(np.uint16)
+                             .view(np.int16)).cuda()[k % 3:k % 3 + n].view(torch.bfloat16)
+            for k, (_, n) in enumerate(specs)]
+    slots = [Z.zero_tensor_slot_t(off, n, 0, 0) for off, n in specs]
+    Z.zero_bucket_flatten(slots, srcs, torch.bfloat16, flat.view(torch.bfloat16), flat_numel)
+    torch.cuda.synchronize()
+    for (off, n), src in zip(specs, srcs):
+        assert torch.equal(flat[off:off + n], src.view(torch.int16)), "slot at %d" % off
+    for lo, hi in ((1005, n32 - 3), (n32 + 97, n32 + 1000)):
+        assert bool((flat[lo:hi] == 0x1357).all()), "gap [%d, %d) written" % (lo, hi)
+    end = specs[-1][0] + specs[-1][1]
+    assert bool((flat[end:flat_numel] == 0).all()), "padding not zeroed"
+    assert bool((flat[flat_numel:] == 0x1357).all()), "wrote past flat_numel"
+    del flat
+    torch.cuda.empty_cache()
+
+
 def test_flatten_per_bucket():
     say("flatten bucket by bucket")
     rng = np.random.default_rng(4)

@@ -373,7 +373,7 @@ __global__ __launch_bounds__(kApplyThreads) void apply_kernel(
 // launch are spread over the XCDs like the step's kernels, so each XCD
 // copies a contiguous run of the batch's tensors.  The body is stored
 // nontemporally: nothing reads it again before the next pass.
-constexpr int kFlatBatch = 128;            // tensors per launch (kernel arguments)
+constexpr int kFlatBatch = 192;            // tensors per launch (kernel arguments)
 constexpr int kFlatThreads = 256;
 constexpr int64_t kFlatMaxPiece = int64_t(1) << 30;   // elements per table entry
 
@@ -387,8 +387,11 @@ constexpr int kFlatDirect = 16;
 
 struct FlatBatch {
     const unsigned short* src[kFlatBatch];   // nullptr: write zeros
-    int64_t dst[kFlatBatch];                 // first flat element
-    int64_t n[kFlatBatch];
+    // first flat element, counted from dst_base: a launch's pieces span
+    // less than 2^32 elements (the launcher starts a new batch otherwise)
+    uint32_t dst[kFlatBatch];
+    uint32_t n[kFlatBatch];                  // elements (a piece is at most 2^30)
+    int64_t dst_base;
     int32_t first_block[kFlatBatch + 1];     // prefix of blocks per entry
     int32_t count;
     int32_t slot_shift;
@@ -438,7 +441,7 @@ __global__ __launch_bounds__(kFlatThreads) void flatten_kernel(FlatBatch b, unsi
     const int t = lo;
     const int64_t jb = blk - b.first_block[t];
     const unsigned short* src = b.src[t];
-    const int64_t d0 = b.dst[t], n = b.n[t], d1 = d0 + n;
+    const int64_t d0 = b.dst_base + b.dst[t], n = b.n[t], d1 = d0 + n;
     // Aligned body [a0, a1) of the destination, head [d0, a0), tail [a1, d1).
     int64_t a0 = (d0 + 7) & ~int64_t(7);
     if (a0 > d1) a0 = d1;
@@ -613,13 +616,15 @@ int copy_ranges(int32_t n, Src src_of, Dst dst_of, Len len_of, unsigned short* f
         const int64_t body = (dst + n) / 8 * 8 > a0 ? ((dst + n) / 8 * 8 - a0) / 8 : 0;
         int64_t nb = (body + kFlatThreads - 1) / kFlatThreads;
         if (nb < 1) nb = 1;
-        if (b.count == kFlatBatch || blocks + nb > (int64_t(1) << 30)) {
+        if (b.count == kFlatBatch || blocks + nb > (int64_t(1) << 30) ||
+            (b.count > 0 && dst + n - b.dst_base > int64_t(0xffffffff))) {
             int rc = flush();
             if (rc) return rc;
         }
+        if (b.count == 0) b.dst_base = dst;
         b.src[b.count] = src;
-        b.dst[b.count] = dst;
-        b.n[b.count] = n;
+        b.dst[b.count] = static_cast<uint32_t>(dst - b.dst_base);
+        b.n[b.count] = static_cast<uint32_t>(n);
         b.first_block[b.count] = static_cast<int32_t>(blocks);
         blocks += nb;
         ++b.count;
