@@ -394,6 +394,7 @@ struct FlatBatch {
     int64_t dst_base;
     int32_t first_block[kFlatBatch + 1];     // prefix of blocks per entry
     int32_t count;
+    int32_t n_blocks;                        // = first_block[count]
     int32_t slot_shift;
     int32_t slot_entry[kFlatSlots + 1];      // entry owning block i << shift; then count - 1
 };
@@ -425,7 +426,7 @@ __device__ __forceinline__ u32x4 shift_pick(const u32x4 lo, const u32x4 hi, int 
 
 __global__ __launch_bounds__(kFlatThreads) void flatten_kernel(FlatBatch b, unsigned short* __restrict__ flat) {
     const int64_t blk = xcd_block(blockIdx.x, gridDim.x / kXcds);
-    if (blk >= b.first_block[b.count]) return;       // grid rounded up to the XCD count
+    if (blk >= b.n_blocks) return;                    // grid rounded up to the XCD count
     // Which table entry owns this block: a binary search over the prefix,
     // narrowed by the coarse index when the table is large.
     int lo = 0, hi = b.count - 1;
@@ -588,6 +589,7 @@ int copy_ranges(int32_t n, Src src_of, Dst dst_of, Len len_of, unsigned short* f
     auto flush = [&]() -> int {
         if (b.count == 0) return ZERO_OK;
         b.first_block[b.count] = static_cast<int32_t>(blocks);
+        b.n_blocks = static_cast<int32_t>(blocks);
         // The coarse index: at most kFlatSlots slots of 2^shift blocks, each
         // naming the entry that owns its first block.
         int shift = 0;
