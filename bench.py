@@ -20,7 +20,6 @@ oracle timed on a bounded sample of the same inputs on one host core.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -31,9 +30,6 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "ZeRO shard step: params updated/s + achieved HBM GB/s (% of 8 TB/s peak)"
-# the sources that decide the kernels' code and launch geometry
-KERNEL_SRCS = [os.path.join(ROOT, "zero_sharded_optimizer_step_amd", "csrc", f)
-               for f in ("zero_kernels.hip", "zero_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_shard13b.json")
 
 
@@ -79,20 +75,20 @@ def parse():
 
 
 def kernel_hash() -> str:
-    h = hashlib.sha256()
-    for path in KERNEL_SRCS:
-        h.update(open(path, "rb").read())
-    return h.hexdigest()[:16]
+    """Hash of the host and gfx950 code of the library the bench loads."""
+    from zero_sharded_optimizer_step_amd import _abi, build
+    return build.code_hash(_abi.LIB_PATH)
 
 
 def measured_traffic(workload: str):
     """HBM bytes per launch of the dominant kernel from the committed
-    counter runs, or None when absent or taken on other kernel sources."""
+    counter runs, or None when absent or taken on a library whose code
+    differs from the one loaded."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256_16") != kernel_hash() or rec.get("workload") != workload:
+    if rec.get("library_code_sha256_16") != kernel_hash() or rec.get("workload") != workload:
         return None
     return rec.get("apply_bytes_per_launch")
 

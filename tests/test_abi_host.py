@@ -36,6 +36,38 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_abi._PROTOTYPES), "binding and header disagree"
 
 
+def test_code_hash_covers_host_and_device_code(tmp_path):
+    # The key of the committed counter record: the built library's host
+    # code and its gfx950 code object, read from the file.
+    from zero_sharded_optimizer_step_amd import build
+    h = build.code_hash(_abi.LIB_PATH)
+    assert re.fullmatch(r"[0-9a-f]{16}", h)
+    assert build.code_hash(_abi.LIB_PATH) == h
+    data = bytearray(open(_abi.LIB_PATH, "rb").read())
+    secs = build._elf_sections(bytes(data))
+    assert ".hip_fatbin" in secs and ".text" in secs
+    # a flipped byte in the host code changes the hash
+    text = secs[".text"]
+    at = bytes(data).index(text[:4096]) + 100
+    data[at] ^= 0xFF
+    bad = tmp_path / "lib_flipped.so"
+    bad.write_bytes(bytes(data))
+    assert build.code_hash(str(bad)) != h
+    # and so does one in the gfx950 kernels' code
+    data[at] ^= 0xFF
+    fb = secs[".hip_fatbin"]
+    elf = fb.index(b"\x7fELF")
+    dev_text = build._elf_sections(fb[elf:])[".text"]
+    at = bytes(data).index(dev_text[:4096]) + 100
+    data[at] ^= 0xFF
+    bad.write_bytes(bytes(data))
+    assert build.code_hash(str(bad)) != h
+    junk = tmp_path / "junk.so"
+    junk.write_bytes(b"not an ELF file")
+    with pytest.raises(ValueError):
+        build.code_hash(str(junk))
+
+
 def test_binding_names_match_the_abi():
     for n in declared_symbols():
         assert callable(getattr(Z, n)), n

@@ -11,8 +11,10 @@ default) and denormals kept (no flush-to-zero, no fast-math).
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
+import struct
 import subprocess
 import sys
 
@@ -59,6 +61,58 @@ def build(out: str = LIB_PATH, verbose: bool = False) -> str:
         print("\n".join(msgs))
     os.replace(tmp, out)
     return out
+
+
+def _elf_sections(d: bytes) -> dict:
+    """Section name -> bytes of a little-endian ELF64 image."""
+    if d[:4] != b"\x7fELF" or d[4] != 2 or d[5] != 1:
+        raise ValueError("not a little-endian ELF64 image")
+    shoff, = struct.unpack_from("<Q", d, 0x28)
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", d, 0x3A)
+    table = []
+    for i in range(shnum):
+        name, _typ, _flags, _addr, off, size = struct.unpack_from("<IIQQQQ", d, shoff + i * shentsize)
+        table.append((name, off, size))
+    strtab = table[shstrndx][1]
+    out = {}
+    for name, off, size in table:
+        end = d.index(b"\0", strtab + name)
+        out[d[strtab + name:end].decode()] = d[off:off + size]
+    return out
+
+
+def code_hash(path: str = LIB_PATH) -> str:
+    """First 16 hex digits of a SHA-256 over the code a built library runs:
+    the host .text and .rodata (entry points, checks and the launch
+    geometry they compute) and, from the clang offload bundle in
+    .hip_fatbin, the gfx950 code object's .text, .rodata (kernel
+    descriptors) and .note (kernel metadata).  These are byte-identical
+    across builds of the same sources, whereas the symbol tables carry a
+    per-build unique name; edits to comments leave the hash unchanged."""
+    secs = _elf_sections(open(path, "rb").read())
+    h = hashlib.sha256()
+    for name in (".text", ".rodata"):
+        h.update(secs[name])
+    fb = secs[".hip_fatbin"]
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    if not fb.startswith(magic):
+        raise ValueError("%s: .hip_fatbin is not an offload bundle" % path)
+    count, = struct.unpack_from("<Q", fb, len(magic))
+    pos = len(magic) + 8
+    found = False
+    for _ in range(count):
+        off, size, id_len = struct.unpack_from("<QQQ", fb, pos)
+        pos += 24
+        ident = fb[pos:pos + id_len].decode()
+        pos += id_len
+        if ident.endswith("-" + ARCH):
+            dev = _elf_sections(fb[off:off + size])
+            for name in (".text", ".rodata", ".note"):
+                h.update(dev[name])
+            found = True
+    if not found:
+        raise ValueError("%s holds no %s code object" % (path, ARCH))
+    return h.hexdigest()[:16]
 
 
 if __name__ == "__main__":

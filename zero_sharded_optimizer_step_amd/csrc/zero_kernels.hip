@@ -305,8 +305,11 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 // when no replica overflowed, then the cast of the new masters into the
 // rank's slice of the full low-precision buffer ([P1] §2.1 all-gather).
 // One element, in fp32 with one rounding per operation (no contraction):
-//   m' = b1 m + c1 g;  v' = b2 v + c2 g^2;  d = sqrt(v') / sqrt(1 - b2^t) + eps;
-//   p' = p (1 - lr wd) - lr / (1 - b1^t) * m' / d.
+//   m' = b1 m + c1 g;  v' = b2 v + c2 g^2;  d = sqrt(v') * inv_sqrt_bc2 + eps;
+//   p' = p * decay - step_size * (m' / d),
+// with the per-step constants inv_sqrt_bc2 = 1 / sqrt(1 - b2^t),
+// decay = 1 - lr wd and step_size = lr / (1 - b1^t), each rounded once to
+// fp32 on the host.
 __device__ __forceinline__ void adamw1(float g, float& p, float& m, float& v, const AdamConsts& k) {
     m = k.b1 * m + k.c1 * g;
     v = k.b2 * v + k.c2 * (g * g);
@@ -369,9 +372,9 @@ __global__ __launch_bounds__(kApplyThreads) void apply_kernel(
 // arbitrary offset costs no unaligned accesses (the second vector of a
 // shifted pair is the next thread's first, served from cache).  The few
 // elements before the first and after the last aligned destination vector
-// of a tensor are copied one by one by its first block.  Blocks of one
-// launch are spread over the XCDs like the step's kernels, so each XCD
-// copies a contiguous run of the batch's tensors.  The body is stored
+// of a tensor are copied one by one by its first block.  The blocks of one
+// launch are split over the XCDs in eighths (one contiguous share of the
+// grid each), so each XCD copies a contiguous run of the batch's tensors.  The body is stored
 // nontemporally: nothing reads it again before the next pass.
 constexpr int kFlatBatch = 192;            // tensors per launch (kernel arguments)
 constexpr int kFlatThreads = 256;
