@@ -80,7 +80,8 @@ const char* zero_last_error(void);
  * valid_numel(r) = clamp(numel - r*shard_numel, 0, shard_numel) are real and
  * the rest is padding at the end of the flat space.
  * Errors: numel < 0, world_size < 1, alignment < 1 or not a power of two,
- * out == NULL -> ZERO_EINVAL.  Host only; touches no device.
+ * a padded count beyond INT64_MAX, out == NULL -> ZERO_EINVAL.  Host only;
+ * touches no device.
  */
 typedef struct {
     int64_t numel;          /* real flat parameter count                  */
@@ -109,8 +110,9 @@ int64_t zero_partition_valid_numel(const zero_partition_t* p, int32_t rank);
  * Host arrays: tensor_numel[n_tensors] (in), slots[n_tensors] (out),
  * buckets[bucket_cap] (out).  *n_buckets receives the bucket count; when it
  * exceeds bucket_cap the call fails with ZERO_ESIZE and *n_buckets holds the
- * capacity needed.  Errors: n_tensors < 0, a negative size,
- * reduce_bucket_size < 1, a NULL pointer -> ZERO_EINVAL.  Host only.
+ * capacity needed.  Errors: n_tensors < 0, a negative size, sizes summing
+ * past INT64_MAX, reduce_bucket_size < 1, a NULL pointer -> ZERO_EINVAL.
+ * Host only.
  */
 typedef struct {
     int64_t offset;         /* first flat element of the tensor           */

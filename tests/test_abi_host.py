@@ -96,6 +96,21 @@ def test_partition_rejects(args):
     assert Z.zero_last_error()
 
 
+def test_partition_rejects_padded_counts_beyond_int64():
+    big = 2**63 - 1
+    part = Z.zero_partition(big, 1, 1)               # no padding needed: representable
+    assert part.padded_numel == big
+    for N, A in ((3, 1024), (8, 128), (2, 2)):
+        with pytest.raises(Z.ZeroError) as e:
+            Z.zero_partition(big, N, A)
+        assert e.value.code == Z.ZERO_EINVAL and "overflows" in Z.zero_last_error()
+    # the largest count that still pads into int64 is accepted
+    unit = 8 * 128
+    top = (big // unit) * unit
+    part = Z.zero_partition(top, 8, 128)
+    assert part.padded_numel == top and part.shard_numel == top // 8
+
+
 def test_partition_valid_numel_out_of_range():
     part = Z.zero_partition(100, 4, 8)
     with pytest.raises(ValueError):
@@ -132,6 +147,14 @@ def test_bucket_plan_ragged_workload():
     assert len(buckets) == nb and [s.bucket for s in slots] == list(bof)
     assert buckets[-1].end == sum(sizes) == RAGGED_2000.numel
     assert all(b.end - b.begin <= 2e8 for b in buckets)
+
+
+def test_bucket_plan_rejects_sizes_summing_past_int64():
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_bucket_plan([2**62, 2**62, 2**62], int(2e8))
+    assert e.value.code == Z.ZERO_EINVAL and "sum past int64" in Z.zero_last_error()
+    slots, buckets = Z.zero_bucket_plan([2**62, 2**62 - 1], int(2e8))   # sums to 2^63 - 1
+    assert [b.n_tensors for b in buckets] == [1, 1] and buckets[-1].end == 2**63 - 1
 
 
 def test_bucket_plan_reports_needed_capacity():
@@ -260,6 +283,11 @@ def test_combine_and_flatten_reject():
     slots[1].offset = 10
     assert L.zero_bucket_flatten(slots, 2, ptrs, Z.ZERO_BF16, 0x4000, 15, None) == Z.ZERO_EINVAL
     assert L.zero_bucket_flatten(slots, 2, ptrs, 7, 0x4000, 100, None) == Z.ZERO_EINVAL
+    # an offset near the top of int64 is out of range, not an overflow
+    slots[1].offset, slots[1].numel = 2**63 - 5, 10
+    assert L.zero_bucket_flatten(slots, 2, ptrs, Z.ZERO_BF16, 0x4000, 100, None) == Z.ZERO_EINVAL
+    assert "out of order or outside" in Z.zero_last_error()
+    slots[1].offset, slots[1].numel = 10, 10
     assert L.zero_bucket_flatten(slots, 2, ptrs, Z.ZERO_BF16, 0x4002, 100, None) == Z.ZERO_EALIGN
     ptrs[1] = 0x2001
     assert L.zero_bucket_flatten(slots, 2, ptrs, Z.ZERO_BF16, 0x4000, 100, None) == Z.ZERO_EALIGN

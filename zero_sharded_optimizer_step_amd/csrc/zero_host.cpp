@@ -124,9 +124,13 @@ int zero_partition(int64_t numel, int32_t world_size, int32_t alignment,
     if (alignment < 1 || (alignment & (alignment - 1)) != 0)
         return fail(ZERO_EINVAL, "alignment %d is not a power of two", alignment);
     // One aligned unit is world_size * alignment elements of the flat space;
-    // every rank gets the same number of units.
+    // every rank gets the same number of units.  The padded count must stay
+    // representable.
     const int64_t unit = static_cast<int64_t>(world_size) * alignment;
     const int64_t units = numel / unit + (numel % unit ? 1 : 0);
+    if (units > INT64_MAX / unit)
+        return fail(ZERO_EINVAL, "numel %lld padded to whole units of %lld overflows int64",
+                    (long long)numel, (long long)unit);
     out->numel = numel;
     out->shard_numel = units * alignment;
     out->padded_numel = out->shard_numel * world_size;
@@ -153,9 +157,14 @@ int zero_bucket_plan(const int64_t* tensor_numel, int32_t n_tensors,
     if (!n_buckets || (n_tensors > 0 && (!tensor_numel || !slots)) || bucket_cap < 0 ||
         (bucket_cap > 0 && !buckets))
         return fail(ZERO_EINVAL, "a required pointer is NULL or bucket_cap < 0");
-    for (int32_t t = 0; t < n_tensors; ++t)
+    int64_t total = 0;
+    for (int32_t t = 0; t < n_tensors; ++t) {
         if (tensor_numel[t] < 0)
             return fail(ZERO_EINVAL, "tensor_numel[%d] = %lld < 0", t, (long long)tensor_numel[t]);
+        if (tensor_numel[t] > INT64_MAX - total)
+            return fail(ZERO_EINVAL, "the tensor sizes sum past int64 at tensor %d", t);
+        total += tensor_numel[t];
+    }
 
     int32_t count = 0;         // buckets opened so far
     int64_t cursor = 0;        // flat offset of the next tensor

@@ -776,7 +776,7 @@ int zero_bucket_flatten(const zero_tensor_slot_t* slots, int32_t n_tensors, cons
     int64_t prev_end = 0;
     for (int32_t t = 0; t < n_tensors; ++t) {
         const zero_tensor_slot_t& s = slots[t];
-        if (s.numel < 0 || s.offset < prev_end || s.offset + s.numel > flat_numel)
+        if (s.numel < 0 || s.offset < prev_end || s.offset > flat_numel || s.numel > flat_numel - s.offset)
             return fail(ZERO_EINVAL, "slot %d [%lld, +%lld) is out of order or outside [0, %lld)", t,
                         (long long)s.offset, (long long)s.numel, (long long)flat_numel);
         if (s.numel > 0 && !src_dev[t]) return fail(ZERO_EINVAL, "src_dev[%d] is NULL", t);
