@@ -293,6 +293,67 @@ def test_combine_and_flatten_reject():
     assert L.zero_bucket_flatten(slots, 2, ptrs, Z.ZERO_BF16, 0x4000, 100, None) == Z.ZERO_EALIGN
 
 
+def test_binding_refuses_buffers_shorter_than_the_call_touches():
+    # The C ABI sees addresses only; the binding compares each buffer's size
+    # with the extent the kernels touch and raises before any call.
+    import torch
+    s = 1024
+    with pytest.raises(ValueError, match="master"):
+        Z.zero_shard_step(good_args(master=FakeTensor(0x100000, 4 * s - 4)), stream=0)
+    with pytest.raises(ValueError, match="replica_grads\\[2\\]"):
+        reps = [FakeTensor(0x10000 * (i + 1), 2 * s, dtype=torch.bfloat16) for i in range(4)]
+        reps[2] = FakeTensor(0x30000, 2 * s - 2, dtype=torch.bfloat16)
+        Z.zero_shard_step(good_args(replica_grads=reps), stream=0)
+    # rank 1 writes full-buffer elements [s, 2s)
+    with pytest.raises(ValueError, match="full_params"):
+        Z.zero_shard_step(good_args(full_params=FakeTensor(0x400000, 2 * 2 * s - 2,
+                                                           dtype=torch.bfloat16)), stream=0)
+    # exactly enough passes the size check and reaches the library's own checks
+    ok = good_args(master=FakeTensor(0x100000, 4 * s), valid_numel=s, step=0)
+    with pytest.raises(Z.ZeroError):
+        Z.zero_shard_step(ok, stream=0)
+    with pytest.raises(ValueError, match="acc"):
+        Z.zero_accumulate_local(FakeTensor(0x10000, 200, dtype=torch.bfloat16),
+                                FakeTensor(0x20000, 399), True, n=100, stream=0)
+    with pytest.raises(ValueError, match="global_buf"):
+        Z.zero_shard_combine(FakeTensor(0x10000, Z.zero_partials_bytes(2)), 2, 1.0,
+                             FakeTensor(0x20000, Z.GLOBAL_BYTES - 1), stream=0)
+    with pytest.raises(ValueError, match="partials"):
+        Z.zero_shard_combine(FakeTensor(0x10000, Z.zero_partials_bytes(2) - 1), 2, 1.0,
+                             FakeTensor(0x20000, Z.GLOBAL_BYTES), stream=0)
+    slots, _ = Z.zero_bucket_plan([10, 7], 100)
+    with pytest.raises(ValueError, match="srcs\\[1\\]"):
+        Z.zero_bucket_flatten(slots, [FakeTensor(0x1000, 20), FakeTensor(0x2000, 13)],
+                              torch.bfloat16, FakeTensor(0x4000, 64), 32, stream=0)
+    with pytest.raises(ValueError, match="flat"):
+        Z.zero_bucket_flatten(slots, [FakeTensor(0x1000, 20), FakeTensor(0x2000, 14)],
+                              torch.bfloat16, FakeTensor(0x4000, 63), 32, stream=0)
+    part = Z.zero_partition(100, 4, 8)               # shards of 32; rank 3 holds 4 real
+    shards = [FakeTensor(0x1000 * (k + 1), 64) for k in range(4)]
+    shards[3] = FakeTensor(0x4000, 7)
+    with pytest.raises(ValueError, match="shards\\[3\\]"):
+        Z.zero_gather_params(part, shards, torch.bfloat16, 90, 100, FakeTensor(0x9000, 64),
+                             stream=0)
+    with pytest.raises(ValueError, match="dst"):
+        Z.zero_gather_params(part, [FakeTensor(0x1000 * (k + 1), 64) for k in range(4)],
+                             torch.bfloat16, 10, 50, FakeTensor(0x9000, 79), stream=0)
+    to = Z.zero_partition(100, 2, 8)                 # new shards of 56 fp32
+    with pytest.raises(ValueError, match="dsts\\[1\\]"):
+        Z.zero_repartition(part, [FakeTensor(0x1000 * (k + 1), 128) for k in range(4)], to,
+                           [FakeTensor(0x8000, 224), FakeTensor(0x9000, 223)], stream=0)
+    with pytest.raises(ValueError, match="srcs\\[3\\]"):
+        Z.zero_repartition(part, [FakeTensor(0x1000 * (k + 1), 128) for k in range(3)] +
+                           [FakeTensor(0x4000, 15)], to,
+                           [FakeTensor(0x8000, 224), FakeTensor(0x9000, 224)], stream=0)
+    g = np.zeros(100, np.float32)
+    with pytest.raises(ValueError, match="exp_avg_sq"):
+        Z.zero_host_adamw(g, 1.0, np.zeros(100, np.float32), np.zeros(100, np.float32),
+                          np.zeros(99, np.float32))
+    with pytest.raises(ValueError, match="params_out"):
+        Z.zero_host_adamw(g, 1.0, np.zeros(100, np.float32), np.zeros(100, np.float32),
+                          np.zeros(100, np.float32), params_out=np.zeros(99, np.uint16))
+
+
 def test_workspace_and_partials_sizes():
     slot = Z.zero_partials_bytes(1)
     assert slot >= 16 + 256 * 16

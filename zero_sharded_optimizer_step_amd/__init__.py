@@ -69,6 +69,17 @@ def _dptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _need(t, nbytes: int, what: str) -> None:
+    """Refuse a buffer smaller than the bytes a call will touch in it.  The
+    C ABI receives only addresses, so this is the one place where a short
+    tensor can be caught before a kernel reads or writes past its end."""
+    if t is None or nbytes <= 0:
+        return
+    have = t.nbytes if isinstance(getattr(t, "nbytes", None), int) else t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError("%s holds %d bytes; the call touches %d" % (what, have, nbytes))
+
+
 # ------------------------------------------------------------------ host only
 def zero_last_error() -> str:
     return lib().zero_last_error().decode()
@@ -145,6 +156,9 @@ def zero_bucket_flatten(slots, srcs, dtype, flat, flat_numel: Optional[int] = No
     ptrs = (_abi.vp * max(n, 1))(*[_dptr(s) for s in srcs])
     if flat_numel is None:
         flat_numel = flat.numel()
+    _need(flat, 2 * flat_numel, "flat")
+    for t, (sl, src) in enumerate(zip(slots, srcs)):
+        _need(src, 2 * sl.numel, "srcs[%d]" % t)
     check(lib().zero_bucket_flatten(arr, n, ptrs, dtype_code(dtype), _dptr(flat), flat_numel,
                                     _stream(stream)), "zero_bucket_flatten")
 
@@ -181,6 +195,23 @@ class StepArgs:
     exp_avg_out: object = None
     exp_avg_sq_out: object = None
 
+    def check_sizes(self, gsize: int) -> None:
+        """Every buffer must hold what the step touches in it: valid_numel
+        elements of each replica slice and state array, and the rank's
+        slice of the full buffer (or its own parameter shard)."""
+        n = self.valid_numel
+        if n <= 0 or not 0 <= self.rank < self.world_size:
+            return            # nothing is touched, or the library rejects the call
+        for i, r in enumerate(self.replica_grads):
+            _need(r, gsize * n, "replica_grads[%d]" % i)
+        for name in ("master", "exp_avg", "exp_avg_sq", "master_out", "exp_avg_out",
+                     "exp_avg_sq_out"):
+            _need(getattr(self, name), 4 * n, name)
+        if self.param_shard is not None:
+            _need(self.param_shard, 2 * n, "param_shard")
+        else:
+            _need(self.full_params, 2 * (self.rank * self.shard_numel + n), "full_params")
+
     def c_args(self) -> zero_step_args:
         reps = list(self.replica_grads)
         self._ptrs = (_abi.vp * max(len(reps), 1))(*[_dptr(r) for r in reps])
@@ -213,6 +244,7 @@ class StepArgs:
         a.loss_scale = self.loss_scale
         a.grad_predivide = self.grad_predivide
         a.max_grad_norm = self.max_grad_norm
+        self.check_sizes(4 if a.grad_dtype == ZERO_FP32 else 2)
         self._c = a
         return a
 
@@ -222,6 +254,7 @@ def _args(a) -> zero_step_args:
 
 
 def zero_shard_reduce(args, slot: int, partials, stream=None) -> None:
+    _need(partials, (slot + 1) * zero_partials_bytes(1), "partials")
     check(lib().zero_shard_reduce(ctypes.byref(_args(args)), slot, _dptr(partials),
                                   _stream(stream)), "zero_shard_reduce")
 
@@ -239,6 +272,8 @@ def zero_accumulate_local(grad, acc, first: bool, n: Optional[int] = None,
     (first) or incremented by grad[:n] widened to fp32.  n defaults to
     grad.numel()."""
     n = grad.numel() if n is None else n
+    _need(grad, grad.element_size() * n, "grad")
+    _need(acc, 4 * n, "acc")
     check(lib().zero_accumulate_local(_dptr(grad), dtype_code(grad.dtype), _dptr(acc), n,
                                       1 if first else 0, _stream(stream)),
           "zero_accumulate_local")
@@ -246,11 +281,14 @@ def zero_accumulate_local(grad, acc, first: bool, n: Optional[int] = None,
 
 def zero_shard_combine(partials, n_slots: int, max_grad_norm: float, global_buf,
                        stream=None) -> None:
+    _need(partials, n_slots * zero_partials_bytes(1), "partials")
+    _need(global_buf, GLOBAL_BYTES, "global_buf")
     check(lib().zero_shard_combine(_dptr(partials), n_slots, max_grad_norm, _dptr(global_buf),
                                    _stream(stream)), "zero_shard_combine")
 
 
 def zero_shard_apply(args, global_buf, stream=None) -> None:
+    _need(global_buf, GLOBAL_BYTES, "global_buf")
     check(lib().zero_shard_apply(ctypes.byref(_args(args)), _dptr(global_buf), _stream(stream)),
           "zero_shard_apply")
 
@@ -293,6 +331,12 @@ def zero_repartition(from_part: zero_partition_t, srcs: Sequence, to_part: zero_
     dp = (_abi.vp * max(len(dsts), 1))(*[_dptr(t) for t in dsts])
     if len(srcs) != from_part.world_size or len(dsts) != to_part.world_size:
         raise ValueError("one tensor per rank of each partition")
+    if from_part.numel == to_part.numel and from_part.world_size >= 1 and to_part.world_size >= 1:
+        for k, t in enumerate(srcs):
+            _need(t, 4 * max(0, min(from_part.shard_numel,
+                                    from_part.numel - k * from_part.shard_numel)), "srcs[%d]" % k)
+        for j, t in enumerate(dsts):
+            _need(t, 4 * to_part.shard_numel, "dsts[%d]" % j)
     check(lib().zero_repartition(ctypes.byref(from_part), sp, ctypes.byref(to_part), dp,
                                  _stream(stream)), "zero_repartition")
 
@@ -320,6 +364,7 @@ def zero_offload_apply(args, global_buf, staging: OffloadStaging, want_info: boo
     """Pass 2 on the host: args.master / exp_avg / exp_avg_sq are host (pinned)
     tensors; waits for the stream."""
     info = zero_step_info() if want_info else None
+    _need(global_buf, GLOBAL_BYTES, "global_buf")
     check(lib().zero_offload_apply(ctypes.byref(_args(args)), _dptr(global_buf),
                                    ctypes.byref(staging.c),
                                    ctypes.byref(info) if info is not None else None,
@@ -343,6 +388,9 @@ def zero_host_adamw(g, coef: float, master, exp_avg, exp_avg_sq, params_out=None
             return None
         return x.data_ptr() if hasattr(x, "data_ptr") else x.ctypes.data
     n = g.numel() if hasattr(g, "numel") and callable(g.numel) else g.size
+    for x, name in ((master, "master"), (exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq")):
+        _need(x, 4 * n, name)
+    _need(params_out, 2 * n, "params_out")
     check(lib().zero_host_adamw(n, ptr(g), coef, ptr(master), ptr(exp_avg), ptr(exp_avg_sq),
                                 ptr(params_out), dtype_code(param_dtype), lr, beta1, beta2, eps,
                                 weight_decay, step, n_threads), "zero_host_adamw")
@@ -355,6 +403,11 @@ def zero_gather_params(part: zero_partition_t, shards: Sequence, dtype, lo: int,
     device tensor per rank)."""
     if len(shards) != part.world_size:
         raise ValueError("one shard per rank")
+    s = part.shard_numel
+    if s > 0 and 0 <= lo < hi <= part.numel:
+        _need(dst, 2 * (hi - lo), "dst")
+        for k in range(lo // s, (hi - 1) // s + 1):
+            _need(shards[k], 2 * (min(hi, (k + 1) * s) - k * s), "shards[%d]" % k)
     sp = (_abi.vp * len(shards))(*[_dptr(t) for t in shards])
     check(lib().zero_gather_params(ctypes.byref(part), sp, dtype_code(dtype), lo, hi, _dptr(dst),
                                    _stream(stream)), "zero_gather_params")
