@@ -30,7 +30,6 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "ZeRO shard step: params updated/s + achieved HBM GB/s (% of 8 TB/s peak)"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_shard13b.json")
 
 
 def parse():
@@ -80,17 +79,22 @@ def kernel_hash() -> str:
     return build.code_hash(_abi.LIB_PATH)
 
 
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+
+
 def measured_traffic(workload: str):
-    """HBM bytes per launch of the dominant kernel from the committed
-    counter runs, or None when absent or taken on a library whose code
+    """Calibrated HBM bytes (FETCH_SIZE + WRITE_SIZE) of the roofline's
+    kernel, over the same unit as its `achieved` figure, from the committed
+    counter runs; None when absent or taken on a library whose code
     differs from the one loaded."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(traffic_file(workload)))
     except (OSError, ValueError):
         return None
     if rec.get("library_code_sha256_16") != kernel_hash() or rec.get("workload") != workload:
         return None
-    return rec.get("apply_bytes_per_launch")
+    return rec.get("roofline_traffic")
 
 
 def log(msg):
@@ -489,9 +493,10 @@ def run_repartition(args, torch, Z, W):
         "config": {"workload": "optimizer state of %d params re-partitioned from 8 ranks to 3 "
                                "(master, exp_avg, exp_avg_sq)" % P, "params": P},
         "hbm_gbps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS, "bytes_per_step": nbytes,
-        "roofline": {"bound": "hbm", "kernel": "flatten_kernel (range copies of zero_repartition)",
+        "roofline": {"bound": "hbm", "kernel": "flatten_kernel (range copies of zero_repartition, "
+                                                "all launches of one step)",
                      "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None},
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": measured_traffic("repartition")},
         "checkpoint_file": {"bytes": fbytes, "save_s": t_save, "save_gbps": fbytes / t_save / 1e9,
                             "load_s": t_load, "load_gbps": fbytes / t_load / 1e9,
                             "where": "temporary directory on the host"},
@@ -612,9 +617,10 @@ def run_zero3(args, torch, Z, W):
                                "prefetch (live bound: 2 layers)", "params": w.numel,
                    "layers": L},
         "hbm_gbps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS, "bytes_per_step": nbytes,
-        "roofline": {"bound": "hbm", "kernel": "flatten_kernel (range copies of zero_gather_params)",
+        "roofline": {"bound": "hbm", "kernel": "flatten_kernel (range copies of zero_gather_params, "
+                                                "all launches of one walk)",
                      "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None},
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": measured_traffic("zero3")},
     }
     print(json.dumps(out), flush=True)
 
