@@ -673,7 +673,9 @@ def main():
     r = run_shard13b(args, torch, Z, W)
     app_gbps = r["bytes_apply"] / (r["apply_ms"] * 1e-3) / 1e9
     step_gbps = r["bytes_step"] / (r["ms"] * 1e-3) / 1e9
-    traffic = measured_traffic("shard13b")
+    # counted on the in-place apply (one state set); the ping-pong variant
+    # is another kernel instantiation, whose counters were not taken
+    traffic = measured_traffic("shard13b") if args.state_buffers == 1 else None
     out = {
         "metric": METRIC,
         "value": r["valid"] / (r["ms"] * 1e-3),
