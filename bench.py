@@ -298,7 +298,7 @@ def run_shard13b_local(args, torch, Z, W):
                        "reduce_fp32_and_fold_and_combine": red_ms, "apply": app_ms},
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": None},
+                     "traffic": measured_traffic("shard13b_local") if K > 1 else None},
         "reduce_gbps": b_red / (red_ms * 1e-3) / 1e9, "apply_gbps": b_app / (app_ms * 1e-3) / 1e9,
         "step_check": {"norm": info.norm, "clipped": info.clipped, "overflow": info.overflow},
     }
