@@ -4,13 +4,19 @@
 
 Default workload: a 13B-parameter flat model over 8 data-parallel ranks;
 this GPU is rank 0 and owns a 1,625,000,064-element shard.  Eight bf16
-replica gradient slices, fp32 master weights and Adam moments (two sets,
-alternated step by step: pass 2 reads one and writes the other), and the
+replica gradient slices, fp32 master weights and Adam moments (one set,
+updated in place; --state-buffers 2 alternates two), and the
 13,000,000,512-element bf16 full parameter buffer sit in HBM before timing
-starts.  One step = replica reduce (+ unscale, inf/nan flag, partial norm),
-combine (norm, clip factor), AdamW + cast into the rank's slice of the full
-buffer: the three kernels zero_shard_step queues, here queued by the split
-calls so that HIP events between them time each kernel.
+starts.  One step = replica reduce (+ unscale, inf/nan flag, partial norm,
+then the fold of the block partials), combine (norm, clip factor), AdamW +
+cast into the rank's slice of the full buffer: the kernels zero_shard_step
+queues, here queued by the split calls so that HIP events between them
+time each kernel.
+
+The harness allocates its buffers with torch's caching allocator in
+expandable-segments mode (PYTORCH_HIP_ALLOC_CONF, unless the environment
+sets it): its fixed-size physical chunks gave a steadier step time than
+one allocation per buffer.
 
 Prints one JSON line.  `value` is params updated per second (the shard's
 real elements / step time); `roofline` is for the dominant kernel (the
@@ -24,6 +30,9 @@ import json
 import os
 import sys
 import time
+
+# before torch is imported: the caching allocator reads it once
+os.environ.setdefault("PYTORCH_HIP_ALLOC_CONF", "expandable_segments:True")
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -729,6 +738,7 @@ def main():
         "apply_gbps": app_gbps,
         "reduce_gbps": r["bytes_reduce"] / (r["reduce_ms"] * 1e-3) / 1e9,
         "step_check": {"norm": r["norm"], "clipped": r["clipped"], "overflow": r["overflow"]},
+        "allocator": os.environ.get("PYTORCH_HIP_ALLOC_CONF"),
     }
     if not args.no_cpu_baseline and args.micro_batches == 1:
         log("timing the CPU oracle on a sample")
