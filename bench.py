@@ -20,8 +20,10 @@ one allocation per buffer.
 
 Prints one JSON line.  `value` is params updated per second (the shard's
 real elements / step time); `roofline` is for the dominant kernel (the
-AdamW + cast pass) against the 8 TB/s HBM peak; `cpu_baseline` is the CPU
-oracle timed on a bounded sample of the same inputs on one host core.
+AdamW + cast pass; in an accumulation window, the adding pass 1) against
+the 8 TB/s HBM peak, with `traffic` from the committed counter record of
+the same library code; `cpu_baseline` is the CPU oracle timed on a bounded
+sample of the same inputs on one host core.
 """
 from __future__ import annotations
 
