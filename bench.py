@@ -13,11 +13,6 @@ cast into the rank's slice of the full buffer: the kernels zero_shard_step
 queues, here queued by the split calls so that HIP events between them
 time each kernel.
 
-The harness allocates its buffers with torch's caching allocator in
-expandable-segments mode (PYTORCH_HIP_ALLOC_CONF, unless the environment
-sets it): its fixed-size physical chunks gave a steadier step time than
-one allocation per buffer.
-
 Prints one JSON line.  `value` is params updated per second (the shard's
 real elements / step time); `roofline` is for the dominant kernel (the
 AdamW + cast pass; in an accumulation window, the adding pass 1) against
@@ -32,9 +27,6 @@ import json
 import os
 import sys
 import time
-
-# before torch is imported: the caching allocator reads it once
-os.environ.setdefault("PYTORCH_HIP_ALLOC_CONF", "expandable_segments:True")
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -740,7 +732,6 @@ def main():
         "apply_gbps": app_gbps,
         "reduce_gbps": r["bytes_reduce"] / (r["reduce_ms"] * 1e-3) / 1e9,
         "step_check": {"norm": r["norm"], "clipped": r["clipped"], "overflow": r["overflow"]},
-        "allocator": os.environ.get("PYTORCH_HIP_ALLOC_CONF"),
     }
     if not args.no_cpu_baseline and args.micro_batches == 1:
         log("timing the CPU oracle on a sample")
