@@ -17,8 +17,11 @@ Prints one JSON line.  `value` is params updated per second (the shard's
 real elements / step time); `roofline` is for the dominant kernel (the
 AdamW + cast pass; in an accumulation window, the adding pass 1) against
 the 8 TB/s HBM peak, with `traffic` from the committed counter record of
-the same library code; `cpu_baseline` is the CPU oracle timed on a bounded
-sample of the same inputs on one host core.
+the same library code; `copy_ceiling` is a plain one-read, one-write copy
+of one gradient slice through the library's flatten kernel, timed in the
+same process, for reading `roofline.frac` against what the part streams in
+practice; `cpu_baseline` is the CPU oracle timed on a bounded sample of the
+same inputs on one host core.
 """
 from __future__ import annotations
 
@@ -640,6 +643,33 @@ def run_zero3(args, torch, Z, W):
     print(json.dumps(out), flush=True)
 
 
+def copy_ceiling(torch, Z, st, reps=10):
+    """A plain copy through the library's flatten kernel, timed in the same
+    process: rank 0's bf16 gradient slice of replica 0 (one table entry:
+    one read and one write stream) into rank 1's slice of the full buffer,
+    which rank 0's step never touches; the slice is zeroed again after.
+    Its bandwidth is what a one-read, one-write stream reaches on this
+    part, the practical ceiling for the streaming passes (the AdamW pass
+    keeps four read and four write streams in flight)."""
+    s = st["s"]
+    src, dst = st["grads"][0], st["full"][s:2 * s]
+    slot = Z.zero_tensor_slot_t(offset=0, numel=s, bucket=0, reserved=0)
+    stream = torch.cuda.current_stream()
+    Z.zero_bucket_flatten([slot], [src], src.dtype, dst, s, stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        Z.zero_bucket_flatten([slot], [src], src.dtype, dst, s, stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[reps // 2]
+    dst.zero_()
+    torch.cuda.synchronize()
+    return {"kernel": "flatten_kernel copying one %d-element bf16 tensor" % s,
+            "bytes": 4 * s, "median_ms": ms, "gbps": 4 * s / (ms * 1e-3) / 1e9}
+
+
 def calibrate_copy(torch, n):
     """Plain copies of a known size, for scaling the HBM byte counters."""
     nbytes = 4 << 30
@@ -733,6 +763,10 @@ def main():
         "reduce_gbps": r["bytes_reduce"] / (r["reduce_ms"] * 1e-3) / 1e9,
         "step_check": {"norm": r["norm"], "clipped": r["clipped"], "overflow": r["overflow"]},
     }
+    cc = copy_ceiling(torch, Z, r["st"])
+    cc["frac_of_peak"] = cc["gbps"] / HBM_PEAK_GBPS
+    cc["roofline_kernel_frac_of_copy"] = roofline["achieved"] / cc["gbps"]
+    out["copy_ceiling"] = cc
     if not args.no_cpu_baseline and args.micro_batches == 1:
         log("timing the CPU oracle on a sample")
         out["cpu_baseline"] = cpu_baseline_shard13b(args, torch, W, r["st"])
