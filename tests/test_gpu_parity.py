@@ -48,6 +48,30 @@ def test_world_matches_oracle(case):
         % (rep.norm_rel_err, rep.state_bitwise, rep.cast_max_ulp))
 
 
+PREDIVIDE_CASES = [
+    # (numel, world, alignment, dtype, sigma, loss_scale, predivide, clip, steps):
+    # DDP-style averaging over a world that is not a power of two, and a
+    # static loss scale that is not one, so the unscale multiplier
+    # fp32(1/(S·D)) is rounded on both sides
+    (100_003, 3, 128, BF16, 1e-3, 1.0, 3.0, 1.0, 2),
+    (300_007, 6, 8, FP16, 1e-3, 1000.0, 6.0, 1.0, 2),
+    (65_537, 5, 8, FP16, 1e-2, 2.0**12, 0.7, 1e9, 2),
+]
+
+
+@pytest.mark.parametrize("case", PREDIVIDE_CASES,
+                         ids=[f"P{c[0]}-N{c[1]}-S{c[5]:g}-D{c[6]:g}" for c in PREDIVIDE_CASES])
+def test_world_with_predivide_matches_oracle(case):
+    numel, world, align, dt, sigma, scale, pre, clip, steps = case
+    say("predivide case %s" % (case,))
+    spec = parity.Spec(numel=numel, world_size=world, alignment=align, grad_dtype=dt,
+                       grad_sigma=sigma, steps=steps, name="predivide-%d-%d" % (numel, world),
+                       hp=Hyper(loss_scale=scale, grad_predivide=pre, max_grad_norm=clip))
+    rep = parity.run(spec)
+    say("norm rel err %.2e, bitwise state fraction %.6f, cast max ulp %d"
+        % (rep.norm_rel_err, rep.state_bitwise, rep.cast_max_ulp))
+
+
 def test_tiny_workload_matches_oracle():
     w = W.TINY
     say("tiny workload")

@@ -1,11 +1,15 @@
 """The oracle's pins must catch plausible mistakes (CPU only).
 
 Each mutant is a copy of the oracle source with one planted mistake (a
-dropped term, a wrong sign or operand, a wrong rounding rule).  It is built
-to a temporary library and the pin tests run against it in a subprocess;
-every mutant must make them fail.  Nothing here touches the HIP library.
+dropped term, a wrong sign or operand, a wrong rounding rule).  A mutant of
+the C file is built to a temporary library; a mutant of the Python layer
+(the unscale multiplier, the cross-rank norm and skip, re-partition,
+gather) is a copy of the oracle package and the pin tests in a temporary
+tree.  The pin tests run against it in a subprocess; every mutant must make
+them fail.  Nothing here touches the HIP library.
 """
 import os
+import shutil
 import subprocess
 import sys
 
@@ -65,4 +69,51 @@ def test_pins_kill_mutant(name, tmp_path):
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         "-W", "ignore::RuntimeWarning"] + PINS,
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 1, "mutant survived the pins: " + name + "\n" + r.stdout[-2000:]
+
+
+PY_SRC = os.path.join(ROOT, "oracle", "__init__.py")
+CKPT_PINS = ["test_checkpoint_host.py::test_repartition_hand_example",
+             "test_checkpoint_host.py::test_repartition_round_trip_and_empty_ranks",
+             "test_checkpoint_host.py::test_oracle_gather_hand_example"]
+
+PY_MUTANTS = {
+    "predivide_dropped": ("return np.float32(1.0 / (float(loss_scale) * float(predivide)))",
+                          "return np.float32(1.0 / float(loss_scale))"),
+    "norm_restarts_every_rank": ("sumsq if last else 0.0", "0.0"),
+    "overflow_does_not_skip": ("    if overflow:\n        return info\n", ""),
+    "repartition_ranks_reversed": ("for r in range(from_world)] +",
+                                   "for r in reversed(range(from_world))] +"),
+    "gather_one_past_the_end": ("return flat[lo:hi].copy()", "return flat[lo:hi + 1].copy()"),
+}
+
+
+def run_pins_on_copy(tmp_path, py_src):
+    """The pin tests, in a temporary tree whose oracle package has `py_src`
+    as its Python layer and loads the oracle library as built."""
+    root = tmp_path / "root"
+    shutil.copytree(os.path.join(ROOT, "oracle"), root / "oracle",
+                    ignore=shutil.ignore_patterns("__pycache__", "*.so*"))
+    (root / "oracle" / "__init__.py").write_text(py_src)
+    shutil.copytree(HERE, root / "tests", ignore=shutil.ignore_patterns("__pycache__", "c"))
+    # the copy's own directory comes first on the path (cwd and conftest);
+    # the library package, which the checkpoint pins import, comes from ROOT
+    env = dict(os.environ, ZERO_ORACLE_LIB=oracle.build(force=False), PYTHONPATH=ROOT)
+    pins = [os.path.basename(f) for f in PINS] + CKPT_PINS
+    return subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                           "-W", "ignore::RuntimeWarning"] + ["tests/" + f for f in pins],
+                          cwd=str(root), env=env, capture_output=True, text=True, timeout=600)
+
+
+def test_pins_pass_on_an_unmutated_copy(tmp_path):
+    r = run_pins_on_copy(tmp_path, open(PY_SRC).read())
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_pins_kill_python_mutant(name, tmp_path):
+    before, after = PY_MUTANTS[name]
+    src = open(PY_SRC).read()
+    assert src.count(before) >= 1, "mutation site not found: " + name
+    r = run_pins_on_copy(tmp_path, src.replace(before, after))
     assert r.returncode == 1, "mutant survived the pins: " + name + "\n" + r.stdout[-2000:]

@@ -52,6 +52,45 @@ def test_reduce_equal_replicas_is_exact_multiple(dtype, N):
 
 
 @pytest.mark.parametrize("dtype", [oracle.FP16, oracle.BF16])
+@pytest.mark.parametrize("N", [2, 3, 4, 6, 8])
+def test_reduce_mean_of_equal_replicas_is_the_replica(dtype, N):
+    """A predivide factor D = N turns the sum into the DDP mean, so N equal
+    replicas give back the replica, bit for bit.  The sum N·x is exact in
+    fp32 (a 16-bit code's significand times N <= 8 fits in 24 bits).  For
+    a power of two N the multiplier 1/N is exact too.  For N = 3 and 6,
+    fp32(1/N)·N = 1 + 2^-25 exactly, so the product is x·(1 + 2^-25), which
+    lies less than half an ulp from x and rounds to x."""
+    if N & (N - 1):
+        assert float(oracle.inv_scale(1.0, float(N))) * N == 1.0 + 2.0**-25
+    rng = np.random.default_rng(100 + N)
+    x = rand_codes(rng, 4001, dtype, sigma=1e-2)
+    xf = decode(x, dtype)
+    for S in (1.0, 2.0**10):
+        xs = f32_bits_to_code(xf * np.float32(S), dtype)     # the scaled code each replica holds
+        g, _, of = oracle.reduce([xs] * N, dtype, oracle.inv_scale(S, float(N)))
+        assert of == 0
+        assert np.array_equal(g.astype(np.float64), decode(xs, dtype).astype(np.float64) / S)
+
+
+def test_reduce_predivide_enters_with_the_loss_scale_as_one_product():
+    """Unscale and predivide are one multiply by fp32(1/(S·D)); with S·D a
+    power of two it is exact, so halving S and doubling D changes nothing,
+    and the result is the plain sum divided by S·D."""
+    rng = np.random.default_rng(7)
+    reps = [rand_codes(rng, 2001, oracle.FP16, sigma=50.0) for _ in range(5)]
+    ref = None
+    for S, D in ((1024.0, 4.0), (512.0, 8.0), (4096.0, 1.0)):
+        g, _, _ = oracle.reduce(reps, oracle.FP16, oracle.inv_scale(S, D))
+        if ref is None:
+            ref = g
+            acc = decode(reps[0], oracle.FP16).copy()
+            for r in reps[1:]:
+                acc = np.add(acc, decode(r, oracle.FP16), dtype=np.float32)
+            assert np.array_equal(g.astype(np.float64), acc.astype(np.float64) / 4096.0)
+        assert np.array_equal(g, ref)
+
+
+@pytest.mark.parametrize("dtype", [oracle.FP16, oracle.BF16])
 def test_reduce_matches_numpy_fp32_running_sum(dtype):
     rng = np.random.default_rng(11)
     N, n = 7, 3001
