@@ -72,6 +72,28 @@ def test_world_with_predivide_matches_oracle(case):
         % (rep.norm_rel_err, rep.state_bitwise, rep.cast_max_ulp))
 
 
+HYPER_CASES = [
+    # AdamW settings other than the workloads' defaults, over enough steps
+    # for the bias corrections to move: a common large-model setting, no
+    # first moment and no decay, and a large step with a strong decay
+    dict(lr=1e-3, beta1=0.8, beta2=0.95, eps=1e-6, weight_decay=0.1),
+    dict(lr=3e-4, beta1=0.0, beta2=0.99, eps=1e-8, weight_decay=0.0),
+    dict(lr=0.1, beta1=0.5, beta2=0.5, eps=1e-3, weight_decay=1.0),
+]
+
+
+@pytest.mark.parametrize("hyper", HYPER_CASES,
+                         ids=["lr%g-b%g-%g-eps%g-wd%g" % tuple(h.values()) for h in HYPER_CASES])
+def test_hyper_parameters_match_oracle(hyper):
+    say("hyper-parameters %s" % hyper)
+    spec = parity.Spec(numel=200_003, world_size=4, alignment=128, grad_dtype=BF16,
+                       grad_sigma=1e-2, steps=5, name="hyper",
+                       hp=Hyper(max_grad_norm=1.0, **hyper))
+    rep = parity.run(spec)
+    say("norm rel err %.2e, bitwise state fraction %.6f, cast max ulp %d"
+        % (rep.norm_rel_err, rep.state_bitwise, rep.cast_max_ulp))
+
+
 def test_tiny_workload_matches_oracle():
     w = W.TINY
     say("tiny workload")

@@ -222,13 +222,16 @@ def test_adamw_clip_coefficient_scales_gradient():
 
 
 @pytest.mark.parametrize("coef", [1.0, 0.37])
-def test_adamw_matches_torch_adamw_float64(coef):
+@pytest.mark.parametrize("hyper", [(6e-5, 0.9, 0.999, 1e-8, 0.01), (1e-3, 0.8, 0.95, 1e-6, 0.1),
+                                   (3e-4, 0.0, 0.99, 1e-8, 0.0), (0.1, 0.5, 0.5, 1e-3, 1.0)],
+                         ids=["default", "large-model", "no-first-moment", "strong-decay"])
+def test_adamw_matches_torch_adamw_float64(coef, hyper):
     # From the same fp32 state, one step of torch.optim.AdamW in float64 (a
     # library evaluation of the textbook update) and the oracle's fp32 step
     # agree within the derived bounds, at every t.
     rng = np.random.default_rng(8)
     n = 4000
-    lr, b1, b2, eps, wd = 6e-5, 0.9, 0.999, 1e-8, 0.01
+    lr, b1, b2, eps, wd = hyper
     p = (rng.standard_normal(n) * 0.02).astype(np.float32)
     m = np.zeros(n, np.float32)
     v = np.zeros(n, np.float32)
