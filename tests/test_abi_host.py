@@ -169,16 +169,20 @@ def test_bucket_plan_reports_needed_capacity():
 
 
 # ---------------------------------------------------------------- scaler
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(12))
 def test_loss_scaler_matches_oracle(seed):
+    # random knobs, floors that are and are not powers of two, and overflow
+    # rates from rare to most steps, so runs sit at the floor for a while
     rng = np.random.default_rng(seed)
     window = int(rng.integers(1, 8))
     hyst = int(rng.integers(1, 4))
-    power = int(rng.integers(0, 20))
-    mine = Z.zero_loss_scaler_init(power, window, hyst, 1.0)
-    ref = oracle.LossScaler(power, window, hyst, 1.0)
+    power = int(rng.integers(-4, 20))
+    floor = [1.0, 0.25, 3.0, 256.0][seed % 4]
+    rate = [0.05, 0.2, 0.6][seed % 3]
+    mine = Z.zero_loss_scaler_init(power, window, hyst, floor)
+    ref = oracle.LossScaler(power, window, hyst, floor)
     for _ in range(400):
-        of = bool(rng.random() < 0.2)
+        of = bool(rng.random() < rate)
         assert Z.zero_loss_scaler_update(mine, of) == ref.update(of)
         assert mine.scale == ref.scale
         assert mine.good_steps == ref.good and mine.hysteresis_left == ref.hyst

@@ -297,6 +297,11 @@ def test_scaler_floor_at_min_scale():
     out = run_scaler([True] * 10, power=3, window=5, hysteresis=1, min_scale=1.0)
     assert [o[1] for o in out] == [4, 2, 1, 1, 1, 1, 1, 1, 1, 1]
     assert all(o[0] for o in out)
+    # a floor that is not a power of two: halving stops at it, and growth
+    # doubles from it
+    out = run_scaler([True, True, True, False, False, True, False, False, False, False],
+                     power=3, window=2, hysteresis=1, min_scale=3.0)
+    assert [o[1] for o in out] == [4, 3, 3, 3, 6, 3, 3, 6, 6, 12]
 
 
 def test_scaler_page_defaults():
