@@ -30,6 +30,7 @@ import math
 import os
 import subprocess
 from dataclasses import dataclass, field
+from typing import Optional
 
 import numpy as np
 
@@ -348,7 +349,8 @@ class StepInfo:
 
 def step(replica_flats, dtype: int, numel: int, world_size: int,
          alignment: int, masters, exp_avgs, exp_avg_sqs, full_params,
-         hp: Hyper, t: int, keep_grads: bool = False, cast: bool = True) -> StepInfo:
+         hp: Hyper, t: int, keep_grads: bool = False, cast: bool = True,
+         param_dtype: Optional[int] = None) -> StepInfo:
     """One sharded step for every rank of the world, in rank order.
 
     replica_flats: N flat uint16 gradient buffers (one per data-parallel
@@ -360,15 +362,17 @@ def step(replica_flats, dtype: int, numel: int, world_size: int,
     A step whose reduced gradient holds inf or nan anywhere is skipped: no
     state changes, and the caller must not advance t.  With cast=False the
     full buffer is left alone (for steps whose cast nobody reads).
+    param_dtype is the format of the full buffer, by default the gradients'.
     """
     return step_accumulated([replica_flats], dtype, numel, world_size, alignment, masters,
-                            exp_avgs, exp_avg_sqs, full_params, hp, t, keep_grads, cast)
+                            exp_avgs, exp_avg_sqs, full_params, hp, t, keep_grads, cast,
+                            param_dtype)
 
 
 def step_accumulated(micro_batches, dtype: int, numel: int, world_size: int,
                      alignment: int, masters, exp_avgs, exp_avg_sqs, full_params,
                      hp: Hyper, t: int, keep_grads: bool = False,
-                     cast: bool = True) -> StepInfo:
+                     cast: bool = True, param_dtype: Optional[int] = None) -> StepInfo:
     """One sharded step over an accumulation window of K micro-batches.
 
     micro_batches: K lists of N replica flats (as `step` takes one).  For
@@ -407,14 +411,14 @@ def step_accumulated(micro_batches, dtype: int, numel: int, world_size: int,
         adamw(grads[r], p, m, v, coef, hp.lr, hp.beta1, hp.beta2, hp.eps,
               hp.weight_decay, t)
         if cast:
-            full_params[lo:lo + n] = to_low_precision(p, dtype)
+            full_params[lo:lo + n] = to_low_precision(p, param_dtype or dtype)
     return info
 
 
 def step_local_accumulated(micro_batches, dtype: int, numel: int, world_size: int,
                            alignment: int, masters, exp_avgs, exp_avg_sqs, full_params,
                            hp: Hyper, t: int, keep_grads: bool = False,
-                           cast: bool = True) -> StepInfo:
+                           cast: bool = True, param_dtype: Optional[int] = None) -> StepInfo:
     """One sharded step over an accumulation window of K micro-batches, with
     the window summed before the reduce (the no_sync pattern).
 
@@ -447,5 +451,5 @@ def step_local_accumulated(micro_batches, dtype: int, numel: int, world_size: in
         adamw(grads[r], p, m, v, coef, hp.lr, hp.beta1, hp.beta2, hp.eps,
               hp.weight_decay, t)
         if cast:
-            full_params[lo:lo + n] = to_low_precision(p, dtype)
+            full_params[lo:lo + n] = to_low_precision(p, param_dtype or dtype)
     return info

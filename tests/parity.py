@@ -141,7 +141,6 @@ def run(spec: Spec, device="cuda", check_every_step: bool = True,
     s, P = world.s, spec.numel
     odt = oracle_dtype(spec.grad_dtype)
     podt = oracle_dtype(pdt)
-    assert odt == podt, "the oracle casts into the gradient's format"
     # initial state: masters from the generator, zero moments, canary params
     mkey = ("master", spec.name, spec.seed)
     for k, r in enumerate(world.ranks):
@@ -197,7 +196,8 @@ def run(spec: Spec, device="cuda", check_every_step: bool = True,
         # oracle casts only on the steps whose result is compared.
         ostep = oracle.step_local_accumulated if local else oracle.step_accumulated
         info = ostep(micro, odt, P, spec.world_size, spec.alignment, o_master,
-                     o_m, o_v, o_full, o_hp, t_orc, keep_grads=compare, cast=compare)
+                     o_m, o_v, o_full, o_hp, t_orc, keep_grads=compare, cast=compare,
+                     param_dtype=podt)
         if compare and info.overflow and t_orc > 1:
             # a skipped step leaves the last applied step's cast in place
             s_, _, valid_ = oracle.partition(P, spec.world_size, spec.alignment)

@@ -94,6 +94,20 @@ def test_hyper_parameters_match_oracle(hyper):
         % (rep.norm_rel_err, rep.state_bitwise, rep.cast_max_ulp))
 
 
+@pytest.mark.parametrize("gdt,pdt,scale", [(BF16, FP16, 1.0), (FP16, BF16, 2.0**14)],
+                         ids=["bf16-grads-fp16-params", "fp16-grads-bf16-params"])
+def test_crossed_gradient_and_parameter_formats(gdt, pdt, scale):
+    """The decode follows grad_dtype and the cast follows param_dtype, each
+    on its own."""
+    say("crossed formats %s -> %s" % (gdt, pdt))
+    spec = parity.Spec(numel=150_001, world_size=4, alignment=8, grad_dtype=gdt,
+                       param_dtype=pdt, grad_sigma=1e-3, steps=2, name="crossed",
+                       hp=Hyper(loss_scale=scale))
+    rep = parity.run(spec)
+    say("norm rel err %.2e, bitwise state fraction %.6f, cast max ulp %d"
+        % (rep.norm_rel_err, rep.state_bitwise, rep.cast_max_ulp))
+
+
 def test_tiny_workload_matches_oracle():
     w = W.TINY
     say("tiny workload")

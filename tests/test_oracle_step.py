@@ -372,6 +372,30 @@ def test_each_rank_updates_only_its_part():
     assert (full[P:] == 0xABCD).all()
 
 
+def test_parameter_format_changes_only_the_cast():
+    """The full buffer's format is independent of the gradients': the state
+    after a step is the same, and the buffer holds each format's
+    round-to-nearest-even of the same new masters."""
+    rng = np.random.default_rng(15)
+    P, N, A = 3000, 3, 8
+    s, padded, valid, reps, master = make_world(rng, P, N, N, A, oracle.BF16, 1e-2)
+    out = {}
+    for pdt in (oracle.BF16, oracle.FP16):
+        ps_ = split(master.copy(), N, s)
+        ms = split(np.zeros(padded, np.float32), N, s)
+        vs = split(np.zeros(padded, np.float32), N, s)
+        full = np.full(padded, 0xABCD, np.uint16)
+        oracle.step(reps, oracle.BF16, P, N, A, ps_, ms, vs, full, oracle.Hyper(), t=1,
+                    param_dtype=pdt)
+        out[pdt] = (np.concatenate(ps_), np.concatenate(ms), np.concatenate(vs), full)
+    for a, b in zip(out[oracle.BF16][:3], out[oracle.FP16][:3]):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    p1 = out[oracle.BF16][0][:P]
+    assert np.array_equal(out[oracle.BF16][3][:P], oracle.f32_to_bf16(p1))
+    assert np.array_equal(out[oracle.FP16][3][:P], oracle.f32_to_f16(p1))
+    assert not np.array_equal(out[oracle.BF16][3][:P], out[oracle.FP16][3][:P])
+
+
 @pytest.mark.parametrize("where", [(0, 0), (3, 4999), (2, 2600)])
 def test_overflow_anywhere_skips_every_rank(where):
     rng = np.random.default_rng(14)
