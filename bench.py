@@ -320,32 +320,137 @@ def run_shard13b_local(args, torch, Z, W):
         "reduce_gbps": b_red / (red_ms * 1e-3) / 1e9, "apply_gbps": b_app / (app_ms * 1e-3) / 1e9,
         "step_check": {"norm": info.norm, "clipped": info.clipped, "overflow": info.overflow},
     }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        out["cpu_baseline"] = cpu_baseline_local(args, torch, W, own, peers, K)
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline_shard13b(args, torch, W, st):
-    """The oracle on the first `cpu_sample` elements of the same inputs: the
-    8-replica reduce, clip (norm of the sample), AdamW and bf16 cast."""
+def cpu_record(n, dt, sample):
+    """A `cpu_baseline` entry: the oracle's rate over a sample of n params."""
+    return dict(value=n / dt, unit="params/s", cores=1, kind="oracle",
+                sample="%s; one host thread of %s (%d CPUs available), %.1f s"
+                       % (sample, host_cpu(), len(os.sched_getaffinity(0)), dt))
+
+
+def host_u16(torch, t):
     import numpy as np
-    import oracle
-    n = min(args.cpu_sample, st["valid"])
-    w = st["w"]
-    reps = [g[:n].view(torch.int16).cpu().numpy().view(np.uint16) for g in st["grads"]]
-    # regenerate the initial masters (the timed steps changed the device copy)
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def initial_masters(torch, W, w, n):
+    """The 13B/8 rank's first n initial masters, regenerated on the device
+    (the timed steps changed the device copy)."""
     mdev = torch.empty(n, dtype=torch.float32, device="cuda")
     W.flat_normal(mdev, 0, w.numel, w.master_sigma, W.master_key(w, 0))
-    p = [mdev.cpu().numpy()]
-    m = [np.zeros(n, np.float32)]
-    v = [np.zeros(n, np.float32)]
+    return mdev.cpu().numpy()
+
+
+def cpu_baseline_shard13b(args, torch, W, grads, micro_batches=1):
+    """The oracle on the first n elements of the same inputs: the 8-replica
+    reduce (once per micro-batch of the window: the first sets the fp32
+    slice, the others add to it, over the same gradients as the GPU run),
+    clip (norm of the sample), AdamW and bf16 cast."""
+    import numpy as np
+    import oracle
+    w = W.SHARD_13B_OF_8
+    n = min(args.cpu_sample // (2 if micro_batches > 1 else 1), grads[0].numel())
+    reps = [host_u16(torch, g[:n]) for g in grads]
+    p, m, v = [initial_masters(torch, W, w, n)], [np.zeros(n, np.float32)], [np.zeros(n, np.float32)]
     full = np.zeros(n, np.uint16)
     hp = oracle.Hyper(lr=w.lr, weight_decay=w.weight_decay, max_grad_norm=w.max_grad_norm)
     t0 = time.perf_counter()
-    oracle.step(reps, oracle.BF16, n, 1, 8, p, m, v, full, hp, 1)
+    oracle.step_accumulated([reps] * micro_batches, oracle.BF16, n, 1, 8, p, m, v, full, hp, 1)
     dt = time.perf_counter() - t0
-    return dict(value=n / dt, unit="params/s", cores=1, kind="oracle",
-                sample="first %d elements of rank 0's shard (8 bf16 replicas): reduce, clip, "
-                       "AdamW, bf16 cast; one host thread of %s (%d CPUs available), %.1f s"
-                       % (n, host_cpu(), len(os.sched_getaffinity(0)), dt))
+    what = "reduce" if micro_batches == 1 else "%d reduces (set, then add)" % micro_batches
+    return cpu_record(n, dt, "first %d elements of rank 0's shard (8 bf16 replicas): %s, clip, "
+                             "AdamW, bf16 cast" % (n, what))
+
+
+def cpu_baseline_local(args, torch, W, own, peers, K):
+    """The oracle on a proportional sample of the accumulation-before-the-
+    reduce leg: for n shard elements, the window sum of 8n elements of the
+    rank's own gradient (K micro-batches, the same gradient each time as on
+    the GPU), the 8-way fp32 reduce of its first n sums and the peers'
+    slices, clip, AdamW and bf16 cast."""
+    import numpy as np
+    import oracle
+    w = W.SHARD_13B_OF_8
+    n = min(args.cpu_sample // 2, peers[0].numel())
+    g_own = host_u16(torch, own[:8 * n])
+    peer = [x[:n].cpu().numpy() for x in peers]
+    p, m, v = initial_masters(torch, W, w, n), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    t0 = time.perf_counter()
+    acc = oracle.accumulate_local([g_own] * K, oracle.BF16)
+    g, ss, of = oracle.reduce_f32([acc[:n]] + peer, oracle.inv_scale(1.0))
+    _, _, coef = oracle.clip(ss, w.max_grad_norm)
+    if not of:
+        oracle.adamw(g, p, m, v, coef, w.lr, 0.9, 0.999, 1e-8, w.weight_decay, 1)
+    oracle.to_low_precision(p, oracle.BF16)
+    dt = time.perf_counter() - t0
+    return cpu_record(n, dt, "%d shard elements: the fp32 window sum of %d elements of the "
+                             "rank's own bf16 gradient over %d micro-batches, the 8-way fp32 "
+                             "reduce, clip, AdamW, bf16 cast" % (n, 8 * n, K))
+
+
+def cpu_baseline_ragged(args, torch, W, r):
+    """The oracle on the first tensors of the ragged workload, up to about
+    `cpu_sample` / 2 params: each of the 8 replicas' tensors flattened into
+    its flat buffer (contiguous gradients), then the step of all 8 ranks of
+    that smaller flat model (reduce, clip, AdamW, bf16 cast)."""
+    import numpy as np
+    import oracle
+    w = W.RAGGED_2000
+    slots, pools = r["slots"], r["pools"]
+    T, n = 0, 0
+    while T < len(slots) and (T == 0 or n + slots[T].numel <= args.cpu_sample // 2):
+        n += slots[T].numel
+        T += 1
+    s, padded, _ = oracle.partition(n, w.world_size, w.alignment)
+    tensors = [[host_u16(torch, pool[x.offset + k + 1:x.offset + k + 1 + x.numel])
+                for k, x in enumerate(slots[:T])] for pool in pools]
+    rng = np.random.default_rng(0)
+    p = [(rng.standard_normal(s) * w.master_sigma).astype(np.float32) for _ in range(w.world_size)]
+    m = [np.zeros(s, np.float32) for _ in range(w.world_size)]
+    v = [np.zeros(s, np.float32) for _ in range(w.world_size)]
+    full = np.zeros(padded, np.uint16)
+    hp = oracle.Hyper(lr=w.lr, weight_decay=w.weight_decay, max_grad_norm=w.max_grad_norm)
+    t0 = time.perf_counter()
+    flats = [oracle.flatten(tt, int(2e8), padded) for tt in tensors]
+    oracle.step(flats, oracle.BF16, n, w.world_size, w.alignment, p, m, v, full, hp, 1)
+    dt = time.perf_counter() - t0
+    return cpu_record(n, dt, "the first %d of the %d tensors (%d params): 8 replicas flattened, "
+                             "then the step of 8 ranks (reduce, clip, AdamW, bf16 cast)"
+                      % (T, len(slots), n))
+
+
+def cpu_baseline_repartition(args, torch, src_world):
+    """The oracle re-cutting three fp32 state arrays of a 4 x `cpu_sample`-
+    param model (about the whole ragged model) from 8 ranks to 3, the slices
+    taken from the device state."""
+    import oracle
+    n = min(4 * args.cpu_sample, src_world.s * 8)
+    s, _, valid = oracle.partition(n, 8, 128)
+    arrays = [[src_world.state(k)[f][:s].cpu().numpy() for k in range(8)] for f in range(3)]
+    t0 = time.perf_counter()
+    for sl in arrays:
+        oracle.repartition(sl, n, 8, 128, 3, 128)
+    dt = time.perf_counter() - t0
+    return cpu_record(n, dt, "master, exp_avg and exp_avg_sq of a %d-param model re-partitioned "
+                             "from 8 ranks to 3" % n)
+
+
+def cpu_baseline_zero3(args, torch, shards):
+    """The oracle gathering the first 8 x `cpu_sample` params of a model
+    sharded over 8 ranks from their shards (slices of the device shards)."""
+    import oracle
+    n = min(8 * args.cpu_sample, shards[0].numel() * 8)
+    s, _, _ = oracle.partition(n, 8, 128)
+    host = [host_u16(torch, x[:s]) for x in shards]
+    t0 = time.perf_counter()
+    oracle.gather(host, n, 8, 128, 0, n)
+    dt = time.perf_counter() - t0
+    return cpu_record(n, dt, "%d bf16 params gathered from 8 rank shards" % n)
 
 
 def host_cpu() -> str:
@@ -426,10 +531,11 @@ def run_ragged(args, torch, Z, W):
     res = world.result()
     return dict(P=P, N=N, s=world.s, flat_ms=flat_ms, step_ms=step_ms,
                 ms=ev[0][0].elapsed_time(ev[-1][2]) / K, n_buckets=len(buckets),
-                norm=res.norm, clipped=res.clipped, overflow=res.overflow)
+                norm=res.norm, clipped=res.clipped, overflow=res.overflow,
+                slots=slots, pools=pools)
 
 
-def report_ragged(args, r, W):
+def report_ragged(args, r, W, torch):
     P, N = r["P"], r["N"]
     flat_bytes = N * P * 4                   # each replica: 2 B read + 2 B written per element
     step_bytes = P * (2 * N + 34)
@@ -454,6 +560,9 @@ def report_ragged(args, r, W):
                      "frac": flat_gbps / HBM_PEAK_GBPS, "traffic": None},
         "step_check": {"norm": r["norm"], "clipped": r["clipped"], "overflow": r["overflow"]},
     }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        out["cpu_baseline"] = cpu_baseline_ragged(args, torch, W, r)
     print(json.dumps(out), flush=True)
 
 
@@ -519,6 +628,9 @@ def run_repartition(args, torch, Z, W):
                             "load_s": t_load, "load_gbps": fbytes / t_load / 1e9,
                             "where": "temporary directory on the host"},
     }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        out["cpu_baseline"] = cpu_baseline_repartition(args, torch, src)
     print(json.dumps(out), flush=True)
 
 
@@ -587,6 +699,9 @@ def run_offload(args, torch, Z, W):
         "roofline": None,
         "step_check": {"norm": info.norm, "clipped": info.clipped, "overflow": info.overflow},
     }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        out["cpu_baseline"] = cpu_baseline_shard13b(args, torch, W, grads)
     print(json.dumps(out), flush=True)
 
 
@@ -640,6 +755,9 @@ def run_zero3(args, torch, Z, W):
                      "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": gbps / HBM_PEAK_GBPS, "traffic": measured_traffic("zero3")},
     }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        out["cpu_baseline"] = cpu_baseline_zero3(args, torch, shards)
     print(json.dumps(out), flush=True)
 
 
@@ -699,7 +817,7 @@ def main():
         calibrate_copy(torch, args.calibrate_copy)
         return
     if args.workload == "ragged":
-        report_ragged(args, run_ragged(args, torch, Z, W), W)
+        report_ragged(args, run_ragged(args, torch, Z, W), W, torch)
         return
     if args.workload == "repartition":
         run_repartition(args, torch, Z, W)
@@ -767,9 +885,10 @@ def main():
     cc["frac_of_peak"] = cc["gbps"] / HBM_PEAK_GBPS
     cc["roofline_kernel_frac_of_copy"] = roofline["achieved"] / cc["gbps"]
     out["copy_ceiling"] = cc
-    if not args.no_cpu_baseline and args.micro_batches == 1:
+    if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
-        out["cpu_baseline"] = cpu_baseline_shard13b(args, torch, W, r["st"])
+        out["cpu_baseline"] = cpu_baseline_shard13b(args, torch, W, r["st"]["grads"],
+                                                    args.micro_batches)
     print(json.dumps(out), flush=True)
 
 

@@ -147,6 +147,22 @@ def bucket_plan(sizes, bucket_size: int):
     return off[:len(n)].copy(), bof[:len(n)].copy(), nb
 
 
+def flatten(tensors, bucket_size: int, padded_numel: int) -> np.ndarray:
+    """contiguous_gradients ("ZeRO技术解析" §5.2): one replica's per-tensor
+    16-bit gradients laid end to end, in order and with no gaps, at the
+    offsets of the bucket plan, then zeros up to the padded length.  The
+    buckets only group the copies; they do not move anything."""
+    tensors = [np.ascontiguousarray(t, dtype=np.uint16) for t in tensors]
+    offsets, _, _ = bucket_plan([t.size for t in tensors], bucket_size)
+    end = int(offsets[-1]) + tensors[-1].size if tensors else 0
+    if end > padded_numel:
+        raise ValueError("the tensors hold more than padded_numel elements")
+    flat = np.zeros(padded_numel, dtype=np.uint16)
+    for t, off in zip(tensors, offsets):
+        flat[int(off):int(off) + t.size] = t
+    return flat
+
+
 # ------------------------------------------------------------ number formats
 def f32_to_f16(x: np.ndarray) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float32)

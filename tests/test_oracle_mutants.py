@@ -85,6 +85,8 @@ PY_MUTANTS = {
     "repartition_ranks_reversed": ("for r in range(from_world)] +",
                                    "for r in reversed(range(from_world))] +"),
     "gather_one_past_the_end": ("return flat[lo:hi].copy()", "return flat[lo:hi + 1].copy()"),
+    "flatten_one_element_late": ("flat[int(off):int(off) + t.size] = t",
+                                 "flat[int(off) + 1:int(off) + 1 + t.size] = t"),
 }
 
 

@@ -165,3 +165,30 @@ def test_bucket_plan_hand_example():
     assert nb == 4
     with pytest.raises(ValueError):
         oracle.bucket_plan([1, 2], 0)
+
+
+def test_flatten_hand_example():
+    # three tensors of 2, 0 and 3 codes, padded to 8: end to end, then zeros
+    t = [np.array([7, 8], np.uint16), np.zeros(0, np.uint16), np.array([1, 2, 3], np.uint16)]
+    assert oracle.flatten(t, 4, 8).tolist() == [7, 8, 1, 2, 3, 0, 0, 0]
+    assert oracle.flatten([], 4, 3).tolist() == [0, 0, 0]
+    with pytest.raises(ValueError):
+        oracle.flatten(t, 4, 4)
+
+
+def test_flatten_places_every_tensor_at_its_running_offset():
+    # each tensor's codes sit at the sum of the sizes before it, whatever the
+    # bucket size; everything after the last tensor is zero
+    rng = np.random.default_rng(4)
+    for trial in range(50):
+        sizes = [int(x) for x in rng.integers(0, 300, size=int(rng.integers(1, 40)))]
+        t = [rng.integers(1, 65536, n).astype(np.uint16) for n in sizes]
+        padded = sum(sizes) + int(rng.integers(0, 50))
+        flats = [oracle.flatten(t, cap, padded) for cap in (1, 97, 10**6)]
+        for f in flats[1:]:
+            assert np.array_equal(f, flats[0])
+        pos = 0
+        for x in t:
+            assert np.array_equal(flats[0][pos:pos + x.size], x)
+            pos += x.size
+        assert not flats[0][pos:].any()
