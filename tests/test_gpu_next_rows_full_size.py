@@ -16,6 +16,13 @@ configurations, the benchmark times them.
   elements equal the generator's values at their flat index, every new
   rank's real elements equal the old slices laid end to end, and the
   padding is zero.
+- Accumulation per micro-batch (`--micro-batches 4`): rank 0 of the 13B/8
+  workload reduces the 8 replicas 4 times into its fp32 slice (the first
+  sets it, the others add), over the same gradients each time as the
+  bench repeats them, then combines and applies.  The oracle's window over
+  every element of the shard (its norm) and at a structural sample (the
+  reduced gradient and AdamW) decide; the whole slice equals the window
+  summed again in fp32 on the device, and the cast and canary hold.
 - Accumulation before the reduce (`--micro-batches 4 --accumulation
   local`): the rank's own 13e9-element gradient summed 4 times in fp32,
   then one reduce of its shard over 8 fp32 replicas.  The oracle's window
@@ -275,4 +282,106 @@ def test_local_accumulation_13b_in_bench_configuration():
         assert bool((full[s + a:s + b] == parity.CANARY).all()), "write outside the slice"
     say("local accumulation matches: norm %.6f (oracle %.6f)" % (info.norm, onorm))
     del own, acc, peers, master, m, v, full, ws, buf16, buf32
+    _free()
+
+
+# ---------------------------------------------- accumulation per micro-batch
+def test_reduced_accumulation_13b_in_bench_configuration():
+    w = W.SHARD_13B_OF_8
+    part = Z.zero_partition(w.numel, w.world_size, w.alignment)
+    s, K = part.shard_numel, 4
+    n = Z.zero_partition_valid_numel(part, 0)
+    nrep = w.world_size
+    gkey = lambda i: W.grad_key(w, 0, 0, i)
+    say("accumulation per micro-batch 13B/8: s=%d, %d replicas, window of %d" % (s, nrep, K))
+    grads = []
+    for i in range(nrep):
+        g = torch.empty(s, dtype=torch.bfloat16, device="cuda")
+        W.flat_normal(g, 0, w.numel, w.grad_sigma, gkey(i))
+        grads.append(g)
+    master = torch.empty(s, dtype=torch.float32, device="cuda")
+    W.flat_normal(master, 0, w.numel, w.master_sigma, W.master_key(w, 0))
+    m = torch.zeros(s, dtype=torch.float32, device="cuda")
+    v = torch.zeros(s, dtype=torch.float32, device="cuda")
+    full = torch.full((part.padded_numel,), parity.CANARY, dtype=torch.int16, device="cuda")
+    ws = torch.empty(Z.zero_shard_workspace_bytes(s), dtype=torch.uint8, device="cuda")
+    hp = Hyper(lr=w.lr, weight_decay=w.weight_decay, max_grad_norm=w.max_grad_norm)
+
+    def args(accumulate):
+        return Z.StepArgs(world_size=w.world_size, rank=0, shard_numel=s, valid_numel=n,
+                          replica_grads=grads, master=master, exp_avg=m, exp_avg_sq=v,
+                          full_params=full.view(torch.bfloat16), workspace=ws, lr=hp.lr,
+                          weight_decay=hp.weight_decay, step=1, max_grad_norm=hp.max_grad_norm,
+                          accumulate=accumulate)
+
+    # the bench's calls: K - 1 passes into the slice, then the step that adds the last
+    for j in range(K - 1):
+        Z.zero_shard_accumulate(args(j > 0))
+    info = Z.zero_shard_step(args(True), want_info=True)
+
+    # the oracle's window over every element of the shard, chunk by chunk in
+    # index order; each chunk's last micro-batch carries the running norm
+    say("oracle: %d reduces over %d elements" % (K, n))
+    rng = np.random.default_rng(12)
+    sample = parity.structural_sample(n, rng)
+    inv = oracle.inv_scale(1.0)
+    ss, of = 0.0, 0
+    codes = [np.empty(sample.size, np.uint16) for _ in range(nrep)]
+    gens = [parity.gen_chunks(0, n, w.numel, w.grad_sigma, gkey(i), torch.bfloat16)
+            for i in range(nrep)]
+    for k, parts in enumerate(zip(*gens)):
+        a, b = parts[0][0], parts[0][1]
+        reps = [x[2] for x in parts]
+        g_chunk, _, _ = oracle.reduce(reps, oracle.BF16, inv)
+        for j in range(1, K):
+            last = j == K - 1
+            r_ss, r_of = oracle.reduce_accumulate(reps, oracle.BF16, inv, g_chunk,
+                                                  ss if last else 0.0, of if last else 0)
+            if last:
+                ss, of = r_ss, r_of
+        sel = (sample >= a) & (sample < b)
+        for i in range(nrep):
+            codes[i][sel] = reps[i][sample[sel] - a]
+        if k % 8 == 0:
+            say("  [%d, %d) done" % (a, b))
+    assert of == 0 and info.overflow == 0
+    applies, onorm, ocoef = oracle.clip(ss, hp.max_grad_norm)
+    assert bool(info.clipped) == applies
+    assert abs(info.norm - onorm) <= parity.RTOL_NORM * onorm, (info.norm, onorm)
+
+    # at the sample: the window's reduced gradient, AdamW and the cast
+    o_g, _, _ = oracle.reduce(codes, oracle.BF16, inv)
+    for j in range(1, K):
+        oracle.reduce_accumulate(codes, oracle.BF16, inv, o_g)
+    gdev = ws[:4 * s].view(torch.float32)
+    parity.assert_bitwise("window's reduced grad (sample)", parity.take(gdev, sample).numpy(), o_g)
+    o_p = parity.gather_generated(sample, 0, w.numel, w.master_sigma, W.master_key(w, 0),
+                                  torch.float32, n).copy()
+    o_m = np.zeros(sample.size, np.float32)
+    o_v = np.zeros(sample.size, np.float32)
+    oracle.adamw(o_g, o_p, o_m, o_v, ocoef, hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, 1)
+    for name, dev_t, ref in (("master", master, o_p), ("exp_avg", m, o_m), ("exp_avg_sq", v, o_v)):
+        parity.assert_rel("%s (sample)" % name, parity.take(dev_t, sample).numpy(), ref,
+                          parity.RTOL_STATE)
+    parity.assert_cast("cast (sample)", parity.take(full, sample).numpy().view(np.uint16),
+                       oracle.f32_to_bf16(o_p))
+
+    # whole-buffer properties: the window summed again in fp32 (replica
+    # order, one unscale per micro-batch, micro-batches added in order), the
+    # cast of every element, and nothing written outside the rank's slice
+    for a, b in _chunked(n):
+        x = grads[0][a:b].float()
+        for i in range(1, nrep):
+            x += grads[i][a:b].float()
+        x *= float(inv)
+        win = x.clone()
+        for j in range(1, K):
+            win += x
+        assert torch.equal(win, gdev[a:b]), "window differs in [%d, %d)" % (a, b)
+        assert torch.equal(full[a:b], master[a:b].to(torch.bfloat16).view(torch.int16))
+    del x, win
+    for a, b in _chunked(part.padded_numel - s, 1 << 30):
+        assert bool((full[s + a:s + b] == parity.CANARY).all()), "write outside the slice"
+    say("accumulation per micro-batch matches: norm %.6f (oracle %.6f)" % (info.norm, onorm))
+    del grads, master, m, v, full, ws
     _free()
