@@ -16,6 +16,9 @@ configurations, the benchmark times them.
   elements equal the generator's values at their flat index, every new
   rank's real elements equal the old slices laid end to end, and the
   padding is zero.
+- Two state sets (`--state-buffers 2`): the 13B/8 step read from one set
+  and written to the other equals the same step in place, bit for bit over
+  every element of the state and of the cast slice.
 - Accumulation per micro-batch (`--micro-batches 4`): rank 0 of the 13B/8
   workload reduces the 8 replicas 4 times into its fp32 slice (the first
   sets it, the others add), over the same gradients each time as the
@@ -384,4 +387,54 @@ def test_reduced_accumulation_13b_in_bench_configuration():
         assert bool((full[s + a:s + b] == parity.CANARY).all()), "write outside the slice"
     say("accumulation per micro-batch matches: norm %.6f (oracle %.6f)" % (info.norm, onorm))
     del grads, master, m, v, full, ws
+    _free()
+
+
+# --------------------------------------------------------- two state sets
+def test_two_state_sets_13b_equal_in_place():
+    w = W.SHARD_13B_OF_8
+    part = Z.zero_partition(w.numel, w.world_size, w.alignment)
+    s = part.shard_numel
+    n = Z.zero_partition_valid_numel(part, 0)
+    say("two state sets 13B/8: s=%d" % s)
+    grads = []
+    for i in range(w.world_size):
+        g = torch.empty(s, dtype=torch.bfloat16, device="cuda")
+        W.flat_normal(g, 0, w.numel, w.grad_sigma, W.grad_key(w, 0, 0, i))
+        grads.append(g)
+    a_p = torch.empty(s, dtype=torch.float32, device="cuda")
+    W.flat_normal(a_p, 0, w.numel, w.master_sigma, W.master_key(w, 0))
+    # a state with nonzero moments: one step in place first
+    a_m = torch.zeros(s, dtype=torch.float32, device="cuda")
+    a_v = torch.zeros(s, dtype=torch.float32, device="cuda")
+    full = torch.zeros(part.padded_numel, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(Z.zero_shard_workspace_bytes(s), dtype=torch.uint8, device="cuda")
+    hp = Hyper(lr=w.lr, weight_decay=w.weight_decay, max_grad_norm=w.max_grad_norm)
+
+    def args(t, p, m, v, out=None):
+        a = Z.StepArgs(world_size=w.world_size, rank=0, shard_numel=s, valid_numel=n,
+                       replica_grads=grads, master=p, exp_avg=m, exp_avg_sq=v,
+                       full_params=full, workspace=ws, lr=hp.lr, weight_decay=hp.weight_decay,
+                       step=t, max_grad_norm=hp.max_grad_norm)
+        if out is not None:
+            a.master_out, a.exp_avg_out, a.exp_avg_sq_out = out
+        return a
+
+    Z.zero_shard_step(args(1, a_p, a_m, a_v))
+    # step 2 from set A into set B, then the same step in place on A
+    b = tuple(torch.full((s,), 7.0, dtype=torch.float32, device="cuda") for _ in range(3))
+    i1 = Z.zero_shard_step(args(2, a_p, a_m, a_v, b), want_info=True)
+    cast_b = full[:s].clone()
+    full[:s].zero_()
+    i2 = Z.zero_shard_step(args(2, a_p, a_m, a_v), want_info=True)
+    assert i1.overflow == 0 and (i1.norm, i1.coef) == (i2.norm, i2.coef)
+    for name, x, y in zip(("master", "exp_avg", "exp_avg_sq"), b, (a_p, a_m, a_v)):
+        for lo, hi in _chunked(n):
+            assert torch.equal(x[lo:hi].view(torch.int32), y[lo:hi].view(torch.int32)), \
+                "%s differs in [%d, %d)" % (name, lo, hi)
+        assert bool((x[n:] == 7.0).all()), "%s: the other set's padding was written" % name
+    for lo, hi in _chunked(s):
+        assert torch.equal(cast_b[lo:hi].view(torch.int16), full[lo:hi].view(torch.int16))
+    say("two state sets equal in place: norm %.6f" % i1.norm)
+    del grads, a_p, a_m, a_v, b, full, ws, cast_b
     _free()
