@@ -170,7 +170,9 @@ typedef struct {
     int64_t valid_numel;      /* real elements of this rank's shard        */
     int32_t grad_dtype;       /* ZERO_FP16, ZERO_BF16, or ZERO_FP32 for
                                  replicas summed by zero_accumulate_local */
-    int32_t param_dtype;      /* ZERO_FP16 or ZERO_BF16                    */
+    int32_t param_dtype;      /* ZERO_FP16 or ZERO_BF16, independent of
+                                 grad_dtype: the decode follows grad_dtype,
+                                 the cast param_dtype                     */
     int32_t n_replicas;       /* gradients summed, 1..ZERO_MAX_REPLICAS    */
     /* 0: pass 1 sets the workspace's fp32 gradient slice to this reduce's
      * result; 1: it adds the result to the slice already there (micro-batch
