@@ -98,7 +98,10 @@ def measured_traffic(workload: str):
         rec = json.load(open(traffic_file(workload)))
     except (OSError, ValueError):
         return None
-    if rec.get("library_code_sha256_16") != kernel_hash() or rec.get("workload") != workload:
+    here = kernel_hash()
+    if rec.get("library_code_sha256_16") != here or rec.get("workload") != workload:
+        log("traffic: the %s counter record was taken on library code %s, this library is %s; "
+            "roofline.traffic is null" % (workload, rec.get("library_code_sha256_16"), here))
         return None
     return rec.get("roofline_traffic")
 
