@@ -95,3 +95,27 @@ def test_layer_walk_with_prefetch(bucket, max_live):
                                             off + w.tensor_sizes[t]))
         seen.append(t)
     assert seen == list(range(len(w.tensor_sizes)))
+
+
+def test_layer_walk_with_a_slow_caller_keeps_every_layer():
+    """The caller's stream may still be reading a bucket while later buckets
+    are gathered on the side stream.  Each layer is copied on the caller's
+    stream only after a bounded GPU sleep, with no host wait inside the
+    walk; every copy must equal its range."""
+    L, n = 40, 1 << 16
+    sizes = [n] * L
+    part = Z.zero_partition(L * n, 4, 128)
+    s = part.shard_numel
+    shards = [torch.randint(-32768, 32767, (s,), dtype=torch.int16, device="cuda")
+              .view(torch.bfloat16) for _ in range(4)]
+    host = [parity.u16(x) for x in shards]
+    say("slow caller: %d layers of %d, one layer per bucket, two live" % (L, n))
+    g = LayerGatherer(part, shards, sizes, n, 2 * n)
+    copies = []
+    for t, params in g.forward():
+        torch.cuda._sleep(1_000_000)            # about half a millisecond of GPU time
+        copies.append(params.clone())
+    torch.cuda.synchronize()
+    for t, c in enumerate(copies):
+        parity.assert_bitwise("layer %d" % t, parity.u16(c),
+                              oracle.gather(host, L * n, 4, 128, t * n, (t + 1) * n))

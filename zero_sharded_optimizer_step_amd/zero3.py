@@ -57,7 +57,12 @@ class LayerGatherer:
         def issue():
             nonlocal nxt, live
             lo, hi, _, _ = self.buckets[nxt]
-            buf = torch.empty(hi - lo, dtype=self.dtype, device=self.shards[0].device)
+            # Allocated on the side stream, which writes it: once the caller
+            # is done (record_stream below), torch's allocator reuses the
+            # memory only after the caller's stream has passed its last
+            # read, so a later gather cannot overwrite a bucket still in use.
+            with torch.cuda.stream(self.side):
+                buf = torch.empty(hi - lo, dtype=self.dtype, device=self.shards[0].device)
             zero_gather_params(self.part, self.shards, self.dtype, lo, hi, buf, self.side)
             ev = torch.cuda.Event()
             ev.record(self.side)
