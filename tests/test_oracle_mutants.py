@@ -12,6 +12,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import pytest
 
@@ -55,21 +56,20 @@ MUTANTS = {
 }
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_pins_kill_mutant(name, tmp_path):
+def run_c_mutant(name, tmp_path):
     before, after = MUTANTS[name]
     src = open(SRC).read()
     # a site shared by the plain and the accumulating reduce is mutated in both
-    assert src.count(before) >= 1, "mutation site not found: " + name
+    if src.count(before) < 1:
+        return None
     mutant_src = tmp_path / "zero_oracle.c"
     mutant_src.write_text(src.replace(before, after))
     lib = str(tmp_path / "liboracle_mutant.so")
     oracle.compile_oracle(str(mutant_src), lib, strict=False)
     env = dict(os.environ, ZERO_ORACLE_LIB=lib)
-    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "-W", "ignore::RuntimeWarning"] + PINS,
-                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
-    assert r.returncode == 1, "mutant survived the pins: " + name + "\n" + r.stdout[-2000:]
+    return subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                           "-W", "ignore::RuntimeWarning"] + PINS,
+                          cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
 
 
 PY_SRC = os.path.join(ROOT, "oracle", "__init__.py")
@@ -107,15 +107,42 @@ def run_pins_on_copy(tmp_path, py_src):
                           cwd=str(root), env=env, capture_output=True, text=True, timeout=600)
 
 
-def test_pins_pass_on_an_unmutated_copy(tmp_path):
-    r = run_pins_on_copy(tmp_path, open(PY_SRC).read())
+def run_python_mutant(name, tmp_path):
+    before, after = PY_MUTANTS[name]
+    src = open(PY_SRC).read()
+    if src.count(before) < 1:
+        return None
+    return run_pins_on_copy(tmp_path, src.replace(before, after))
+
+
+@pytest.fixture(scope="module")
+def pin_runs(tmp_path_factory):
+    """Every mutant's pin run (and one on an unmutated copy), several at a
+    time: each is an independent subprocess in its own directory."""
+    jobs = {("c", n): run_c_mutant for n in MUTANTS}
+    jobs.update({("py", n): run_python_mutant for n in PY_MUTANTS})
+    jobs[("py", None)] = lambda _, tmp: run_pins_on_copy(tmp, open(PY_SRC).read())
+    workers = max(1, min(8, len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(workers) as pool:
+        futs = {k: pool.submit(f, k[1], tmp_path_factory.mktemp("%s_%s" % (k[0], k[1])))
+                for k, f in jobs.items()}
+        return {k: f.result() for k, f in futs.items()}
+
+
+def test_pins_pass_on_an_unmutated_copy(pin_runs):
+    r = pin_runs[("py", None)]
     assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
 
 
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_kill_mutant(name, pin_runs):
+    r = pin_runs[("c", name)]
+    assert r is not None, "mutation site not found: " + name
+    assert r.returncode == 1, "mutant survived the pins: " + name + "\n" + r.stdout[-2000:]
+
+
 @pytest.mark.parametrize("name", sorted(PY_MUTANTS))
-def test_pins_kill_python_mutant(name, tmp_path):
-    before, after = PY_MUTANTS[name]
-    src = open(PY_SRC).read()
-    assert src.count(before) >= 1, "mutation site not found: " + name
-    r = run_pins_on_copy(tmp_path, src.replace(before, after))
+def test_pins_kill_python_mutant(name, pin_runs):
+    r = pin_runs[("py", name)]
+    assert r is not None, "mutation site not found: " + name
     assert r.returncode == 1, "mutant survived the pins: " + name + "\n" + r.stdout[-2000:]
