@@ -1,0 +1,56 @@
+"""Host-side checks of the benchmark (CPU only): the one-GPU refusal, and
+the committed HBM counter records against the library as built."""
+import glob
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+RECORDS = sorted(glob.glob(os.path.join(ROOT, "profiles", "traffic_*.json")))
+
+
+@pytest.mark.parametrize("path", RECORDS, ids=[os.path.basename(p) for p in RECORDS])
+def test_traffic_record_matches_the_built_library(path):
+    """Each record names its workload and the library code it was counted
+    on; while the built library has that code the bench reports the
+    record's traffic, which stays within 1 % of the algorithmic bytes."""
+    import bench
+    rec = json.load(open(path))
+    assert os.path.basename(path) == "traffic_%s.json" % rec["workload"]
+    if rec["library_code_sha256_16"] != bench.kernel_hash():
+        pytest.skip("counted on library code %s; this build is %s"
+                    % (rec["library_code_sha256_16"], bench.kernel_hash()))
+    assert bench.measured_traffic(rec["workload"]) == rec["roofline_traffic"]
+    assert abs(rec["roofline_traffic"] / algorithmic_bytes(rec) - 1.0) < 0.01
+
+
+def algorithmic_bytes(rec):
+    """The bytes the roofline kernel must move per unit the record counts,
+    from the workloads' sizes."""
+    import zero_sharded_optimizer_step_amd as Z
+    from zero_sharded_optimizer_step_amd import workloads as W
+    if "algorithmic_bytes_per_launch" in rec:
+        return rec["algorithmic_bytes_per_launch"]
+    w = W.SHARD_13B_OF_8
+    if rec["workload"] == "shard13b":        # AdamW + cast: 16 B read, 14 B written
+        part = Z.zero_partition(w.numel, w.world_size, w.alignment)
+        return 30 * Z.zero_partition_valid_numel(part, 0)
+    if rec["workload"] == "zero3":           # every parameter read and written once
+        return 4 * w.numel
+    if rec["workload"] == "repartition":     # 3 fp32 arrays: read once, new padded written
+        P = W.RAGGED_2000.numel
+        return 3 * (4 * P + 4 * Z.zero_partition(P, 3, 128).padded_numel)
+    raise AssertionError("no algorithmic figure for " + rec["workload"])
