@@ -140,12 +140,15 @@ int zero_bucket_plan(const int64_t* tensor_numel, int32_t n_tensors,
  * For each t < n_tensors, copies tensor_numel = slots[t].numel 16-bit
  * values from src_dev[t] (device, 2-byte aligned, any offset) to flat
  * elements [slots[t].offset, +numel) of flat_dev (device, 16-byte aligned),
- * then writes zeros over [end of the last slot, flat_numel) -- the
- * partition padding when flat_numel is the padded size.  slots (host) must
- * have non-decreasing, non-overlapping ranges inside [0, flat_numel);
- * src_dev is a host array of device pointers.  A bucket at a time may be
- * flattened by passing its slots and flat_numel = bucket end (no padding
- * is then written).  The sources must not overlap flat_dev.  Bit copy:
+ * writes zeros over any gap between the end of slot t - 1 and the start of
+ * slot t, then over [end of the last slot, flat_numel) -- the partition
+ * padding when flat_numel is the padded size.  Elements before the first
+ * slot are not touched.  So every element the step may read, from the
+ * first slot on, holds a gradient or zero.  slots (host) must have
+ * non-decreasing, non-overlapping ranges inside [0, flat_numel); src_dev is
+ * a host array of device pointers.  A bucket at a time may be flattened by
+ * passing its slots and flat_numel = bucket end (no padding is then
+ * written).  The sources must not overlap flat_dev.  Bit copy:
  * dtype (ZERO_FP16 / ZERO_BF16) is checked, the values are not
  * interpreted.
  * Errors: NULL pointers, bad dtype, slots out of order or out of range ->
@@ -366,9 +369,10 @@ int zero_loss_scaler_update(zero_loss_scaler_t* st, int32_t overflow,
  * GPU the shards may be slices of one buffer; across GPUs they would be
  * peer-mapped pointers.  dst must not overlap the shards.  Bit copy: dtype
  * is checked, values are not read.
- * Errors: NULL arguments, lo < 0, hi < lo, hi > numel, bad dtype, a NULL
- * shard that [lo, hi) meets -> ZERO_EINVAL; misaligned dst or shard ->
- * ZERO_EALIGN; launch -> ZERO_EDEVICE. */
+ * Errors: NULL arguments, a partition that zero_partition does not
+ * reproduce from its numel, world_size and alignment, lo < 0, hi < lo,
+ * hi > numel, bad dtype, a NULL shard that [lo, hi) meets -> ZERO_EINVAL;
+ * misaligned dst or shard -> ZERO_EALIGN; launch -> ZERO_EDEVICE. */
 int zero_gather_params(const zero_partition_t* p, const void* const* shards, int32_t dtype,
                        int64_t lo, int64_t hi, void* dst, void* stream);
 
@@ -486,12 +490,46 @@ int zero_ckpt_header_check(const zero_ckpt_header_t* h, uint64_t file_bytes,
  * elements each (16-byte aligned).  Every flat element i < numel is copied
  * from old rank i / from->shard_numel to new rank i / to->shard_numel; the
  * new slices' padding is zeroed.  Source and destination must not
- * overlap.  Device work only, queued on `stream`.
- * Errors: NULL arguments, different numel, a NULL pointer for a rank that
- * holds elements -> ZERO_EINVAL; misaligned pointers -> ZERO_EALIGN;
- * launch -> ZERO_EDEVICE. */
+ * overlap.  Device work only, queued on `stream`; the copies follow
+ * zero_repartition_plan.
+ * Errors: NULL arguments, different numel, a partition that zero_partition
+ * does not reproduce from its numel, world_size and alignment, a NULL
+ * pointer for a rank that holds elements -> ZERO_EINVAL; misaligned
+ * pointers -> ZERO_EALIGN; launch -> ZERO_EDEVICE. */
 int zero_repartition(const zero_partition_t* from, const float* const* src_dev,
                      const zero_partition_t* to, float* const* dst_dev, void* stream);
+
+/* Where new rank `new_rank` of partition *to finds its real elements under
+ * partition *from of the same numel: the read plan of an elastic resume
+ * ([P2] practice notes: the saved shard information lets a run continue
+ * on another world).  zero_repartition copies along these pieces on the
+ * device; a checkpoint reader follows them to seek in the old ranks' files.
+ *
+ * Piece q moves `count` elements from element old_offset of old rank
+ * old_rank's slice to element new_offset of the new rank's slice.  The
+ * pieces come in ascending new_offset, old_rank and new_offset both
+ * increase from piece to piece, and together they cover the new rank's
+ * real elements [0, valid_numel) exactly once; each lies inside its old
+ * rank's real elements.  The new rank's padding [valid_numel, shard_numel)
+ * is in no piece (a reader zeroes it).  At most from->world_size pieces.
+ * pieces: host array of piece_cap entries (out); *n_pieces receives the
+ * count (0 for a rank with no real elements).  When it exceeds piece_cap
+ * the call fails with ZERO_ESIZE and *n_pieces holds the capacity needed.
+ * Errors: NULL from, to or n_pieces, pieces NULL with piece_cap > 0,
+ * piece_cap < 0, a partition that zero_partition does not reproduce from
+ * its numel, world_size and alignment, different numel, new_rank out of
+ * range -> ZERO_EINVAL.  Host only. */
+typedef struct {
+    int64_t old_offset;       /* first element, inside the old rank's slice */
+    int64_t new_offset;       /* first element, inside the new rank's slice */
+    int64_t count;            /* elements, > 0                               */
+    int32_t old_rank;         /* rank of *from whose slice holds them        */
+    int32_t reserved;         /* 0                                           */
+} zero_repartition_piece_t;
+
+int zero_repartition_plan(const zero_partition_t* from, const zero_partition_t* to,
+                          int32_t new_rank, zero_repartition_piece_t* pieces,
+                          int32_t piece_cap, int32_t* n_pieces);
 
 #ifdef __cplusplus
 }

@@ -423,3 +423,70 @@ def test_step_accepts_fp32_replicas_only_as_gradients():
     bad = good_args(param_dtype=Z.ZERO_FP32)
     with pytest.raises(Z.ZeroError):
         Z.zero_shard_step(bad, stream=0)
+
+
+# ------------------------------------------- partitions are re-derived, not trusted
+def _hand_built(numel, world, align, shard, padded=None):
+    p = _abi.zero_partition_t()
+    p.numel, p.world_size, p.alignment = numel, world, align
+    p.shard_numel = shard
+    p.padded_numel = shard * world if padded is None else padded
+    return p
+
+
+@pytest.mark.parametrize("part", [
+    _hand_built(1000, 4, 8, 264),                      # covers numel but is not minimal
+    _hand_built(1000, 4, 8, 256, padded=1000),          # padded_numel inconsistent
+    _hand_built(1000, 4, 8, 2**62),                     # shard * world overflows int64
+    _hand_built(1000, 4, 3, 252),                       # alignment not a power of two
+    _hand_built(1000, 0, 8, 256),                       # no ranks
+    _hand_built(-1, 4, 8, 0),                           # negative numel
+])
+def test_gather_and_repartition_refuse_inconsistent_partitions(part):
+    # Both checks run before any device work, so no GPU is needed.
+    L = Z.lib()
+    shards = (_abi.vp * 4)(0x1000, 0x2000, 0x3000, 0x4000)
+    assert L.zero_gather_params(ctypes.byref(part), shards, Z.ZERO_BF16, 0, 10, 0x8000,
+                                None) == Z.ZERO_EINVAL
+    good = Z.zero_partition(1000, 4, 8)
+    ptrs = (_abi.vp * 4)(0x1000, 0x2000, 0x3000, 0x4000)
+    assert L.zero_repartition(ctypes.byref(part), ptrs, ctypes.byref(good), ptrs,
+                              None) == Z.ZERO_EINVAL
+    assert L.zero_repartition(ctypes.byref(good), ptrs, ctypes.byref(part), ptrs,
+                              None) == Z.ZERO_EINVAL
+
+
+_EMPTY_RANK_CALLS = r"""
+import ctypes, sys
+sys.path.insert(0, %r)
+import zero_sharded_optimizer_step_amd as Z
+from zero_sharded_optimizer_step_amd import _abi
+L = Z.lib()
+a = _abi.zero_step_args()
+a.world_size, a.rank, a.shard_numel, a.valid_numel = 8, 7, 1024, 0
+a.grad_dtype = a.param_dtype = Z.ZERO_BF16
+a.n_replicas, a.step, a.loss_scale, a.grad_predivide = 8, 1, 1.0, 1.0
+a.lr, a.beta1, a.beta2, a.eps = 1e-3, 0.9, 0.999, 1e-8
+a.workspace = 0x100000
+a.workspace_bytes = 1 << 30
+a.replica_grad = None           # an empty rank passes no replica array
+codes = [L.zero_shard_accumulate(ctypes.byref(a), None),
+         L.zero_shard_reduce(ctypes.byref(a), 0, 0x200000, None),
+         L.zero_shard_step(ctypes.byref(a), 0.0, 0, None, None)]
+print(codes)
+"""
+
+
+def test_empty_rank_may_pass_no_replica_array():
+    # valid_numel 0 accepts replica_grad == NULL.  The calls pass their
+    # checks and reach the launch, which on a machine without a GPU fails
+    # with ZERO_EDEVICE; the process must not crash on the NULL array.  Run
+    # in a child so that a crash fails this test only.
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, "-c", _EMPTY_RANK_CALLS % ROOT], capture_output=True,
+                       text=True, timeout=120, env=dict(os.environ, HIP_VISIBLE_DEVICES=""))
+    assert r.returncode == 0, r.stderr[-2000:]
+    codes = eval(r.stdout.strip().splitlines()[-1])
+    assert all(c in (Z.ZERO_OK, Z.ZERO_EDEVICE) for c in codes), codes
+

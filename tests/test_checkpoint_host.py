@@ -132,3 +132,78 @@ def test_oracle_gather_hand_example():
     assert oracle.gather(shards, 10, 3, 2, 3, 9).tolist() == [3, 4, 5, 6, 7, 8]
     assert oracle.gather(shards, 10, 3, 2, 0, 10).tolist() == list(range(10))
     assert oracle.gather(shards, 10, 3, 2, 5, 5).size == 0
+
+
+# ----------------------------------------------------- the library's read plan
+def _apply_plan(old_slices, old_part, new_part, new_rank):
+    """New rank new_rank's slice, built only from the library's read plan."""
+    x = np.zeros(new_part.shard_numel, np.float32)
+    covered = np.zeros(new_part.shard_numel, np.int32)
+    pieces = Z.zero_repartition_plan(old_part, new_part, new_rank)
+    n_new = Z.zero_partition_valid_numel(new_part, new_rank)
+    last_new, last_old = -1, -1
+    for p in pieces:
+        assert p.count > 0 and p.reserved == 0
+        assert p.new_offset > last_new and p.old_rank > last_old     # ascending
+        last_new, last_old = p.new_offset, p.old_rank
+        n_k = Z.zero_partition_valid_numel(old_part, p.old_rank)
+        assert 0 <= p.old_offset and p.old_offset + p.count <= n_k   # inside real elements
+        x[p.new_offset:p.new_offset + p.count] = \
+            old_slices[p.old_rank][p.old_offset:p.old_offset + p.count]
+        covered[p.new_offset:p.new_offset + p.count] += 1
+    assert np.all(covered[:n_new] == 1) and np.all(covered[n_new:] == 0)
+    assert len(pieces) <= old_part.world_size
+    return x
+
+
+def test_repartition_plan_matches_oracle_by_brute_force():
+    # Every (numel, old world, old alignment, new world, new alignment) of a
+    # small grid: the slices the plan builds equal the oracle's re-cut, and
+    # each real element is read exactly once from inside an old rank's
+    # real elements.
+    cases = 0
+    for P in (0, 1, 5, 7, 8, 63, 64, 65, 200, 257, 1000):
+        for N, A in ((1, 1), (2, 8), (3, 2), (4, 8), (7, 1), (8, 128)):
+            s_old, _, valid_old = oracle.partition(P, N, A)
+            old = [np.where(np.arange(s_old) < valid_old[r],
+                            r * s_old + np.arange(s_old) + 1, 0).astype(np.float32)
+                   for r in range(N)]
+            old_part = Z.zero_partition(P, N, A)
+            for M, B in ((1, 1), (2, 1), (3, 8), (5, 2), (8, 8), (16, 1)):
+                new_part = Z.zero_partition(P, M, B)
+                ref = oracle.repartition(old, P, N, A, M, B)
+                for j in range(M):
+                    got = _apply_plan(old, old_part, new_part, j)
+                    assert np.array_equal(got, ref[j]), (P, N, A, M, B, j)
+                    cases += 1
+    assert cases > 1000
+
+
+def test_repartition_plan_capacity_and_errors():
+    L = Z.lib()
+    old = Z.zero_partition(1000, 8, 8)          # shards of 128
+    new = Z.zero_partition(1000, 2, 8)          # shards of 504: rank 0 reads old ranks 0..3
+    n = Z._abi.i32(-1)
+    pieces = (Z.zero_repartition_piece_t * 8)()
+    assert L.zero_repartition_plan(ctypes.byref(old), ctypes.byref(new), 0, pieces, 2,
+                                   ctypes.byref(n)) == Z.ZERO_ESIZE and n.value == 4
+    assert L.zero_repartition_plan(ctypes.byref(old), ctypes.byref(new), 0, pieces, 4,
+                                   ctypes.byref(n)) == Z.ZERO_OK and n.value == 4
+    assert [(p.old_rank, p.old_offset, p.new_offset, p.count) for p in pieces[:4]] == \
+        [(0, 0, 0, 128), (1, 0, 128, 128), (2, 0, 256, 128), (3, 0, 384, 120)]
+    assert L.zero_repartition_plan(ctypes.byref(old), ctypes.byref(new), 2, pieces, 8,
+                                   ctypes.byref(n)) == Z.ZERO_EINVAL          # rank out of range
+    other = Z.zero_partition(999, 2, 8)
+    assert L.zero_repartition_plan(ctypes.byref(old), ctypes.byref(other), 0, pieces, 8,
+                                   ctypes.byref(n)) == Z.ZERO_EINVAL          # numel differs
+    bad = Z.zero_partition(1000, 2, 8)
+    bad.shard_numel = 512                                                    # not minimal
+    bad.padded_numel = 1024
+    assert L.zero_repartition_plan(ctypes.byref(old), ctypes.byref(bad), 0, pieces, 8,
+                                   ctypes.byref(n)) == Z.ZERO_EINVAL
+    assert "zero_partition gives" in Z.zero_last_error()
+    assert L.zero_repartition_plan(ctypes.byref(old), ctypes.byref(new), 0, None, 8,
+                                   ctypes.byref(n)) == Z.ZERO_EINVAL
+    # a rank with no real elements reads nothing
+    tail = Z.zero_partition(10, 8, 8)            # shards of 8: ranks 2..7 are empty
+    assert Z.zero_repartition_plan(Z.zero_partition(10, 1, 1), tail, 5) == []

@@ -154,6 +154,27 @@ def test_poisoned_step_is_skipped_everywhere(kind, where):
     assert rep.skipped == 1
 
 
+@pytest.mark.parametrize("dt", [FP16, BF16])
+@pytest.mark.parametrize("kind", [0, 1, 2])
+def test_nonfinite_code_in_padding_is_no_overflow(kind, dt):
+    # Reading: the overflow flag covers the ranks' real elements.  A replica
+    # whose padding (past the last real element, on the last rank) holds
+    # +inf, -inf or nan still takes the step, on both sides, and the state
+    # matches the oracle.
+    numel, world = 20_011, 4
+    part = Z.zero_partition(numel, world, 128)
+    assert part.padded_numel - numel == 469
+    idx = numel + 200                                   # inside rank 3's padding
+    say("non-finite code %d in the padding at %d, %s" % (kind, idx, str(dt)[6:]))
+    sched = [W.Poison(0, 1, idx, kind), W.Poison(1, 3, part.padded_numel - 1, kind)]
+    scale = 2.0**12 if dt == FP16 else 1.0
+    spec = parity.Spec(numel=numel, world_size=world, alignment=128, grad_dtype=dt,
+                       grad_sigma=1e-3, steps=2, poison=sched, name="padding-poison",
+                       hp=Hyper(loss_scale=scale))
+    rep = parity.run(spec)
+    assert rep.skipped == 0 and rep.steps == 2
+
+
 def test_dynamic_scale_trajectory_small():
     # The scaled workload's schedule, at a size the oracle runs every step of.
     steps = 200
@@ -363,12 +384,13 @@ def test_flatten_large_tables_with_crowded_slots():
 
 
 def test_flatten_destinations_beyond_2_pow_32_elements():
-    # Slots whose destinations cross 2^32 elements, with gaps between them.
+    # Slots whose destinations cross 2^32 elements, with gaps between them
+    # (zeroed, like the padding) and untouched elements before the first.
     # A launch's table counts destinations from its first one in 32 bits,
     # so the launcher must start a new batch before that would overflow.
     say("flatten: destinations beyond 2^32 elements")
     n32 = 1 << 32
-    specs = [(0, 1000), (1000, 5), (n32 - 3, 100), (n32 + 1000, 7), (n32 + 1007, 33)]
+    specs = [(16, 984), (1000, 5), (n32 - 3, 100), (n32 + 1000, 7), (n32 + 1007, 33)]
     flat_numel = n32 + 4096
     flat = torch.full((flat_numel + 64,), 0x1357, dtype=torch.int16, device="cuda")
     rng = np.random.default_rng(12)
@@ -380,13 +402,37 @@ def test_flatten_destinations_beyond_2_pow_32_elements():
     torch.cuda.synchronize()
     for (off, n), src in zip(specs, srcs):
         assert torch.equal(flat[off:off + n], src.view(torch.int16)), "slot at %d" % off
+    assert bool((flat[:16] == 0x1357).all()), "wrote before the first slot"
     for lo, hi in ((1005, n32 - 3), (n32 + 97, n32 + 1000)):
-        assert bool((flat[lo:hi] == 0x1357).all()), "gap [%d, %d) written" % (lo, hi)
+        assert bool((flat[lo:hi] == 0).all()), "gap [%d, %d) not zeroed" % (lo, hi)
     end = specs[-1][0] + specs[-1][1]
     assert bool((flat[end:flat_numel] == 0).all()), "padding not zeroed"
     assert bool((flat[flat_numel:] == 0x1357).all()), "wrote past flat_numel"
     del flat
     torch.cuda.empty_cache()
+
+
+def test_flatten_zeroes_gaps_between_slots():
+    # Gaps between consecutive slots are zeroed like the padding, so no
+    # stale value between two tensors can reach the reduce; elements before
+    # the first slot belong to someone else and are left alone.
+    say("flatten: gaps between slots")
+    specs = [(5, 100), (120, 33), (153, 0), (160, 9), (300, 1)]
+    flat_numel = 333
+    flat = torch.full((flat_numel + 64,), 0x7F80, dtype=torch.int16, device="cuda")   # +inf
+    rng = np.random.default_rng(13)
+    srcs = [torch.from_numpy(rng.integers(0, 65536, max(n, 1), dtype=np.uint64)
+                             .astype(np.uint16).view(np.int16)).cuda()[:n].view(torch.bfloat16)
+            for _, n in specs]
+    slots = [Z.zero_tensor_slot_t(off, n, 0, 0) for off, n in specs]
+    Z.zero_bucket_flatten(slots, srcs, torch.bfloat16, flat.view(torch.bfloat16), flat_numel)
+    got = parity.u16(flat.view(torch.bfloat16))
+    ref = np.zeros(flat_numel + 64, np.uint16)
+    ref[:5] = 0x7F80
+    ref[flat_numel:] = 0x7F80
+    for (off, n), src in zip(specs, srcs):
+        ref[off:off + n] = parity.u16(src)
+    parity.assert_bitwise("flat", got, ref)
 
 
 def test_flatten_per_bucket():

@@ -414,6 +414,41 @@ def test_overflow_anywhere_skips_every_rank(where):
         assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("dtype", [oracle.FP16, oracle.BF16])
+@pytest.mark.parametrize("kind", [0, 1, 2])
+def test_nonfinite_code_in_padding_is_no_overflow(dtype, kind):
+    # Reading: the overflow flag covers the real elements only.  Padding
+    # holds no parameter, so the unsharded step (a world of one rank with
+    # alignment 1, which has no padding at all) never sees it; the sharded
+    # step's concatenated parts equal that step whatever the replicas'
+    # padding holds, and it is not skipped.
+    rng = np.random.default_rng(21)
+    P, N, A = 5000, 4, 128                      # s = 1280, padding 120 on rank 3
+    scale = 2.0**16 if dtype == oracle.FP16 else 1.0
+    s, padded, valid, reps, master = make_world(rng, P, N, N, A, dtype, 1e-3, scale)
+    assert padded - P == 120
+    codes = (0x7C00, 0xFC00, 0x7E00) if dtype == oracle.FP16 else (0x7F80, 0xFF80, 0x7FC0)
+    for i, r in enumerate(reps):
+        r[P + 7 * i] = codes[kind]
+    hp = oracle.Hyper(loss_scale=scale)
+    ps_, ms, vs = split(master, N, s), split(np.zeros(padded, np.float32), N, s), \
+        split(np.zeros(padded, np.float32), N, s)
+    full = np.zeros(padded, np.uint16)
+    info = oracle.step(reps, dtype, P, N, A, ps_, ms, vs, full, hp, t=1)
+    assert not info.overflow and not info.skipped and math.isfinite(info.sumsq)
+    p1 = [master[:P].copy()]
+    m1, v1 = [np.zeros(P, np.float32)], [np.zeros(P, np.float32)]
+    full1 = np.zeros(P, np.uint16)
+    info1 = oracle.step([r[:P].copy() for r in reps], dtype, P, 1, 1, p1, m1, v1, full1, hp, t=1)
+    # both sum the squares over the same elements in the same order
+    assert info1.sumsq == info.sumsq and info1.coef == info.coef
+    assert np.array_equal(np.concatenate([x[:n] for x, n in zip(ps_, valid)]), p1[0])
+    assert np.array_equal(full[:P], full1)
+    # the state's padding (zero here) is never written
+    for x, n in zip(ps_ + ms + vs, valid * 3):
+        assert not np.any(x[n:])
+
+
 # ----------------------------------------------------- gradient accumulation
 @pytest.mark.parametrize("dtype", [oracle.FP16, oracle.BF16])
 def test_accumulate_adds_the_reduced_micro_batch(dtype):

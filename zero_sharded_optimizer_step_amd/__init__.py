@@ -14,22 +14,25 @@ from typing import Optional, Sequence
 
 from . import _abi
 from ._abi import (ZERO_BF16, ZERO_CKPT_MAGIC, ZERO_CKPT_VERSION, ZERO_EALIGN, ZERO_EDEVICE,
-                   ZERO_EINVAL, ZERO_ESIZE, ZERO_FP16, ZERO_FP32, ZERO_MAX_REPLICAS, ZERO_OK,
-                   ZeroError,
+                   ZERO_EINVAL, ZERO_ESIZE, ZERO_FP16, ZERO_FP32, ZERO_MAX_REPLICAS,
+                   ZERO_OK, ZeroError,
                    check, lib, zero_bucket_t, zero_ckpt_header_t, zero_global_t,
                    zero_loss_scaler_t, zero_offload_staging_t, zero_partition_t,
-                   zero_step_args, zero_step_info, zero_tensor_slot_t)
+                   zero_repartition_piece_t, zero_step_args, zero_step_info,
+                   zero_tensor_slot_t)
 
 __all__ = [
     "ZERO_OK", "ZERO_EINVAL", "ZERO_EALIGN", "ZERO_ESIZE", "ZERO_EDEVICE",
-    "ZERO_FP16", "ZERO_BF16", "ZERO_FP32", "ZERO_MAX_REPLICAS", "ZeroError", "lib",
+    "ZERO_FP16", "ZERO_BF16", "ZERO_FP32", "ZERO_MAX_REPLICAS",
+    "ZeroError", "lib",
     "zero_last_error", "zero_partition", "zero_partition_valid_numel",
     "zero_bucket_plan", "zero_bucket_flatten", "zero_shard_workspace_bytes",
     "zero_partials_bytes", "zero_shard_reduce", "zero_shard_accumulate",
     "zero_accumulate_local", "zero_shard_combine",
     "zero_shard_apply", "zero_shard_step", "zero_loss_scaler_init",
     "zero_loss_scaler_update", "zero_ckpt_header_make", "zero_ckpt_header_check",
-    "zero_repartition", "zero_gather_params", "zero_offload_apply", "zero_host_adamw", "zero_host_threads",
+    "zero_repartition", "zero_repartition_plan", "zero_gather_params", "zero_offload_apply",
+    "zero_host_adamw", "zero_host_threads",
     "OffloadStaging",
     "StepArgs", "dtype_code", "GLOBAL_BYTES",
 ]
@@ -147,8 +150,9 @@ def zero_loss_scaler_update(st: zero_loss_scaler_t, overflow: bool) -> bool:
 # --------------------------------------------------------------- device calls
 def zero_bucket_flatten(slots, srcs, dtype, flat, flat_numel: Optional[int] = None,
                         stream=None) -> None:
-    """Copy tensors `srcs` (device) into `flat` at their slots' offsets and
-    zero [end of the last slot, flat_numel)."""
+    """Copy tensors `srcs` (device) into `flat` at their slots' offsets,
+    zero the gaps between consecutive slots and [end of the last slot,
+    flat_numel)."""
     n = len(slots)
     if len(srcs) != n:
         raise ValueError("one source tensor per slot")
@@ -339,6 +343,23 @@ def zero_repartition(from_part: zero_partition_t, srcs: Sequence, to_part: zero_
             _need(t, 4 * to_part.shard_numel, "dsts[%d]" % j)
     check(lib().zero_repartition(ctypes.byref(from_part), sp, ctypes.byref(to_part), dp,
                                  _stream(stream)), "zero_repartition")
+
+
+def zero_repartition_plan(from_part: zero_partition_t, to_part: zero_partition_t,
+                          new_rank: int) -> list:
+    """The pieces (zero_repartition_piece_t) new rank `new_rank` of to_part
+    reads from the old ranks of from_part, in ascending new_offset."""
+    n = _abi.i32(0)
+    cap = 0
+    while True:
+        pieces = (zero_repartition_piece_t * max(cap, 1))()
+        rc = lib().zero_repartition_plan(ctypes.byref(from_part), ctypes.byref(to_part), new_rank,
+                                         pieces, cap, ctypes.byref(n))
+        if rc == ZERO_ESIZE and n.value > cap:
+            cap = n.value
+            continue
+        check(rc, "zero_repartition_plan")
+        return pieces[:n.value]
 
 
 # ------------------------------------------------------- optimizer offload

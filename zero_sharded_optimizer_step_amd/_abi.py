@@ -79,6 +79,11 @@ class zero_ckpt_header_t(ctypes.Structure):
 
 assert ctypes.sizeof(zero_ckpt_header_t) == 128
 
+class zero_repartition_piece_t(ctypes.Structure):
+    _fields_ = [("old_offset", i64), ("new_offset", i64), ("count", i64), ("old_rank", i32),
+                ("reserved", i32)]
+
+
 class zero_offload_staging_t(ctypes.Structure):
     _fields_ = [("grad_stage", vp * 2), ("param_stage", vp * 2), ("chunk_elems", i64),
                 ("n_threads", i32), ("reserved", i32)]
@@ -113,6 +118,10 @@ _PROTOTYPES = {
                                               ctypes.POINTER(zero_partition_t)]),
     "zero_repartition": (ctypes.c_int, [ctypes.POINTER(zero_partition_t), ctypes.POINTER(vp),
                                         ctypes.POINTER(zero_partition_t), ctypes.POINTER(vp), vp]),
+    "zero_repartition_plan": (ctypes.c_int, [ctypes.POINTER(zero_partition_t),
+                                             ctypes.POINTER(zero_partition_t), i32,
+                                             ctypes.POINTER(zero_repartition_piece_t), i32,
+                                             ctypes.POINTER(i32)]),
     "zero_gather_params": (ctypes.c_int, [ctypes.POINTER(zero_partition_t), ctypes.POINTER(vp),
                                           i32, i64, i64, vp, vp]),
     "zero_offload_apply": (ctypes.c_int, [ctypes.POINTER(zero_step_args), vp,

@@ -23,7 +23,8 @@ from typing import List, Optional, Sequence, Tuple
 import torch
 
 from . import (dtype_code, zero_ckpt_header_check, zero_ckpt_header_make, zero_ckpt_header_t,
-               zero_loss_scaler_t, zero_partition_t, zero_partition_valid_numel)
+               zero_loss_scaler_t, zero_partition_t, zero_partition_valid_numel,
+               zero_repartition_plan)
 
 HEADER_BYTES = ctypes.sizeof(zero_ckpt_header_t)
 STAGING_ELEMS = 1 << 26             # 256 MiB of fp32 per transfer
@@ -112,7 +113,9 @@ def load_rank_resharded(directory: str, new_part: zero_partition_t, new_rank: in
     """Fill new rank `new_rank` of partition new_part (same numel, any world
     size and alignment) from a directory of one run's shard files, reading
     only the byte ranges it owns; the padding is zeroed.  Returns the run's
-    (step, scaler)."""
+    (step, scaler).  Which old file and which elements each piece comes
+    from is the library's read plan (zero_repartition_plan); this function
+    only seeks and reads."""
     old_world = read_header(rank_path(directory, 0))[0].world_size
     hp = [read_header(rank_path(directory, r)) for r in range(old_world)]
     headers = [h for h, _ in hp]
@@ -124,19 +127,17 @@ def load_rank_resharded(directory: str, new_part: zero_partition_t, new_rank: in
     s_new = new_part.shard_numel
     if len(state) != 3 or any(t.dtype != torch.float32 or t.numel() < s_new for t in state):
         raise ValueError("state is three fp32 tensors of shard_numel elements")
-    lo = new_rank * s_new
-    hi = lo + zero_partition_valid_numel(new_part, new_rank)
+    n_new = zero_partition_valid_numel(new_part, new_rank)
     for t in state:
-        t[hi - lo:s_new].zero_()
-    if hi <= lo:
+        t[n_new:s_new].zero_()
+    pieces = zero_repartition_plan(old, new_part, new_rank)
+    if not pieces:
         return step, scaler
-    s_old = old.shard_numel
-    staging = _staging(state[0].device, hi - lo)
-    for k in range(lo // s_old, (hi - 1) // s_old + 1):
-        a, b = max(lo, k * s_old), min(hi, (k + 1) * s_old)
-        n_k = headers[k].valid_numel
-        with open(rank_path(directory, k), "rb") as f:
+    staging = _staging(state[0].device, max(p.count for p in pieces))
+    for p in pieces:
+        n_k = headers[p.old_rank].valid_numel
+        with open(rank_path(directory, p.old_rank), "rb") as f:
             for field, t in enumerate(state):
-                f.seek(HEADER_BYTES + 4 * (field * n_k + (a - k * s_old)))
-                _read_fp32(f, t[a - lo:b - lo], staging)
+                f.seek(HEADER_BYTES + 4 * (field * n_k + p.old_offset))
+                _read_fp32(f, t[p.new_offset:p.new_offset + p.count], staging)
     return step, scaler

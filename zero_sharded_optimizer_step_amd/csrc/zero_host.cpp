@@ -38,7 +38,7 @@ AdamConsts adam_consts(double lr, double beta1, double beta2, double eps, double
     return k;
 }
 
-int validate_step_args(const zero_step_args* a) {
+int validate_step_args(const zero_step_args* a, bool check_workspace) {
     if (!a) return fail(ZERO_EINVAL, "args is NULL");
     if (a->world_size < 1) return fail(ZERO_EINVAL, "world_size %d < 1", a->world_size);
     if (a->rank < 0 || a->rank >= a->world_size)
@@ -70,8 +70,9 @@ int validate_step_args(const zero_step_args* a) {
     if (!finite_positive(a->eps)) return fail(ZERO_EINVAL, "eps must be finite and > 0");
     if (!std::isfinite(a->weight_decay)) return fail(ZERO_EINVAL, "weight_decay must be finite");
     if (std::isnan(a->max_grad_norm)) return fail(ZERO_EINVAL, "max_grad_norm is NaN");
-    if (!a->workspace) return fail(ZERO_EINVAL, "workspace is NULL");
-    if (!aligned16(a->workspace)) return fail(ZERO_EALIGN, "workspace is not 16-byte aligned");
+    if (check_workspace && !a->workspace) return fail(ZERO_EINVAL, "workspace is NULL");
+    if (check_workspace && !aligned16(a->workspace))
+        return fail(ZERO_EALIGN, "workspace is not 16-byte aligned");
     // A rank with no real elements reads and writes no element, so its data
     // pointers may be NULL (empty tensors).
     if (a->valid_numel > 0) {
@@ -101,9 +102,24 @@ int validate_step_args(const zero_step_args* a) {
     }
     // Start of this rank's slice of the full buffer: shard_numel is a
     // multiple of 8, so 2-byte elements keep 16-byte alignment.
-    if (a->workspace_bytes < zero_shard_workspace_bytes(a->shard_numel))
+    if (check_workspace && a->workspace_bytes < zero_shard_workspace_bytes(a->shard_numel))
         return fail(ZERO_ESIZE, "workspace_bytes %zu < %zu needed", a->workspace_bytes,
                     zero_shard_workspace_bytes(a->shard_numel));
+    return ZERO_OK;
+}
+
+int check_partition(const zero_partition_t* p, const char* what) {
+    if (!p) return fail(ZERO_EINVAL, "%s is NULL", what);
+    zero_partition_t q;
+    if (zero_partition(p->numel, p->world_size, p->alignment, &q) != ZERO_OK)
+        return fail(ZERO_EINVAL, "%s (numel %lld, world_size %d, alignment %d) is not a valid "
+                                 "partition", what, (long long)p->numel, p->world_size,
+                    p->alignment);
+    if (q.shard_numel != p->shard_numel || q.padded_numel != p->padded_numel)
+        return fail(ZERO_EINVAL, "%s has shard_numel %lld / padded_numel %lld; zero_partition "
+                                 "gives %lld / %lld", what, (long long)p->shard_numel,
+                    (long long)p->padded_numel, (long long)q.shard_numel,
+                    (long long)q.padded_numel);
     return ZERO_OK;
 }
 
@@ -318,6 +334,48 @@ int zero_ckpt_header_check(const zero_ckpt_header_t* h, uint64_t file_bytes,
                     (unsigned long long)file_bytes,
                     (unsigned long long)(sizeof(zero_ckpt_header_t) + payload));
     if (part) *part = p;
+    return ZERO_OK;
+}
+
+int zero_repartition_plan(const zero_partition_t* from, const zero_partition_t* to,
+                          int32_t new_rank, zero_repartition_piece_t* pieces, int32_t piece_cap,
+                          int32_t* n_pieces) {
+    clear_error();
+    if (!n_pieces || piece_cap < 0 || (piece_cap > 0 && !pieces))
+        return fail(ZERO_EINVAL, "n_pieces is NULL, piece_cap < 0 or pieces is NULL");
+    int rc;
+    if ((rc = check_partition(from, "from"))) return rc;
+    if ((rc = check_partition(to, "to"))) return rc;
+    if (from->numel != to->numel)
+        return fail(ZERO_EINVAL, "partitions cover %lld and %lld elements", (long long)from->numel,
+                    (long long)to->numel);
+    if (new_rank < 0 || new_rank >= to->world_size)
+        return fail(ZERO_EINVAL, "new_rank %d outside [0, %d)", new_rank, to->world_size);
+    // The new rank's real elements are flat [lo, hi).  Flat element i < numel
+    // is element i - k*s_old of old rank k = i / s_old, one of that rank's
+    // real elements; the old ranks that [lo, hi) meets give one contiguous
+    // piece each.
+    const int64_t s_old = from->shard_numel;
+    const int64_t lo = static_cast<int64_t>(new_rank) * to->shard_numel;
+    const int64_t hi = lo + zero_partition_valid_numel(to, new_rank);
+    const int64_t k0 = hi > lo ? lo / s_old : 0;
+    const int64_t count = hi > lo ? (hi - 1) / s_old - k0 + 1 : 0;
+    *n_pieces = static_cast<int32_t>(count);
+    if (count > piece_cap)
+        return fail(ZERO_ESIZE, "the plan has %lld pieces, capacity is %d", (long long)count,
+                    piece_cap);
+    for (int64_t q = 0; q < count; ++q) {
+        const int64_t k = k0 + q;
+        const int64_t a = lo > k * s_old ? lo : k * s_old;
+        const int64_t e = (k + 1) * s_old;
+        const int64_t b = hi < e ? hi : e;
+        zero_repartition_piece_t& pc = pieces[q];
+        pc.old_offset = a - k * s_old;
+        pc.new_offset = a - lo;
+        pc.count = b - a;
+        pc.old_rank = static_cast<int32_t>(k);
+        pc.reserved = 0;
+    }
     return ZERO_OK;
 }
 

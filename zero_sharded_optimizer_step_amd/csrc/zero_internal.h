@@ -18,7 +18,7 @@ inline bool aligned16(const void* p) {
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
 
-inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+constexpr size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Launch geometry.  Both streaming passes give each thread one "quad" of 4
 // consecutive elements and launch one thread per quad (no grid-stride
@@ -56,7 +56,7 @@ struct SlotHeader {
 constexpr size_t kSlotBytes = sizeof(SlotHeader) + kFoldBlocks * sizeof(Partial);
 
 // Quads (the last one possibly partial) of n elements.
-inline int64_t quads_of(int64_t n) { return (n + kQuad - 1) / kQuad; }
+constexpr int64_t quads_of(int64_t n) { return (n + kQuad - 1) / kQuad; }
 
 // A launch: `blocks` (a multiple of kXcds * group) of which the first
 // `needed` hold work, remapped in XCD runs of `group` logical blocks.
@@ -67,7 +67,7 @@ struct Grid {
 constexpr int64_t kXcdGroup = 256;
 
 // Blocks of `threads` threads covering quads_of(n) quads, at least one.
-inline Grid grid_for(int64_t n, int threads) {
+constexpr Grid grid_for(int64_t n, int threads) {
     int64_t b = (quads_of(n) + threads - 1) / threads;
     if (b < 1) b = 1;
     if (b >= kXcds * kXcdGroup) {
@@ -87,27 +87,30 @@ constexpr int64_t xcd_logical_block(uint32_t b, uint32_t group) {
     return static_cast<int64_t>((b / kXcds) / group) * (kXcds * group) + (b % kXcds) * group +
            (b / kXcds) % group;
 }
-inline int64_t reduce_blocks_for(int64_t n) { return grid_for(n, kReduceThreads).blocks; }
-inline int64_t apply_blocks_for(int64_t n) { return grid_for(n, kApplyThreads).blocks; }
+constexpr int64_t reduce_blocks_for(int64_t n) { return grid_for(n, kReduceThreads).blocks; }
+constexpr int64_t apply_blocks_for(int64_t n) { return grid_for(n, kApplyThreads).blocks; }
 inline int fold_blocks_for(int64_t reduce_blocks) {
     return static_cast<int>(reduce_blocks < kFoldBlocks ? reduce_blocks : kFoldBlocks);
 }
 
 // Byte offsets inside a zero_shard_step workspace: the fp32 reduced
 // gradient, the reduce's per-block partials, one slot, one zero_global_t.
-inline size_t ws_grad_bytes(int64_t shard_numel) {
+constexpr size_t ws_grad_bytes(int64_t shard_numel) {
     return round_up(static_cast<size_t>(shard_numel) * 4u, 256);
 }
-inline size_t ws_blocks_offset(int64_t shard_numel) { return ws_grad_bytes(shard_numel); }
-inline size_t ws_blocks_bytes(int64_t shard_numel) {
+constexpr size_t ws_blocks_offset(int64_t shard_numel) { return ws_grad_bytes(shard_numel); }
+constexpr size_t ws_blocks_bytes(int64_t shard_numel) {
     return round_up(static_cast<size_t>(reduce_blocks_for(shard_numel)) * sizeof(Partial), 256);
 }
-inline size_t ws_slot_offset(int64_t shard_numel) {
+constexpr size_t ws_slot_offset(int64_t shard_numel) {
     return ws_blocks_offset(shard_numel) + ws_blocks_bytes(shard_numel);
 }
-inline size_t ws_global_offset(int64_t shard_numel) {
+constexpr size_t ws_global_offset(int64_t shard_numel) {
     return ws_slot_offset(shard_numel) + round_up(kSlotBytes, 256);
 }
+
+// The whole workspace of a shard (zero_shard_workspace_bytes).
+constexpr size_t ws_total_bytes(int64_t shard_numel) { return ws_global_offset(shard_numel) + 256; }
 
 // Where a rank's cast parameters go: its ZeRO-3 shard when given, else
 // its slice of the full buffer.
@@ -117,8 +120,17 @@ inline unsigned short* param_out(const zero_step_args* a) {
            static_cast<size_t>(a->rank) * static_cast<size_t>(a->shard_numel);
 }
 
-// Checks every field of a step's arguments (see zero_shard_step).
-int validate_step_args(const zero_step_args* a);
+// Checks every field of a step's arguments (see zero_shard_step); without
+// check_workspace the workspace fields are not looked at (the caller
+// supplies the workspace itself).
+int validate_step_args(const zero_step_args* a, bool check_workspace = true);
+
+// ZERO_OK when *p is exactly what zero_partition makes of its numel,
+// world_size and alignment; otherwise records why (naming the partition
+// `what`) and returns ZERO_EINVAL.  Every entry point that takes a
+// partition struct re-derives it this way, so a hand-built one with an
+// inconsistent or overflowing shard size is refused.
+int check_partition(const zero_partition_t* p, const char* what);
 
 // AdamW's per-step fp32 constants, each computed in fp64 from the step's
 // hyper-parameters and rounded once; the GPU pass and the host (offloaded)

@@ -18,6 +18,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <vector>
 
 #include "zero_internal.h"
 
@@ -514,9 +515,11 @@ void launch_reduce_dt(const ReplicaPtrs& reps, int nrep, int64_t n_valid, float 
 
 // Pass 1 into the workspace; with fold, its block partials then go to `slot`.
 int launch_pass1(const zero_step_args* a, hipStream_t st) {
+    // An empty rank (valid_numel 0) may pass no replica array at all; its
+    // launch reads no replica element.
     ReplicaPtrs reps;
     for (int r = 0; r < ZERO_MAX_REPLICAS; ++r)
-        reps.p[r] = r < a->n_replicas ? a->replica_grad[r] : nullptr;
+        reps.p[r] = (a->replica_grad && r < a->n_replicas) ? a->replica_grad[r] : nullptr;
     const float inv = static_cast<float>(1.0 / (a->loss_scale * a->grad_predivide));
     unsigned char* ws = static_cast<unsigned char*>(a->workspace);
     float* g = reinterpret_cast<float*>(ws);
@@ -581,8 +584,10 @@ int launch_apply(const zero_step_args* a, const void* global, hipStream_t st) {
 }
 
 // Copy n ranges of 16-bit values, range t from src(t) to flat elements
-// [dst(t), dst(t) + len(t)) (ascending, non-overlapping), then zero
-// [end of the last range, flat_numel); batched into flatten launches.
+// [dst(t), dst(t) + len(t)) (ascending, non-overlapping), zero any gap
+// between consecutive ranges, then zero [end of the last range,
+// flat_numel); batched into flatten launches.  Elements before the first
+// range are not touched.
 template <class Src, class Dst, class Len>
 int copy_ranges(int32_t n, Src src_of, Dst dst_of, Len len_of, unsigned short* flat, int64_t flat_numel,
                 hipStream_t st) {
@@ -648,6 +653,7 @@ int copy_ranges(int32_t n, Src src_of, Dst dst_of, Len len_of, unsigned short* f
     int64_t end = 0;
     for (int32_t t = 0; t < n; ++t) {
         const int64_t d = dst_of(t), len = len_of(t);
+        if (t > 0 && d > end && (rc = add(nullptr, end, d - end))) return rc;
         if ((rc = add(src_of(t), d, len))) return rc;
         end = d + len;
     }
@@ -655,10 +661,32 @@ int copy_ranges(int32_t n, Src src_of, Dst dst_of, Len len_of, unsigned short* f
     return flush();
 }
 
+// One rank's whole step once its arguments are checked: pass 1 and the fold
+// into the workspace's own slot, a combine with the peers' contribution,
+// pass 2, and the optional read-back of the result.
+int run_step(const zero_step_args* a, double peer_sumsq, int32_t peer_overflow, zero_step_info* info,
+             hipStream_t st) {
+    unsigned char* ws = static_cast<unsigned char*>(a->workspace);
+    unsigned char* slot = ws + ws_slot_offset(a->shard_numel);
+    void* global = ws + ws_global_offset(a->shard_numel);
+    int rc;
+    if ((rc = launch_reduce(a, slot, st))) return rc;
+    if ((rc = launch_combine(slot, 1, peer_sumsq, peer_overflow ? 1 : 0, a->max_grad_norm, global, st)))
+        return rc;
+    if ((rc = launch_apply(a, global, st))) return rc;
+    if (info) {
+        hipError_t e = hipMemcpyAsync(info, global, sizeof(zero_global_t), hipMemcpyDeviceToHost, st);
+        if (e == hipSuccess) e = hipStreamSynchronize(st);
+        if (e != hipSuccess) return fail(ZERO_EDEVICE, "reading the step result: %s", hipGetErrorString(e));
+    }
+    return ZERO_OK;
+}
+
 }  // namespace
 }  // namespace zero
 
 using namespace zero;
+
 
 extern "C" {
 
@@ -747,20 +775,7 @@ int zero_shard_step(const zero_step_args* a, double peer_sumsq, int32_t peer_ove
     int rc = validate_step_args(a);
     if (rc) return rc;
     if (!(peer_sumsq >= 0.0)) return fail(ZERO_EINVAL, "peer_sumsq must be >= 0 (got NaN or negative)");
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    unsigned char* ws = static_cast<unsigned char*>(a->workspace);
-    unsigned char* slot = ws + ws_slot_offset(a->shard_numel);
-    void* global = ws + ws_global_offset(a->shard_numel);
-    if ((rc = launch_reduce(a, slot, st))) return rc;
-    if ((rc = launch_combine(slot, 1, peer_sumsq, peer_overflow ? 1 : 0, a->max_grad_norm, global, st)))
-        return rc;
-    if ((rc = launch_apply(a, global, st))) return rc;
-    if (info) {
-        hipError_t e = hipMemcpyAsync(info, global, sizeof(zero_global_t), hipMemcpyDeviceToHost, st);
-        if (e == hipSuccess) e = hipStreamSynchronize(st);
-        if (e != hipSuccess) return fail(ZERO_EDEVICE, "reading the step result: %s", hipGetErrorString(e));
-    }
-    return ZERO_OK;
+    return run_step(a, peer_sumsq, peer_overflow, info, static_cast<hipStream_t>(stream));
 }
 
 int zero_bucket_flatten(const zero_tensor_slot_t* slots, int32_t n_tensors, const void* const* src_dev,
@@ -796,8 +811,8 @@ int zero_gather_params(const zero_partition_t* p, const void* const* shards, int
     if (!p || !shards || !dst) return fail(ZERO_EINVAL, "a required pointer is NULL");
     if (dtype != ZERO_FP16 && dtype != ZERO_BF16)
         return fail(ZERO_EINVAL, "dtype %d is not ZERO_FP16 or ZERO_BF16", dtype);
-    if (p->world_size < 1 || p->shard_numel * p->world_size < p->numel)
-        return fail(ZERO_EINVAL, "the partition is invalid (use zero_partition)");
+    int rc = check_partition(p, "the partition");
+    if (rc) return rc;
     if (lo < 0 || hi < lo || hi > p->numel)
         return fail(ZERO_EINVAL, "range [%lld, %lld) outside [0, %lld)", (long long)lo,
                     (long long)hi, (long long)p->numel);
@@ -825,12 +840,12 @@ int zero_repartition(const zero_partition_t* from, const float* const* src_dev,
                      const zero_partition_t* to, float* const* dst_dev, void* stream) {
     clear_error();
     if (!from || !to || !src_dev || !dst_dev) return fail(ZERO_EINVAL, "a required pointer is NULL");
+    int rc;
+    if ((rc = check_partition(from, "from"))) return rc;
+    if ((rc = check_partition(to, "to"))) return rc;
     if (from->numel != to->numel)
         return fail(ZERO_EINVAL, "partitions cover %lld and %lld elements", (long long)from->numel,
                     (long long)to->numel);
-    if (from->world_size < 1 || to->world_size < 1 ||
-        from->shard_numel * from->world_size < from->numel || to->shard_numel * to->world_size < to->numel)
-        return fail(ZERO_EINVAL, "a partition is invalid (use zero_partition)");
     for (int32_t k = 0; k < from->world_size; ++k) {
         if (zero_partition_valid_numel(from, k) > 0 && !src_dev[k])
             return fail(ZERO_EINVAL, "src_dev[%d] is NULL", k);
@@ -841,30 +856,34 @@ int zero_repartition(const zero_partition_t* from, const float* const* src_dev,
         if (to->shard_numel > 0 && !dst_dev[j]) return fail(ZERO_EINVAL, "dst_dev[%d] is NULL", j);
         if (!aligned16(dst_dev[j])) return fail(ZERO_EALIGN, "dst_dev[%d] is not 16-byte aligned", j);
     }
-    // New rank j's real range [j*s', j*s' + n'_j) meets old ranks
-    // lo/s .. (hi-1)/s; each overlap is one contiguous copy, done as 16-bit
-    // halves by the flatten kernel; its padding is zero-filled after.
+    // New rank j copies the pieces of its read plan, each one contiguous
+    // run of an old rank's slice, as 16-bit halves through the flatten
+    // kernel; its padding is zero-filled after them.
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const int64_t s_old = from->shard_numel, s_new = to->shard_numel;
+    const int64_t s_new = to->shard_numel;
+    std::vector<zero_repartition_piece_t> plan;
     for (int32_t j = 0; j < to->world_size; ++j) {
         if (s_new == 0) break;
-        const int64_t lo = static_cast<int64_t>(j) * s_new;
-        const int64_t hi = lo + zero_partition_valid_numel(to, j);
-        const int64_t k0 = hi > lo ? lo / s_old : 0;
-        const int32_t n_pieces = hi > lo ? static_cast<int32_t>((hi - 1) / s_old - k0 + 1) : 0;
-        auto piece_lo = [&](int32_t q) { const int64_t k = k0 + q; return lo > k * s_old ? lo : k * s_old; };
-        auto piece_hi = [&](int32_t q) {
-            const int64_t k = k0 + q, e = (k + 1) * s_old;
-            return hi < e ? hi : e;
-        };
-        int rc = copy_ranges(
+        int32_t n_pieces = 0;
+        rc = zero_repartition_plan(from, to, j, plan.data(), static_cast<int32_t>(plan.size()),
+                                   &n_pieces);
+        if (rc == ZERO_ESIZE) {
+            try {
+                plan.resize(static_cast<size_t>(n_pieces));
+            } catch (...) {
+                return fail(ZERO_ESIZE, "no host memory for a plan of %d pieces", n_pieces);
+            }
+            rc = zero_repartition_plan(from, to, j, plan.data(), n_pieces, &n_pieces);
+        }
+        if (rc) return rc;
+        rc = copy_ranges(
             n_pieces,
             [&](int32_t q) {
-                const int64_t k = k0 + q;
-                return reinterpret_cast<const unsigned short*>(src_dev[k] + (piece_lo(q) - k * s_old));
+                return reinterpret_cast<const unsigned short*>(src_dev[plan[q].old_rank] +
+                                                               plan[q].old_offset);
             },
-            [&](int32_t q) { return 2 * (piece_lo(q) - lo); },
-            [&](int32_t q) { return 2 * (piece_hi(q) - piece_lo(q)); },
+            [&](int32_t q) { return 2 * plan[q].new_offset; },
+            [&](int32_t q) { return 2 * plan[q].count; },
             reinterpret_cast<unsigned short*>(dst_dev[j]), 2 * s_new, st);
         if (rc) return rc;
     }

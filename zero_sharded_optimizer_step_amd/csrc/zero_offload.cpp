@@ -238,8 +238,13 @@ int zero_offload_apply(const zero_step_args* a, const void* global_dev,
         e = hipMemcpyAsync(out_dev + lo, pst, len * 2, hipMemcpyHostToDevice, up);
         if (e == hipSuccess) e = hipEventRecord(up_done[c & 1], up);
     }
-    if (e == hipSuccess) e = hipStreamSynchronize(up);
-    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    // Wait for both streams whatever happened above: after an error some
+    // copies into or out of the caller's staging buffers and parameter
+    // slice may still be queued, and none may run after this call returns.
+    const hipError_t e_up = hipStreamSynchronize(up);
+    const hipError_t e_st = hipStreamSynchronize(st);
+    if (e == hipSuccess) e = e_up;
+    if (e == hipSuccess) e = e_st;
     cleanup();
     if (e != hipSuccess) return hip_fail(e, "offloaded step");
     return ZERO_OK;
