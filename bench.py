@@ -329,11 +329,14 @@ def run_shard13b_local(args, torch, Z, W):
     print(json.dumps(out), flush=True)
 
 
-def cpu_record(n, dt, sample):
-    """A `cpu_baseline` entry: the oracle's rate over a sample of n params."""
+def cpu_record(n, dt, sample, total):
+    """A `cpu_baseline` entry: the oracle's rate over a sample of n of the
+    workload's `total` params (the timed region covers those n only)."""
     return dict(value=n / dt, unit="params/s", cores=1, kind="oracle",
                 sample="%s; one host thread of %s (%d CPUs available), %.1f s"
-                       % (sample, host_cpu(), len(os.sched_getaffinity(0)), dt))
+                       % (sample, host_cpu(), len(os.sched_getaffinity(0)), dt),
+                sample_elements=int(n), workload_elements=int(total),
+                sample_fraction=float(n) / float(total) if total else 1.0, seconds=dt)
 
 
 def host_u16(torch, t):
@@ -366,8 +369,9 @@ def cpu_baseline_shard13b(args, torch, W, grads, micro_batches=1):
     oracle.step_accumulated([reps] * micro_batches, oracle.BF16, n, 1, 8, p, m, v, full, hp, 1)
     dt = time.perf_counter() - t0
     what = "reduce" if micro_batches == 1 else "%d reduces (set, then add)" % micro_batches
-    return cpu_record(n, dt, "first %d elements of rank 0's shard (8 bf16 replicas): %s, clip, "
-                             "AdamW, bf16 cast" % (n, what))
+    return cpu_record(n, dt, "first %d of the %d elements of rank 0's shard (8 bf16 replicas): "
+                             "%s, clip, AdamW, bf16 cast" % (n, grads[0].numel(), what),
+                      grads[0].numel())
 
 
 def cpu_baseline_local(args, torch, W, own, peers, K):
@@ -391,9 +395,10 @@ def cpu_baseline_local(args, torch, W, own, peers, K):
         oracle.adamw(g, p, m, v, coef, w.lr, 0.9, 0.999, 1e-8, w.weight_decay, 1)
     oracle.to_low_precision(p, oracle.BF16)
     dt = time.perf_counter() - t0
-    return cpu_record(n, dt, "%d shard elements: the fp32 window sum of %d elements of the "
-                             "rank's own bf16 gradient over %d micro-batches, the 8-way fp32 "
-                             "reduce, clip, AdamW, bf16 cast" % (n, 8 * n, K))
+    return cpu_record(n, dt, "%d of the %d shard elements: the fp32 window sum of %d elements "
+                             "of the rank's own bf16 gradient over %d micro-batches, the 8-way "
+                             "fp32 reduce, clip, AdamW, bf16 cast"
+                      % (n, peers[0].numel(), 8 * n, K), peers[0].numel())
 
 
 def cpu_baseline_ragged(args, torch, W, r):
@@ -424,7 +429,7 @@ def cpu_baseline_ragged(args, torch, W, r):
     dt = time.perf_counter() - t0
     return cpu_record(n, dt, "the first %d of the %d tensors (%d params): 8 replicas flattened, "
                              "then the step of 8 ranks (reduce, clip, AdamW, bf16 cast)"
-                      % (T, len(slots), n))
+                      % (T, len(slots), n), w.numel)
 
 
 def cpu_baseline_repartition(args, torch, src_world):
@@ -440,7 +445,7 @@ def cpu_baseline_repartition(args, torch, src_world):
         oracle.repartition(sl, n, 8, 128, 3, 128)
     dt = time.perf_counter() - t0
     return cpu_record(n, dt, "master, exp_avg and exp_avg_sq of a %d-param model re-partitioned "
-                             "from 8 ranks to 3" % n)
+                             "from 8 ranks to 3" % n, src_world.numel)
 
 
 def cpu_baseline_zero3(args, torch, shards):
@@ -453,7 +458,8 @@ def cpu_baseline_zero3(args, torch, shards):
     t0 = time.perf_counter()
     oracle.gather(host, n, 8, 128, 0, n)
     dt = time.perf_counter() - t0
-    return cpu_record(n, dt, "%d bf16 params gathered from 8 rank shards" % n)
+    return cpu_record(n, dt, "%d bf16 params gathered from 8 rank shards" % n,
+                      shards[0].numel() * len(shards))
 
 
 def host_cpu() -> str:

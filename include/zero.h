@@ -320,7 +320,14 @@ int zero_shard_apply(const zero_step_args* a, const void* global_dev,
  * <= 0, lr, betas or eps out of range, a NULL pointer -> ZERO_EINVAL; a
  * misaligned device pointer -> ZERO_EALIGN; workspace_bytes too small ->
  * ZERO_ESIZE; a HIP failure -> ZERO_EDEVICE.  When valid_numel is 0 the
- * rank touches no element and only the workspace must be given. */
+ * rank touches no element and only the workspace must be given.
+ * Graph capture: without info the call queues four kernels and nothing
+ * else, so it can be captured in a HIP graph.  The step's scalars (t, lr,
+ * betas, eps, weight decay, loss scale, predivide, max_grad_norm,
+ * peer_sumsq, peer_overflow) travel as kernel arguments and are fixed at
+ * capture: every replay uses the captured values.  Since t changes after
+ * every applied step and the loss scale after scaler events, re-capture
+ * when any of them changes, or capture only where they stay fixed. */
 int zero_shard_step(const zero_step_args* a, double peer_sumsq,
                     int32_t peer_overflow, zero_step_info* info, void* stream);
 

@@ -18,8 +18,10 @@ records how many elements are.
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
-from typing import Callable, List, Optional
+from typing import Callable, List, Optional, Sequence
 
 import numpy as np
 import torch
@@ -359,15 +361,157 @@ def structural_sample(n: int, rng: np.random.Generator, n_random: int = 1 << 16)
     return s[(s >= 0) & (s < n)]
 
 
+# ------------------------------------------- every element, at full size
+# The update pass of the oracle over a whole shard, chunk by chunk.  AdamW
+# and the cast act on each element alone, so the pass splits every chunk
+# over a few host threads, each running the oracle's own single-threaded C
+# on its part (ctypes releases the GIL); the values are the same as one
+# call over the chunk.  Comparisons take a bitwise fast path and fall back
+# to the stated tolerances only where bits differ.
+
+HOST_THREADS = max(1, min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity")
+                          else (os.cpu_count() or 1)))
+_POOL: Optional[ThreadPoolExecutor] = None
+
+
+def pool() -> ThreadPoolExecutor:
+    global _POOL
+    if _POOL is None:
+        _POOL = ThreadPoolExecutor(max_workers=HOST_THREADS)
+    return _POOL
+
+
+def _parts(n: int, k: int):
+    step = -(-n // k) if n else 1
+    return [(a, min(n, a + step)) for a in range(0, n, step)]
+
+
+def adamw_parallel(g: np.ndarray, p: np.ndarray, m: np.ndarray, v: np.ndarray, coef: float,
+                   hp, t: int) -> None:
+    """oracle.adamw over the arrays, in element ranges on the host threads."""
+    def one(r):
+        a, b = r
+        oracle.adamw(g[a:b], p[a:b], m[a:b], v[a:b], coef, hp.lr, hp.beta1, hp.beta2, hp.eps,
+                     hp.weight_decay, t)
+    list(pool().map(one, _parts(g.size, HOST_THREADS)))
+
+
+def cast_parallel(p: np.ndarray, pdt: int) -> np.ndarray:
+    """The oracle's round-to-nearest-even of p, in element ranges on the
+    host threads."""
+    out = np.empty(p.size, np.uint16)
+
+    def one(r):
+        a, b = r
+        out[a:b] = oracle.to_low_precision(p[a:b], pdt)
+    list(pool().map(one, _parts(p.size, HOST_THREADS)))
+    return out
+
+
+def gen_host(lo: int, hi: int, total: int, sigma: float, key, dtype=torch.float32,
+             scale: float = 1.0) -> np.ndarray:
+    """Generator values of flat [lo, hi) of a virtual tensor of `total`
+    elements, made on the device and copied to the host (fp32, or 16-bit
+    codes for 16-bit dtypes)."""
+    t = torch.empty(hi - lo, dtype=dtype, device="cuda")
+    W.flat_normal(t, lo, total, sigma, key, scale)
+    return f32(t) if dtype == torch.float32 else u16(t)
+
+
+def equal_or_rel(name: str, got: np.ndarray, ref: np.ndarray, rtol: float = RTOL_STATE) -> int:
+    """got == ref bit for bit, else within rtol element by element;
+    returns how many elements differ in their bits."""
+    if np.array_equal(got.view(np.uint32), ref.view(np.uint32)):
+        return 0
+    assert_rel(name, got, ref, rtol)
+    return int(np.count_nonzero(got.view(np.uint32) != ref.view(np.uint32)))
+
+
+def equal_or_ulp(name: str, got: np.ndarray, ref: np.ndarray) -> int:
+    """16-bit codes equal, else within MAX_ULP_CAST; returns how many differ."""
+    if np.array_equal(got, ref):
+        return 0
+    assert_cast(name, got, ref)
+    return int(np.count_nonzero(got != ref))
+
+
+@dataclass
+class FullReduce:
+    g: np.ndarray                    # the oracle's reduced gradient of [lo, hi), fp32
+    sumsq: float
+    overflow: int
+
+
+def oracle_reduce_full(n_replicas: int, lo: int, hi: int, total: int, sigma: float, key_of,
+                       dtype, inv: float, log: Optional[Callable[[str], None]] = None
+                       ) -> FullReduce:
+    """The oracle's reduce of flat [lo, hi) of every replica, regenerated
+    chunk by chunk, keeping its fp32 result for every element: the sum of
+    squares runs over the elements in index order, as the oracle's one-pass
+    step takes them."""
+    odt = oracle_dtype(dtype)
+    g = np.empty(hi - lo, np.float32)
+    ss, of = 0.0, 0
+    gens = [gen_chunks(lo, hi, total, sigma, key_of(i), dtype) for i in range(n_replicas)]
+    for k, parts in enumerate(zip(*gens)):
+        a, b = parts[0][0], parts[0][1]
+        g_chunk, ss, of = oracle.reduce([x[2] for x in parts], odt, inv, ss, of)
+        g[a - lo:b - lo] = g_chunk
+        if log and k % 8 == 0:
+            log("  oracle reduce: [%d, %d) done" % (a, b))
+    return FullReduce(g, ss, of)
+
+
+def check_every_element(what: str, o_g: np.ndarray, state: Sequence, init_master, coef: float,
+                        hp, ts: Sequence[int], pdt: int, full=None, full_off: int = 0,
+                        grad=None, log: Optional[Callable[[str], None]] = None) -> dict:
+    """Compare a rank's state after AdamW steps `ts` (all on the reduced
+    gradient o_g, the oracle's, of its n = o_g.size real elements) with the
+    oracle's, element by element over the whole shard.
+
+    state: (master, exp_avg, exp_avg_sq), device or host fp32 tensors.
+    init_master(a, b): the initial masters of elements [a, b) as a host fp32
+        array, from the seeded generator; the moments start at zero.
+    full: the 16-bit full buffer (int16 view) whose element full_off + i
+        holds element i's cast; compared with the oracle's encoder of the
+        oracle's master within MAX_ULP_CAST.
+    grad: the device's fp32 reduced gradient, compared bit for bit.
+    Returns counts of elements compared and of elements whose bits differ."""
+    n = o_g.size
+    odt_cast = pdt
+    stats = dict(elements=n, state_bits_differ=0, cast_differ=0)
+    for a in range(0, n, W.CHUNK):
+        b = min(n, a + W.CHUNK)
+        p = np.array(init_master(a, b), dtype=np.float32)          # a copy: updated in place
+        m = np.zeros(b - a, np.float32)
+        v = np.zeros(b - a, np.float32)
+        for t in ts:
+            adamw_parallel(o_g[a:b], p, m, v, coef, hp, t)
+        where = "%s [%d, %d)" % (what, a, b)
+        if grad is not None:
+            assert_bitwise("%s reduced grad" % where, f32(grad[a:b]), o_g[a:b])
+        for name, dev, ref in zip(("master", "exp_avg", "exp_avg_sq"), state, (p, m, v)):
+            stats["state_bits_differ"] += equal_or_rel("%s %s" % (where, name), f32(dev[a:b]),
+                                                       ref)
+        if full is not None:
+            stats["cast_differ"] += equal_or_ulp("%s cast" % where,
+                                                 u16(full[full_off + a:full_off + b]),
+                                                 cast_parallel(p, odt_cast))
+        if log and (a // W.CHUNK) % 8 == 0:
+            log("  every element: %s checked" % where)
+    return stats
+
+
 _SHARD13B = None
 
 
 def shard13b_reference(log: Optional[Callable[[str], None]] = None) -> dict:
     """The oracle's side of rank 0 of the 13B/8 workload with the bench's
-    inputs, computed once per process: the norm and overflow flag over every
-    element (inputs regenerated chunk by chunk), and, at a structural sample
-    of the shard, the reduced gradient and the state after AdamW steps 1 and
-    2 on the same gradients (as the bench repeats them)."""
+    inputs, computed once per process: the reduced gradient of every
+    element with the norm and overflow flag over them (inputs regenerated
+    chunk by chunk), the initial masters' generator, and, at a structural
+    sample of the shard, the state after AdamW steps 1 and 2 on the same
+    gradients (as the bench repeats them) for quick first checks."""
     global _SHARD13B
     if _SHARD13B is not None:
         return _SHARD13B
@@ -377,10 +521,11 @@ def shard13b_reference(log: Optional[Callable[[str], None]] = None) -> dict:
     gkey = lambda i: W.grad_key(w, 0, 0, i)
     sample = structural_sample(n, np.random.default_rng(5))
     inv = oracle.inv_scale(1.0)
-    on = oracle_norm_and_sample(w.world_size, 0, n, w.numel, w.grad_sigma, gkey, torch.bfloat16,
-                                sample, inv, log=log)
+    fr = oracle_reduce_full(w.world_size, 0, n, w.numel, w.grad_sigma, gkey, torch.bfloat16, inv,
+                            log=log)
+    on = OracleNorm(fr.sumsq, fr.overflow, [])
     applies, onorm, ocoef = oracle.clip(on.sumsq, w.max_grad_norm)
-    o_g, _, _ = oracle.reduce(on.codes, oracle.BF16, inv)
+    o_g = fr.g[sample].copy()
     p = gather_generated(sample, 0, w.numel, w.master_sigma, W.master_key(w, 0), torch.float32,
                          n).copy()
     m = np.zeros(sample.size, np.float32)
@@ -392,5 +537,7 @@ def shard13b_reference(log: Optional[Callable[[str], None]] = None) -> dict:
         states.append((p.copy(), m.copy(), v.copy()))
     _SHARD13B = dict(w=w, part=part, s=part.shard_numel, n=n, gkey=gkey, sample=sample, inv=inv,
                      overflow=on.overflow, sumsq=on.sumsq, applies=applies, norm=onorm,
-                     coef=ocoef, g=o_g, states=states, hp=hp)
+                     coef=ocoef, g=o_g, g_full=fr.g, states=states, hp=hp,
+                     init_master=lambda a, b: gen_host(a, b, w.numel, w.master_sigma,
+                                                       W.master_key(w, 0)))
     return _SHARD13B

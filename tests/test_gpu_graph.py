@@ -6,7 +6,10 @@ decision is taken on the device, so the whole step can be captured once
 and replayed.  A captured step is replayed 4 times, each time on new
 gradients copied into the captured input buffers and with eager work and
 synchronisations between replays (one replay is poisoned and must skip);
-every replay must equal an eager world's step bit for bit.
+every replay must equal an eager world's step bit for bit.  The step's
+scalars (t, lr, loss scale, ...) are kernel arguments fixed at capture, so
+every replay here is a step at t = 1 and is compared with an eager step at
+t = 1; a caller whose t or scale changes re-captures.
 """
 import pytest
 import torch

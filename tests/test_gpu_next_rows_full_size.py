@@ -4,9 +4,9 @@ configurations, the benchmark times them.
 - Offload (`bench.py --workload offload`): rank 0 of the 13B/8 workload with
   its fp32 state in pinned host memory.  Pass 1 and the combine run on the
   GPU, zero_offload_apply does the rest; two steps on the same gradients.
-  The oracle's norm over every element and its AdamW at a structural sample
-  decide; every cast equals the round-to-nearest-even of its host master,
-  and nothing outside the rank's slice is written.
+  The oracle's reduce, AdamW and cast over every element decide (a
+  structural sample is checked first), and nothing outside the rank's
+  slice is written.
 - ZeRO-3 gather (`--workload zero3`): the 13B model's bf16 parameters as 8
   rank shards, walked as 40 layers with prefetch.  Every layer equals its
   flat range of the parameter buffer (the definition: the shards laid end
@@ -18,19 +18,20 @@ configurations, the benchmark times them.
   padding is zero.
 - Two state sets (`--state-buffers 2`): the 13B/8 step read from one set
   and written to the other equals the same step in place, bit for bit over
-  every element of the state and of the cast slice.
+  every element of the state and of the cast slice, and both equal the
+  oracle's two steps over every element.
 - Accumulation per micro-batch (`--micro-batches 4`): rank 0 of the 13B/8
   workload reduces the 8 replicas 4 times into its fp32 slice (the first
   sets it, the others add), over the same gradients each time as the
   bench repeats them, then combines and applies.  The oracle's window over
-  every element of the shard (its norm) and at a structural sample (the
-  reduced gradient and AdamW) decide; the whole slice equals the window
-  summed again in fp32 on the device, and the cast and canary hold.
+  every element of the shard (its norm, its reduced gradient, AdamW and the
+  cast) decides, after a quick check at a structural sample; the canary
+  outside the slice holds.
 - Accumulation before the reduce (`--micro-batches 4 --accumulation
   local`): the rank's own 13e9-element gradient summed 4 times in fp32,
   then one reduce of its shard over 8 fp32 replicas.  The oracle's window
-  sums at a sample of the whole gradient, its norm over every element of
-  the shard and its AdamW at a structural sample decide.
+  sums at a sample of the whole gradient, and its reduce, AdamW and cast
+  over every element of the shard decide.
 """
 import numpy as np
 import pytest
@@ -104,11 +105,11 @@ def test_offload_13b_in_bench_configuration():
         parity.assert_cast("step %d cast (sample)" % t,
                            parity.take(full, sample).numpy().view(np.uint16),
                            oracle.f32_to_bf16(o_p))
-        for a0, b0 in _chunked(n):
-            tmp2 = master[a0:b0].to("cuda")
-            assert torch.equal(full[a0:b0], tmp2.to(torch.bfloat16).view(torch.int16)), \
-                "cast differs in [%d, %d)" % (a0, b0)
-        del tmp2
+        say("step %d: the oracle's update over all %d elements" % (t, n))
+        st = parity.check_every_element("offloaded step %d" % t, oref["g_full"], (master, m, v),
+                                        oref["init_master"], oref["coef"], hp, range(1, t + 1),
+                                        oracle.BF16, full=full, full_off=0, log=say)
+        assert st["elements"] == n
     for a0, b0 in _chunked(part.padded_numel - s, 1 << 30):
         assert bool((full[s + a0:s + b0] == parity.CANARY).all()), "write outside the slice"
     say("offload matches: norm %.6f" % info.norm)
@@ -239,6 +240,7 @@ def test_local_accumulation_13b_in_bench_configuration():
     sample = parity.structural_sample(n, rng)
     inv = oracle.inv_scale(1.0)
     ss, of = 0.0, 0
+    o_g_full = np.empty(n, np.float32)
     vals = [np.zeros(sample.size, np.float32) for _ in range(w.world_size)]
     buf16 = torch.empty(W.CHUNK, dtype=torch.bfloat16, device="cuda")
     buf32 = torch.empty(W.CHUNK, dtype=torch.float32, device="cuda")
@@ -250,7 +252,7 @@ def test_local_accumulation_13b_in_bench_configuration():
         for i in range(1, w.world_size):
             W.flat_normal(buf32[:b - a], a, w.numel, w.grad_sigma * K, gkey(i))
             reps.append(buf32[:b - a].cpu().numpy())
-        _, ss, of = oracle.reduce_f32(reps, inv, ss, of)
+        o_g_full[a:b], ss, of = oracle.reduce_f32(reps, inv, ss, of)
         sel = (sample >= a) & (sample < b)
         for i in range(w.world_size):
             vals[i][sel] = reps[i][sample[sel] - a]
@@ -273,14 +275,14 @@ def test_local_accumulation_13b_in_bench_configuration():
                           parity.RTOL_STATE)
     parity.assert_cast("cast (sample)", parity.take(full, sample).numpy().view(np.uint16),
                        oracle.f32_to_bf16(o_p))
-    # whole-buffer properties: the fp32 sum in replica order, the cast, the canary
-    for a, b in _chunked(n):
-        sum_ = acc[a:b].clone()
-        for x in peers:
-            sum_ += x[a:b]
-        sum_ *= float(inv)
-        assert torch.equal(sum_, gdev[a:b]), "reduced gradient differs in [%d, %d)" % (a, b)
-        assert torch.equal(full[a:b], master[a:b].to(torch.bfloat16).view(torch.int16))
+    # every element: the oracle's reduced gradient, AdamW and cast
+    say("the oracle's update over all %d elements" % n)
+    st = parity.check_every_element(
+        "local accumulation", o_g_full, (master, m, v),
+        lambda a, b: parity.gen_host(a, b, w.numel, w.master_sigma, W.master_key(w, 0)), ocoef,
+        hp, (1,), oracle.BF16, full=full, full_off=0, grad=gdev, log=say)
+    assert st["elements"] == n
+    del o_g_full
     for a, b in _chunked(P - s, 1 << 30):
         assert bool((full[s + a:s + b] == parity.CANARY).all()), "write outside the slice"
     say("local accumulation matches: norm %.6f (oracle %.6f)" % (info.norm, onorm))
@@ -329,6 +331,7 @@ def test_reduced_accumulation_13b_in_bench_configuration():
     sample = parity.structural_sample(n, rng)
     inv = oracle.inv_scale(1.0)
     ss, of = 0.0, 0
+    o_g_full = np.empty(n, np.float32)
     codes = [np.empty(sample.size, np.uint16) for _ in range(nrep)]
     gens = [parity.gen_chunks(0, n, w.numel, w.grad_sigma, gkey(i), torch.bfloat16)
             for i in range(nrep)]
@@ -342,6 +345,7 @@ def test_reduced_accumulation_13b_in_bench_configuration():
                                                   ss if last else 0.0, of if last else 0)
             if last:
                 ss, of = r_ss, r_of
+        o_g_full[a:b] = g_chunk
         sel = (sample >= a) & (sample < b)
         for i in range(nrep):
             codes[i][sel] = reps[i][sample[sel] - a]
@@ -369,20 +373,15 @@ def test_reduced_accumulation_13b_in_bench_configuration():
     parity.assert_cast("cast (sample)", parity.take(full, sample).numpy().view(np.uint16),
                        oracle.f32_to_bf16(o_p))
 
-    # whole-buffer properties: the window summed again in fp32 (replica
-    # order, one unscale per micro-batch, micro-batches added in order), the
-    # cast of every element, and nothing written outside the rank's slice
-    for a, b in _chunked(n):
-        x = grads[0][a:b].float()
-        for i in range(1, nrep):
-            x += grads[i][a:b].float()
-        x *= float(inv)
-        win = x.clone()
-        for j in range(1, K):
-            win += x
-        assert torch.equal(win, gdev[a:b]), "window differs in [%d, %d)" % (a, b)
-        assert torch.equal(full[a:b], master[a:b].to(torch.bfloat16).view(torch.int16))
-    del x, win
+    # every element: the oracle's window, AdamW and cast; nothing written
+    # outside the rank's slice
+    say("the oracle's update over all %d elements" % n)
+    st = parity.check_every_element(
+        "accumulation per micro-batch", o_g_full, (master, m, v),
+        lambda a, b: parity.gen_host(a, b, w.numel, w.master_sigma, W.master_key(w, 0)), ocoef,
+        hp, (1,), oracle.BF16, full=full, full_off=0, grad=gdev, log=say)
+    assert st["elements"] == n
+    del o_g_full
     for a, b in _chunked(part.padded_numel - s, 1 << 30):
         assert bool((full[s + a:s + b] == parity.CANARY).all()), "write outside the slice"
     say("accumulation per micro-batch matches: norm %.6f (oracle %.6f)" % (info.norm, onorm))
@@ -435,6 +434,15 @@ def test_two_state_sets_13b_equal_in_place():
         assert bool((x[n:] == 7.0).all()), "%s: the other set's padding was written" % name
     for lo, hi in _chunked(s):
         assert torch.equal(cast_b[lo:hi].view(torch.int16), full[lo:hi].view(torch.int16))
-    say("two state sets equal in place: norm %.6f" % i1.norm)
+    # and both equal the oracle's two steps, every element
+    oref = parity.shard13b_reference(log=say)
+    assert (bool(i1.clipped), i1.overflow) == (oref["applies"], 0)
+    assert abs(i1.norm - oref["norm"]) <= parity.RTOL_NORM * oref["norm"]
+    say("the oracle's two steps over all %d elements" % n)
+    st = parity.check_every_element("second state set after step 2", oref["g_full"], b,
+                                    oref["init_master"], oref["coef"], hp, (1, 2), oracle.BF16,
+                                    full=full.view(torch.int16), full_off=0, log=say)
+    assert st["elements"] == n
+    say("two state sets equal in place and the oracle: norm %.6f" % i1.norm)
     del grads, a_p, a_m, a_v, b, full, ws, cast_b
     _free()

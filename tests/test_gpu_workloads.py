@@ -4,14 +4,16 @@ The encoder layer (67M params, 10 steps) and the fp16 scaler run (50M
 params, 200 steps) are compared with the oracle element by element over
 their whole state.  The 13B/8 shard runs in the launch configuration the
 bench times, and the ragged 2000-tensor workload runs bucketed and flattened
-over a world of 8 ranks (2.18e9 params).  For those two the oracle
-regenerates the inputs chunk by chunk to take its own norm over every
-element, then evaluates AdamW on a sample (block and XCD-range edges plus
-65,536 random elements); every element is also covered by whole-buffer
-properties (the reduced gradient against a torch fp32 sum in replica order,
-the cast against torch's round-to-nearest-even, the full buffer outside the
-rank's slice untouched, the flattened buffers against the generator).
-Each case prints its progress before and while it touches the GPU.
+over a world of 8 ranks (2.18e9 params).  For those, and for a shard beyond
+2^31 elements, the oracle regenerates the inputs chunk by chunk and takes
+its reduce over every element (its norm, overflow flag and fp32 reduced
+gradient), then its AdamW and cast over every element, a chunk at a time,
+split over host threads; every element of the reduced gradient, master,
+both moments and the cast is compared with the device's.  A structural
+sample (block and XCD-range edges plus random elements) is checked first,
+as a quick pre-check, and the full buffer outside the ranks' slices must
+keep its canary.  Each case prints its progress before and while it
+touches the GPU.
 """
 import numpy as np
 import pytest
@@ -113,16 +115,6 @@ def test_13b_shard_in_bench_configuration():
     gdev = ws[:4 * s].view(torch.float32)
     parity.assert_bitwise("reduced grad (sample)", parity.take(gdev, sample).numpy(), o_g)
 
-    # whole-buffer properties of pass 1: the fp32 sum in replica order
-    say("whole-buffer checks")
-    for a, b in _chunked(n):
-        acc = grads[0][a:b].float()
-        for i in range(1, nrep):
-            acc += grads[i][a:b].float()
-        acc *= float(inv)
-        assert torch.equal(acc, gdev[a:b]), "reduced gradient differs in [%d, %d)" % (a, b)
-    del acc
-
     for t in (1, 2):
         if t == 2:
             say("step 2 (same gradients, as the bench repeats)")
@@ -135,10 +127,15 @@ def test_13b_shard_in_bench_configuration():
                               ref, parity.RTOL_STATE)
         got = parity.take(full, sample).numpy().view(np.uint16)
         parity.assert_cast("step %d cast (sample)" % t, got, oracle.f32_to_bf16(o_p))
-        # the cast of every element is the round-to-nearest-even of its master
-        for a, b in _chunked(n):
-            assert torch.equal(full[a:b], master[a:b].to(torch.bfloat16).view(torch.int16)), \
-                "cast differs in [%d, %d)" % (a, b)
+        # every element: the oracle's AdamW steps 1..t and its cast
+        say("step %d: the oracle's update over all %d elements" % (t, n))
+        st = parity.check_every_element("step %d" % t, oref["g_full"], (master, m, v),
+                                        oref["init_master"], oref["coef"], hp, range(1, t + 1),
+                                        oracle.BF16, full=full, full_off=0,
+                                        grad=gdev if t == 1 else None, log=say)
+        assert st["elements"] == n == 1_625_000_064
+        say("step %d: %d elements equal the oracle (%d state values and %d casts not bit-equal)"
+            % (t, st["elements"], st["state_bits_differ"], st["cast_differ"]))
     # nothing written outside rank 0's real elements
     for a, b in _chunked(part.padded_numel - s, 1 << 30):
         assert bool((full[s + a:s + b] == parity.CANARY).all()), "write outside the slice"
@@ -188,12 +185,15 @@ def test_ragged_bucketed_workload():
     # each rank's own block and XCD-range edges, both ends, random elements
     sample = np.unique(np.concatenate(
         [r * s + parity.structural_sample(world.valid[r], rng, n_random=8192) for r in range(N)]))
-    say("oracle: reduce over %d elements x %d replicas, %d sampled" % (P, N, sample.size))
+    say("oracle: reduce over %d elements x %d replicas" % (P, N))
     inv = oracle.inv_scale(1.0)
-    on = parity.oracle_norm_and_sample(N, 0, P, P, w.grad_sigma, gkey, torch.bfloat16, sample,
-                                       inv, log=say)
-    applies, onorm, ocoef = oracle.clip(on.sumsq, w.max_grad_norm)
-    o_g, _, _ = oracle.reduce(on.codes, oracle.BF16, inv)
+    fr = parity.oracle_reduce_full(N, 0, P, P, w.grad_sigma, gkey, torch.bfloat16, inv, log=say)
+    assert fr.overflow == 0
+    applies, onorm, ocoef = oracle.clip(fr.sumsq, w.max_grad_norm)
+    # the sample first, as a quick check
+    real = sample < P
+    sample = sample[real]
+    o_g = fr.g[sample].copy()
     o_p = parity.gather_generated(sample, 0, P, 0.02, W.master_key(w, 0), torch.float32, P).copy()
     o_m = np.zeros(sample.size, np.float32)
     o_v = np.zeros(sample.size, np.float32)
@@ -223,11 +223,20 @@ def test_ragged_bucketed_workload():
     full = world.full_params.view(torch.int16)
     parity.assert_cast("cast (sample)", parity.take(full, sample).numpy().view(np.uint16),
                        oracle.f32_to_bf16(o_p))
+    # every element of every rank: the oracle's reduced gradient, AdamW and cast
+    total = 0
     for r in range(N):
         lo, n = r * s, world.valid[r]
-        assert torch.equal(full[lo:lo + n], world.master[r][:n].to(torch.bfloat16).view(torch.int16))
+        say("rank %d: the oracle's update over all %d elements" % (r, n))
+        st = parity.check_every_element(
+            "rank %d" % r, fr.g[lo:lo + n], (world.master[r], world.exp_avg[r], world.exp_avg_sq[r]),
+            lambda a, b, lo=lo: parity.gen_host(lo + a, lo + b, P, 0.02, W.master_key(w, 0)),
+            ocoef, hp, (1,), oracle.BF16, full=full, full_off=lo, grad=world.reduced_grad(r))
+        total += st["elements"]
         assert bool((full[lo + n:lo + s] == parity.CANARY).all()), "padding written, rank %d" % r
-    say("ragged workload matches: norm %.6f (oracle %.6f)" % (res.norm, onorm))
+    assert total == P == 2_184_105_843
+    say("ragged workload matches over all %d elements: norm %.6f (oracle %.6f)"
+        % (total, res.norm, onorm))
 
 
 def test_shard_beyond_2_pow_31_elements():
@@ -248,10 +257,10 @@ def test_shard_beyond_2_pow_31_elements():
         parity.structural_sample(P, rng, n_random=1 << 15),
         (1 << 31) + np.arange(-4, 5, dtype=np.int64), np.arange(P - 7, P, dtype=np.int64)]))
     inv = oracle.inv_scale(1.0)
-    on = parity.oracle_norm_and_sample(R, 0, P, P, 1e-3, gkey, torch.bfloat16, sample, inv,
-                                       log=say)
-    applies, onorm, ocoef = oracle.clip(on.sumsq, 1.0)
-    o_g, _, _ = oracle.reduce(on.codes, oracle.BF16, inv)
+    fr = parity.oracle_reduce_full(R, 0, P, P, 1e-3, gkey, torch.bfloat16, inv, log=say)
+    assert fr.overflow == 0
+    applies, onorm, ocoef = oracle.clip(fr.sumsq, 1.0)
+    o_g = fr.g[sample].copy()
     o_p = parity.gather_generated(sample, 0, P, 0.02, ("big-master",), torch.float32, P).copy()
     o_m = np.zeros(sample.size, np.float32)
     o_v = np.zeros(sample.size, np.float32)
@@ -272,11 +281,11 @@ def test_shard_beyond_2_pow_31_elements():
     full = world.full_params.view(torch.int16)
     parity.assert_cast("cast (sample)", parity.take(full, sample).numpy().view(np.uint16),
                        oracle.f32_to_bf16(o_p))
-    g = world.reduced_grad(0)
-    for a, b in _chunked(P):
-        acc = world.grads[0][a:b].float()
-        acc += world.grads[1][a:b].float()
-        assert torch.equal(acc, g[a:b]), "reduced gradient differs in [%d, %d)" % (a, b)
-        assert torch.equal(full[a:b], world.master[0][a:b].to(torch.bfloat16).view(torch.int16))
+    say("the oracle's update over all %d elements" % P)
+    st = parity.check_every_element(
+        "beyond 2^31", fr.g, (world.master[0], world.exp_avg[0], world.exp_avg_sq[0]),
+        lambda a, b: parity.gen_host(a, b, P, 0.02, ("big-master",)), ocoef, Hyper(), (1,),
+        oracle.BF16, full=full, full_off=0, grad=world.reduced_grad(0), log=say)
+    assert st["elements"] == P
     assert bool((full[P:s] == parity.CANARY).all())
-    say("shard beyond 2^31 matches: norm %.6f" % res.norm)
+    say("shard beyond 2^31 matches over all %d elements: norm %.6f" % (P, res.norm))
