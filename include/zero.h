@@ -332,6 +332,34 @@ int zero_shard_step(const zero_step_args* a, double peer_sumsq,
                     int32_t peer_overflow, zero_step_info* info, void* stream);
 
 /* ------------------------------------------------------------------------
+ * The step without any allocation, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, and harnesses
+ * that forbid hipMalloc.  It is zero_shard_step with the workspace taken
+ * from a scratch array inside the library instead of from the caller: one
+ * array of 67,375,616 bytes per GPU (the workspace of a
+ * ZERO_NOALLOC_MAX_SHARD-element shard), created with the library's code
+ * on each GPU that runs it and held until the process ends.  The call
+ * itself allocates nothing (no hipMalloc, no allocating library routine).
+ *
+ * Arguments as zero_shard_step, except: a->workspace must be NULL and
+ * a->workspace_bytes 0; a->accumulate must be 0 (the scratch keeps no
+ * accumulation window between calls); shard_numel at most
+ * ZERO_NOALLOC_MAX_SHARD.  Every call on one GPU uses that GPU's one array:
+ * calls queued on one stream are ordered and safe, but two calls that may
+ * run at the same time on one GPU (different streams, different host
+ * threads) race on it and give wrong results.  The array keeps the last
+ * call's contents; nothing in it has to start at zero, since every step
+ * writes all it reads.  The first call on a device looks up the array's
+ * address there.
+ * Errors: as zero_shard_step; a non-NULL workspace or accumulate set ->
+ * ZERO_EINVAL; shard_numel > ZERO_NOALLOC_MAX_SHARD -> ZERO_ESIZE; the
+ * address lookup failing -> ZERO_EDEVICE. */
+#define ZERO_NOALLOC_MAX_SHARD 16777216LL
+
+int zero_shard_step_noalloc(const zero_step_args* a, double peer_sumsq, int32_t peer_overflow,
+                            zero_step_info* info, void* stream);
+
+/* ------------------------------------------------------------------------
  * Dynamic loss scaler for fp16 ([P1] §3.3: loss_scale_window 100,
  * hysteresis 2; [P1] §5.1: initial_scale_power 16, min_loss_scale 1).  The
  * pages give only these knobs; the rule is this library's reading:

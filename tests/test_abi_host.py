@@ -490,3 +490,33 @@ def test_empty_rank_may_pass_no_replica_array():
     codes = eval(r.stdout.strip().splitlines()[-1])
     assert all(c in (Z.ZERO_OK, Z.ZERO_EDEVICE) for c in codes), codes
 
+
+# ------------------------------------------------- the allocation-free step
+@pytest.mark.parametrize("kw,code", [kc for kc in BAD if "workspace" not in kc[0]])
+def test_noalloc_step_rejects_bad_arguments_before_any_work(kw, code):
+    if kw.get("replica_grads") == []:
+        return                                  # the binding cannot build that struct
+    a = good_args(workspace=None, **kw)
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_shard_step_noalloc(a, stream=0)
+    assert e.value.code == code, Z.zero_last_error()
+
+
+def test_noalloc_step_own_limits():
+    # A caller's workspace, an accumulation window and shards beyond the
+    # scratch array are refused before the scratch address is even looked up.
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_shard_step_noalloc(good_args(), stream=0)
+    assert e.value.code == Z.ZERO_EINVAL and "workspace must be NULL" in Z.zero_last_error()
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_shard_step_noalloc(good_args(workspace=None, accumulate=True), stream=0)
+    assert e.value.code == Z.ZERO_EINVAL and "accumulate" in Z.zero_last_error()
+    big = Z.ZERO_NOALLOC_MAX_SHARD + 8
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_shard_step_noalloc(good_args(workspace=None, shard_numel=big, valid_numel=0),
+                                  stream=0)
+    assert e.value.code == Z.ZERO_ESIZE
+    # the largest accepted shard's workspace is what the scratch array holds
+    assert Z.zero_shard_workspace_bytes(Z.ZERO_NOALLOC_MAX_SHARD) == 67_375_616
+    assert Z.zero_shard_workspace_bytes(Z.ZERO_NOALLOC_MAX_SHARD - 8) <= 67_375_616
+

@@ -15,7 +15,7 @@ from typing import Optional, Sequence
 from . import _abi
 from ._abi import (ZERO_BF16, ZERO_CKPT_MAGIC, ZERO_CKPT_VERSION, ZERO_EALIGN, ZERO_EDEVICE,
                    ZERO_EINVAL, ZERO_ESIZE, ZERO_FP16, ZERO_FP32, ZERO_MAX_REPLICAS,
-                   ZERO_OK, ZeroError,
+                   ZERO_NOALLOC_MAX_SHARD, ZERO_OK, ZeroError,
                    check, lib, zero_bucket_t, zero_ckpt_header_t, zero_global_t,
                    zero_loss_scaler_t, zero_offload_staging_t, zero_partition_t,
                    zero_repartition_piece_t, zero_step_args, zero_step_info,
@@ -23,13 +23,13 @@ from ._abi import (ZERO_BF16, ZERO_CKPT_MAGIC, ZERO_CKPT_VERSION, ZERO_EALIGN, Z
 
 __all__ = [
     "ZERO_OK", "ZERO_EINVAL", "ZERO_EALIGN", "ZERO_ESIZE", "ZERO_EDEVICE",
-    "ZERO_FP16", "ZERO_BF16", "ZERO_FP32", "ZERO_MAX_REPLICAS",
+    "ZERO_FP16", "ZERO_BF16", "ZERO_FP32", "ZERO_MAX_REPLICAS", "ZERO_NOALLOC_MAX_SHARD",
     "ZeroError", "lib",
     "zero_last_error", "zero_partition", "zero_partition_valid_numel",
     "zero_bucket_plan", "zero_bucket_flatten", "zero_shard_workspace_bytes",
     "zero_partials_bytes", "zero_shard_reduce", "zero_shard_accumulate",
     "zero_accumulate_local", "zero_shard_combine",
-    "zero_shard_apply", "zero_shard_step", "zero_loss_scaler_init",
+    "zero_shard_apply", "zero_shard_step", "zero_shard_step_noalloc", "zero_loss_scaler_init",
     "zero_loss_scaler_update", "zero_ckpt_header_make", "zero_ckpt_header_check",
     "zero_repartition", "zero_repartition_plan", "zero_gather_params", "zero_offload_apply",
     "zero_host_adamw", "zero_host_threads",
@@ -305,6 +305,18 @@ def zero_shard_step(args, peer_sumsq: float = 0.0, peer_overflow: bool = False,
     check(lib().zero_shard_step(ctypes.byref(_args(args)), peer_sumsq, 1 if peer_overflow else 0,
                                 ctypes.byref(info) if info is not None else None,
                                 _stream(stream)), "zero_shard_step")
+    return info
+
+
+def zero_shard_step_noalloc(args, peer_sumsq: float = 0.0, peer_overflow: bool = False,
+                            want_info: bool = False, stream=None) -> Optional[zero_step_info]:
+    """zero_shard_step with the library's own scratch memory as workspace
+    (args.workspace must be None); allocates nothing."""
+    info = zero_step_info() if want_info else None
+    check(lib().zero_shard_step_noalloc(ctypes.byref(_args(args)), peer_sumsq,
+                                        1 if peer_overflow else 0,
+                                        ctypes.byref(info) if info is not None else None,
+                                        _stream(stream)), "zero_shard_step_noalloc")
     return info
 
 

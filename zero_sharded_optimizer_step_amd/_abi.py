@@ -21,6 +21,7 @@ ZERO_FP16 = 1
 ZERO_BF16 = 2
 ZERO_FP32 = 3
 ZERO_MAX_REPLICAS = 64
+ZERO_NOALLOC_MAX_SHARD = 16777216
 
 i32, i64, f32, f64, vp, sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                               ctypes.c_double, ctypes.c_void_p, ctypes.c_size_t)
@@ -107,6 +108,8 @@ _PROTOTYPES = {
     "zero_shard_apply": (ctypes.c_int, [ctypes.POINTER(zero_step_args), vp, vp]),
     "zero_shard_step": (ctypes.c_int, [ctypes.POINTER(zero_step_args), f64, i32,
                                        ctypes.POINTER(zero_step_info), vp]),
+    "zero_shard_step_noalloc": (ctypes.c_int, [ctypes.POINTER(zero_step_args), f64, i32,
+                                               ctypes.POINTER(zero_step_info), vp]),
     "zero_loss_scaler_init": (ctypes.c_int, [i32, i32, i32, f64,
                                              ctypes.POINTER(zero_loss_scaler_t)]),
     "zero_loss_scaler_update": (ctypes.c_int, [ctypes.POINTER(zero_loss_scaler_t), i32,

@@ -18,6 +18,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 #include <vector>
 
 #include "zero_internal.h"
@@ -687,6 +688,43 @@ int run_step(const zero_step_args* a, double peer_sumsq, int32_t peer_overflow, 
 
 using namespace zero;
 
+// ---------------------------------------------------- allocation-free step
+// The workspace of zero_shard_step_noalloc: one array per GPU, loaded with
+// the library's code object and held until the process ends, sized for the
+// largest shard that call accepts.  Host code never passes its name to a
+// kernel (on the host it is only a stand-in for the symbol); it takes the
+// device address that hipGetSymbolAddress returns for the current device.
+constexpr size_t kNoAllocBytes = ws_total_bytes(ZERO_NOALLOC_MAX_SHARD);
+static_assert(kNoAllocBytes == 67375616, "scratch: 64 MiB of fp32 gradient plus partials");
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];       // device address of `scratch`, per device
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device and kept.
+int noalloc_scratch(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(ZERO_EDEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(ZERO_EDEVICE, "device %d is beyond the %d this library tracks", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(ZERO_EDEVICE, "hipGetSymbolAddress of the scratch array on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return ZERO_OK;
+}
+}  // namespace
+
 
 extern "C" {
 
@@ -776,6 +814,29 @@ int zero_shard_step(const zero_step_args* a, double peer_sumsq, int32_t peer_ove
     if (rc) return rc;
     if (!(peer_sumsq >= 0.0)) return fail(ZERO_EINVAL, "peer_sumsq must be >= 0 (got NaN or negative)");
     return run_step(a, peer_sumsq, peer_overflow, info, static_cast<hipStream_t>(stream));
+}
+
+int zero_shard_step_noalloc(const zero_step_args* a, double peer_sumsq, int32_t peer_overflow,
+                            zero_step_info* info, void* stream) {
+    clear_error();
+    int rc = validate_step_args(a, false);
+    if (rc) return rc;
+    if (a->workspace || a->workspace_bytes)
+        return fail(ZERO_EINVAL, "workspace must be NULL and workspace_bytes 0: this call uses the "
+                                 "library's own scratch memory");
+    if (a->accumulate)
+        return fail(ZERO_EINVAL, "accumulate must be 0: the scratch memory holds no accumulation "
+                                 "window between calls");
+    if (a->shard_numel > ZERO_NOALLOC_MAX_SHARD)
+        return fail(ZERO_ESIZE, "shard_numel %lld exceeds ZERO_NOALLOC_MAX_SHARD (%lld)",
+                    (long long)a->shard_numel, (long long)ZERO_NOALLOC_MAX_SHARD);
+    if (!(peer_sumsq >= 0.0)) return fail(ZERO_EINVAL, "peer_sumsq must be >= 0 (got NaN or negative)");
+    void* ws = nullptr;
+    if ((rc = noalloc_scratch(&ws))) return rc;
+    zero_step_args b = *a;
+    b.workspace = ws;
+    b.workspace_bytes = kNoAllocBytes;
+    return run_step(&b, peer_sumsq, peer_overflow, info, static_cast<hipStream_t>(stream));
 }
 
 int zero_bucket_flatten(const zero_tensor_slot_t* slots, int32_t n_tensors, const void* const* src_dev,
