@@ -71,6 +71,11 @@ def parse():
                     help="shard13b: 1 updates one fp32 state set in place (the default); "
                          "2 keeps two sets and alternates them, so pass 2 reads one and "
                          "writes the other")
+    ap.add_argument("--state-layout", default="separate", choices=["separate", "tiled"],
+                    help="shard13b: 'separate' keeps master, exp_avg and exp_avg_sq in three "
+                         "arrays; 'tiled' keeps them in one array of 256-element tiles "
+                         "(ZERO_STATE_TILED), so the update pass moves two state streams "
+                         "instead of six")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 29,
                     help="elements of the shard the CPU oracle is timed on")
@@ -111,7 +116,7 @@ def log(msg):
 
 
 # ------------------------------------------------------------------ workloads
-def setup_shard13b(torch, Z, W, state_buffers=1):
+def setup_shard13b(torch, Z, W, state_buffers=1, state_layout="separate"):
     w = W.SHARD_13B_OF_8
     part = Z.zero_partition(w.numel, w.world_size, w.alignment)
     s = part.shard_numel
@@ -128,9 +133,18 @@ def setup_shard13b(torch, Z, W, state_buffers=1):
     W.flat_normal(master, 0, w.numel, w.master_sigma, W.master_key(w, 0))
     m = torch.zeros(s, dtype=torch.float32, device=dev)
     v = torch.zeros(s, dtype=torch.float32, device=dev)
-    # the second state set of the ping-pong layout
     alt = None
-    if state_buffers == 2:
+    if state_layout == "tiled":
+        # one tiled array holds all three; the library tiles the initial state
+        tiled = torch.empty(Z.tiled_state_numel(s), dtype=torch.float32, device=dev)
+        Z.zero_state_tile(master, m, v, tiled)
+        torch.cuda.synchronize()
+        del master, v
+        master, m, v = tiled, None, None
+        if state_buffers == 2:
+            alt = (torch.zeros(Z.tiled_state_numel(s), dtype=torch.float32, device=dev), None, None)
+    elif state_buffers == 2:
+        # the second state set of the ping-pong layout
         alt = tuple(torch.zeros(s, dtype=torch.float32, device=dev) for _ in range(3))
     full = torch.zeros(part.padded_numel, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(Z.zero_shard_workspace_bytes(s), dtype=torch.uint8, device=dev)
@@ -141,7 +155,8 @@ def setup_shard13b(torch, Z, W, state_buffers=1):
 
 
 def run_shard13b(args, torch, Z, W):
-    st = setup_shard13b(torch, Z, W, args.state_buffers)
+    st = setup_shard13b(torch, Z, W, args.state_buffers, args.state_layout)
+    layout = Z.ZERO_STATE_TILED if args.state_layout == "tiled" else Z.ZERO_STATE_SEPARATE
     w, s, valid = st["w"], st["s"], st["valid"]
     torch.cuda.synchronize()
 
@@ -155,7 +170,8 @@ def run_shard13b(args, torch, Z, W):
                        replica_grads=st["grads"], master=src[0], exp_avg=src[1],
                        exp_avg_sq=src[2], full_params=st["full"], workspace=st["ws"],
                        lr=w.lr, weight_decay=w.weight_decay, step=t,
-                       max_grad_norm=w.max_grad_norm, accumulate=accumulate)
+                       max_grad_norm=w.max_grad_norm, accumulate=accumulate,
+                       state_layout=layout)
         if len(sets) == 2:
             a.master_out, a.exp_avg_out, a.exp_avg_sq_out = sets[t % 2]
         return a
@@ -874,7 +890,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": W.SHARD_13B_OF_8.name, "shard_numel": r["st"]["s"],
                    "world_size": 8, "replicas": 8, "micro_batches": args.micro_batches,
-                   "state_buffers": args.state_buffers,
+                   "state_buffers": args.state_buffers, "state_layout": args.state_layout,
                    "grad_dtype": "bf16", "param_dtype": "bf16",
                    "lr": 6e-5, "weight_decay": 0.01, "max_grad_norm": 1.0},
         "hbm_gbps": step_gbps,

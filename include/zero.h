@@ -65,6 +65,18 @@ extern "C" {
 /* Largest number of data-parallel replicas one reduce can sum. */
 #define ZERO_MAX_REPLICAS 64
 
+/* Layouts of a rank's fp32 optimizer state (zero_step_args.state_layout).
+ * SEPARATE: three arrays master[s], exp_avg[s], exp_avg_sq[s].
+ * TILED: one array of ceil(s / ZERO_STATE_TILE) tiles, tile k holding
+ *   master, then exp_avg, then exp_avg_sq of elements
+ *   [k*ZERO_STATE_TILE, (k+1)*ZERO_STATE_TILE), ZERO_STATE_TILE values each:
+ *   element i's master is at (i / T) * 3T + i % T, its exp_avg T further
+ *   and its exp_avg_sq 2T further (T = ZERO_STATE_TILE).  The update pass
+ *   then moves two state streams instead of six. */
+#define ZERO_STATE_SEPARATE 0
+#define ZERO_STATE_TILED    1
+#define ZERO_STATE_TILE     256
+
 /* Thread-local text of the last failure on this thread ("" if none). */
 const char* zero_last_error(void);
 
@@ -214,6 +226,14 @@ typedef struct {
     float* master_out;
     float* exp_avg_out;
     float* exp_avg_sq_out;
+    /* ZERO_STATE_SEPARATE (0) or ZERO_STATE_TILED.  Tiled: `master` is the
+     * rank's tiled state (fp32[3 * ZERO_STATE_TILE * ceil(shard_numel /
+     * ZERO_STATE_TILE)], 16-byte aligned) and exp_avg, exp_avg_sq must be
+     * NULL; the optional second set is master_out alone (tiled too), with
+     * exp_avg_out and exp_avg_sq_out NULL.  zero_state_tile and
+     * zero_state_untile convert between the layouts. */
+    int32_t state_layout;
+    int32_t reserved;         /* 0 */
 } zero_step_args;
 
 /* Result of the cross-rank combine, 32 bytes in device memory. */
@@ -440,7 +460,9 @@ typedef struct {
 
 /* a: as for zero_shard_apply (and checked the same way), except that
  * master, exp_avg and exp_avg_sq are HOST pointers (fp32[shard_numel],
- * updated in place); the replica pointers are checked but not read.  global_dev: the combine's zero_global_t (device).  info, if
+ * updated in place; with a->state_layout ZERO_STATE_TILED, master is the
+ * host tiled state and the other two are NULL); the replica pointers are
+ * checked but not read.  global_dev: the combine's zero_global_t (device).  info, if
  * not NULL, receives it.  Errors: as zero_shard_apply; a NULL or short
  * staging buffer, chunk_elems not a positive multiple of 8 -> ZERO_EINVAL;
  * a HIP failure -> ZERO_EDEVICE. */
@@ -533,6 +555,32 @@ int zero_ckpt_header_check(const zero_ckpt_header_t* h, uint64_t file_bytes,
  * pointers -> ZERO_EALIGN; launch -> ZERO_EDEVICE. */
 int zero_repartition(const zero_partition_t* from, const float* const* src_dev,
                      const zero_partition_t* to, float* const* dst_dev, void* stream);
+
+/* Layout conversion of a rank's optimizer state (ZERO_STATE_SEPARATE <->
+ * ZERO_STATE_TILED; the layouts are described at ZERO_STATE_TILE).
+ * zero_state_tile: for i in [0, n), element first + i of the tiled array
+ * `tiled` receives master[i], exp_avg[i] and exp_avg_sq[i];
+ * zero_state_untile: the reverse, element first + i of `tiled` into
+ * master[i], exp_avg[i], exp_avg_sq[i].  A rank's whole state is n =
+ * shard_numel, first = 0; a chunk at a time is fine (checkpoints do that).
+ * Bit copies; device pointers (16-byte aligned), asynchronous on `stream`;
+ * the two sides must not overlap.  Tile slots past the last converted
+ * element are not touched.  Errors: n < 0, first < 0, a NULL pointer
+ * when n > 0 -> ZERO_EINVAL; misalignment -> ZERO_EALIGN; launch ->
+ * ZERO_EDEVICE. */
+int zero_state_tile(const float* master, const float* exp_avg, const float* exp_avg_sq, int64_t n,
+                    float* tiled, int64_t first, void* stream);
+int zero_state_untile(const float* tiled, int64_t first, int64_t n, float* master, float* exp_avg,
+                      float* exp_avg_sq, void* stream);
+
+/* zero_repartition for a ZERO_STATE_TILED state: all three fields of the
+ * state move at once.  src_dev[k] is old rank k's tiled state, dst_dev[j]
+ * new rank j's (to->shard_numel elements' worth of whole tiles, 16-byte
+ * aligned); the new ranks' padding elements are zeroed in all three fields.
+ * The copies follow zero_repartition_plan.  Errors as zero_repartition
+ * ([P2] practice notes: a run resumes under another world size). */
+int zero_repartition_tiled(const zero_partition_t* from, const float* const* src_dev,
+                           const zero_partition_t* to, float* const* dst_dev, void* stream);
 
 /* Where new rank `new_rank` of partition *to finds its real elements under
  * partition *from of the same numel: the read plan of an elastic resume

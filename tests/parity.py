@@ -113,6 +113,7 @@ class Spec:
     # sum each replica's window in fp32 before one reduce (no_sync pattern)
     # instead of reducing every micro-batch into the rank's slice
     local_accumulation: bool = False
+    state_layout: int = Z.ZERO_STATE_SEPARATE     # or Z.ZERO_STATE_TILED
     name: str = "case"
     seed: int = 0
 
@@ -135,7 +136,8 @@ def run(spec: Spec, device="cuda", check_every_step: bool = True,
     pdt = spec.param_dtype or spec.grad_dtype
     local = spec.local_accumulation
     world = SimulatedWorld(spec.numel, spec.world_size, nrep, spec.alignment,
-                           torch.float32 if local else spec.grad_dtype, pdt, device)
+                           torch.float32 if local else spec.grad_dtype, pdt, device,
+                           state_layout=spec.state_layout)
     # local accumulation: the micro-batch gradients live in their own 16-bit
     # buffers and world.grads are the replicas' fp32 window sums
     mbuf = [torch.zeros_like(g, dtype=spec.grad_dtype) for g in world.grads] if local else \
@@ -145,10 +147,13 @@ def run(spec: Spec, device="cuda", check_every_step: bool = True,
     podt = oracle_dtype(pdt)
     # initial state: masters from the generator, zero moments, canary params
     mkey = ("master", spec.name, spec.seed)
+    o_master = []
     for k, r in enumerate(world.ranks):
-        W.flat_normal(world.master[k], r * s, P, spec.master_sigma, mkey)
+        m0 = torch.empty(s, dtype=torch.float32, device=device)
+        W.flat_normal(m0, r * s, P, spec.master_sigma, mkey)
+        world.set_state(k, m0)
+        o_master.append(f32(m0))                         # generator output
     world.full_params.view(torch.int16).fill_(CANARY)
-    o_master = [f32(m) for m in world.master]            # generator output
     o_m = [np.zeros(s, np.float32) for _ in world.ranks]
     o_v = [np.zeros(s, np.float32) for _ in world.ranks]
     o_full = np.full(world.padded, CANARY, np.uint16)
@@ -244,9 +249,10 @@ def _compare(world, info, o_master, o_m, o_v, o_full, odt, step, rep):
         if info.grads:
             assert_bitwise("step %d rank %d reduced grad" % (step, r),
                            f32(world.reduced_grad(k)[:n]), info.grads[r])
-        for name, gpu, ref in (("master", world.master[k], o_master[k]),
-                               ("exp_avg", world.exp_avg[k], o_m[k]),
-                               ("exp_avg_sq", world.exp_avg_sq[k], o_v[k])):
+        sep = world.separate_state(k)
+        for name, gpu, ref in (("master", sep[0], o_master[k]),
+                               ("exp_avg", sep[1], o_m[k]),
+                               ("exp_avg_sq", sep[2], o_v[k])):
             got = f32(gpu)
             eq.append(assert_rel("step %d rank %d %s" % (step, r, name), got[:n], ref[:n],
                                  RTOL_STATE))

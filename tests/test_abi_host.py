@@ -520,3 +520,67 @@ def test_noalloc_step_own_limits():
     assert Z.zero_shard_workspace_bytes(Z.ZERO_NOALLOC_MAX_SHARD) == 67_375_616
     assert Z.zero_shard_workspace_bytes(Z.ZERO_NOALLOC_MAX_SHARD - 8) <= 67_375_616
 
+
+# ------------------------------------------------------ the tiled state layout
+def tiled_args(**kw):
+    d = dict(exp_avg=None, exp_avg_sq=None, state_layout=Z.ZERO_STATE_TILED,
+             master=FakeTensor(0x1000000, 4 * Z.tiled_state_numel(1024)))
+    d.update(kw)
+    return good_args(**d)
+
+
+@pytest.mark.parametrize("kw,code,what", [
+    (dict(exp_avg=FakeTensor(0x200000)), Z.ZERO_EINVAL, "must be NULL"),
+    (dict(exp_avg_sq=FakeTensor(0x300000)), Z.ZERO_EINVAL, "must be NULL"),
+    (dict(master=FakeTensor(0)), Z.ZERO_EINVAL, "NULL"),
+    (dict(master=FakeTensor(0x1000008, 1 << 20)), Z.ZERO_EALIGN, "aligned"),
+    (dict(master_out=FakeTensor(0x1000000, 1 << 20)), Z.ZERO_EINVAL, "output state"),
+    (dict(master_out=FakeTensor(0x2000004, 1 << 20)), Z.ZERO_EALIGN, "master_out"),
+    (dict(state_layout=2), Z.ZERO_EINVAL, "state_layout"),
+])
+def test_tiled_state_arguments_are_checked(kw, code, what):
+    a = tiled_args(**kw)
+    for call in (lambda: Z.zero_shard_step(a, stream=0),
+                 lambda: Z.zero_shard_apply(a, FakeTensor(0x700000), stream=0)):
+        with pytest.raises(Z.ZeroError) as e:
+            call()
+        assert e.value.code == code and what in Z.zero_last_error(), Z.zero_last_error()
+
+
+def test_tiled_state_sizes_and_binding_checks():
+    assert Z.tiled_state_numel(0) == 0
+    assert Z.tiled_state_numel(1) == 768 and Z.tiled_state_numel(256) == 768
+    assert Z.tiled_state_numel(257) == 1536
+    assert Z.tiled_state_numel(1_625_000_064) == 3 * 256 * 6_347_657
+    # the binding refuses a tiled state shorter than its whole tiles
+    with pytest.raises(ValueError):
+        tiled_args(master=FakeTensor(0x1000000, 4 * Z.tiled_state_numel(1024) - 4)).c_args()
+    # a separate-layout call still needs all three arrays
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_shard_step(good_args(exp_avg=None), stream=0)
+    assert e.value.code == Z.ZERO_EINVAL
+
+
+def test_layout_conversions_reject_bad_arguments_before_any_work():
+    L = Z.lib()
+    a, b, c, t = 0x10000, 0x20000, 0x30000, 0x40000
+    assert L.zero_state_tile(a, b, c, 0, None, 0, None) == Z.ZERO_OK         # nothing to do
+    assert L.zero_state_tile(a, b, c, -1, t, 0, None) == Z.ZERO_EINVAL
+    assert L.zero_state_tile(a, b, c, 10, t, -1, None) == Z.ZERO_EINVAL
+    assert L.zero_state_tile(a, None, c, 10, t, 0, None) == Z.ZERO_EINVAL
+    assert L.zero_state_tile(a, b, c + 4, 10, t, 0, None) == Z.ZERO_EALIGN
+    assert L.zero_state_untile(t, 0, 10, a, b, None, None) == Z.ZERO_EINVAL
+    assert L.zero_state_untile(t + 8, 0, 10, a, b, c, None) == Z.ZERO_EALIGN
+    assert L.zero_state_untile(t, 2**62, 2**62, a, b, c, None) == Z.ZERO_EINVAL
+    good = Z.zero_partition(1000, 4, 8)
+    bad = Z.zero_partition(1000, 4, 8)
+    bad.shard_numel = 512
+    ptrs = (_abi.vp * 4)(0x100000, 0x200000, 0x300000, 0x400000)
+    assert L.zero_repartition_tiled(ctypes.byref(bad), ptrs, ctypes.byref(good), ptrs,
+                                    None) == Z.ZERO_EINVAL
+    other = Z.zero_partition(999, 4, 8)
+    assert L.zero_repartition_tiled(ctypes.byref(good), ptrs, ctypes.byref(other), ptrs,
+                                    None) == Z.ZERO_EINVAL
+    mis = (_abi.vp * 4)(0x100000, 0x200004, 0x300000, 0x400000)
+    assert L.zero_repartition_tiled(ctypes.byref(good), mis, ctypes.byref(good), ptrs,
+                                    None) == Z.ZERO_EALIGN

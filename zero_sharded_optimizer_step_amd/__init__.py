@@ -15,7 +15,8 @@ from typing import Optional, Sequence
 from . import _abi
 from ._abi import (ZERO_BF16, ZERO_CKPT_MAGIC, ZERO_CKPT_VERSION, ZERO_EALIGN, ZERO_EDEVICE,
                    ZERO_EINVAL, ZERO_ESIZE, ZERO_FP16, ZERO_FP32, ZERO_MAX_REPLICAS,
-                   ZERO_NOALLOC_MAX_SHARD, ZERO_OK, ZeroError,
+                   ZERO_NOALLOC_MAX_SHARD, ZERO_OK, ZERO_STATE_SEPARATE, ZERO_STATE_TILE,
+                   ZERO_STATE_TILED, ZeroError,
                    check, lib, zero_bucket_t, zero_ckpt_header_t, zero_global_t,
                    zero_loss_scaler_t, zero_offload_staging_t, zero_partition_t,
                    zero_repartition_piece_t, zero_step_args, zero_step_info,
@@ -24,6 +25,7 @@ from ._abi import (ZERO_BF16, ZERO_CKPT_MAGIC, ZERO_CKPT_VERSION, ZERO_EALIGN, Z
 __all__ = [
     "ZERO_OK", "ZERO_EINVAL", "ZERO_EALIGN", "ZERO_ESIZE", "ZERO_EDEVICE",
     "ZERO_FP16", "ZERO_BF16", "ZERO_FP32", "ZERO_MAX_REPLICAS", "ZERO_NOALLOC_MAX_SHARD",
+    "ZERO_STATE_SEPARATE", "ZERO_STATE_TILED", "ZERO_STATE_TILE", "tiled_state_numel",
     "ZeroError", "lib",
     "zero_last_error", "zero_partition", "zero_partition_valid_numel",
     "zero_bucket_plan", "zero_bucket_flatten", "zero_shard_workspace_bytes",
@@ -31,7 +33,8 @@ __all__ = [
     "zero_accumulate_local", "zero_shard_combine",
     "zero_shard_apply", "zero_shard_step", "zero_shard_step_noalloc", "zero_loss_scaler_init",
     "zero_loss_scaler_update", "zero_ckpt_header_make", "zero_ckpt_header_check",
-    "zero_repartition", "zero_repartition_plan", "zero_gather_params", "zero_offload_apply",
+    "zero_repartition", "zero_repartition_plan", "zero_repartition_tiled", "zero_state_tile",
+    "zero_state_untile", "zero_gather_params", "zero_offload_apply",
     "zero_host_adamw", "zero_host_threads",
     "OffloadStaging",
     "StepArgs", "dtype_code", "GLOBAL_BYTES",
@@ -58,6 +61,12 @@ def dtype_code(dtype) -> int:
     if dtype == torch.float32:
         return ZERO_FP32
     raise ValueError("only float16, bfloat16 and float32 are supported, got %s" % dtype)
+
+
+def tiled_state_numel(shard_numel: int) -> int:
+    """fp32 values of a rank's ZERO_STATE_TILED state: whole tiles of
+    master, exp_avg and exp_avg_sq."""
+    return 3 * ZERO_STATE_TILE * (-(-shard_numel // ZERO_STATE_TILE))
 
 
 def _stream(stream) -> Optional[int]:
@@ -198,6 +207,9 @@ class StepArgs:
     master_out: object = None           # optional second state set (ping-pong)
     exp_avg_out: object = None
     exp_avg_sq_out: object = None
+    # ZERO_STATE_TILED: `master` (and `master_out`) hold the tiled state and
+    # exp_avg, exp_avg_sq (and their outputs) are None
+    state_layout: int = ZERO_STATE_SEPARATE
 
     def check_sizes(self, gsize: int) -> None:
         """Every buffer must hold what the step touches in it: valid_numel
@@ -208,9 +220,13 @@ class StepArgs:
             return            # nothing is touched, or the library rejects the call
         for i, r in enumerate(self.replica_grads):
             _need(r, gsize * n, "replica_grads[%d]" % i)
-        for name in ("master", "exp_avg", "exp_avg_sq", "master_out", "exp_avg_out",
-                     "exp_avg_sq_out"):
-            _need(getattr(self, name), 4 * n, name)
+        if self.state_layout == ZERO_STATE_TILED:
+            for name in ("master", "master_out"):
+                _need(getattr(self, name), 4 * tiled_state_numel(n), name)
+        else:
+            for name in ("master", "exp_avg", "exp_avg_sq", "master_out", "exp_avg_out",
+                         "exp_avg_sq_out"):
+                _need(getattr(self, name), 4 * n, name)
         if self.param_shard is not None:
             _need(self.param_shard, 2 * n, "param_shard")
         else:
@@ -248,6 +264,7 @@ class StepArgs:
         a.loss_scale = self.loss_scale
         a.grad_predivide = self.grad_predivide
         a.max_grad_norm = self.max_grad_norm
+        a.state_layout = self.state_layout
         self.check_sizes(4 if a.grad_dtype == ZERO_FP32 else 2)
         self._c = a
         return a
@@ -355,6 +372,48 @@ def zero_repartition(from_part: zero_partition_t, srcs: Sequence, to_part: zero_
             _need(t, 4 * to_part.shard_numel, "dsts[%d]" % j)
     check(lib().zero_repartition(ctypes.byref(from_part), sp, ctypes.byref(to_part), dp,
                                  _stream(stream)), "zero_repartition")
+
+
+def zero_repartition_tiled(from_part: zero_partition_t, srcs: Sequence, to_part: zero_partition_t,
+                           dsts: Sequence, stream=None) -> None:
+    """Move a ZERO_STATE_TILED state (one tiled tensor per rank) from
+    partition from_part to to_part."""
+    if len(srcs) != from_part.world_size or len(dsts) != to_part.world_size:
+        raise ValueError("one tensor per rank of each partition")
+    if from_part.numel == to_part.numel and from_part.world_size >= 1 and to_part.world_size >= 1:
+        for k, t in enumerate(srcs):
+            n_k = max(0, min(from_part.shard_numel, from_part.numel - k * from_part.shard_numel))
+            _need(t, 4 * tiled_state_numel(n_k), "srcs[%d]" % k)
+        for j, t in enumerate(dsts):
+            _need(t, 4 * tiled_state_numel(to_part.shard_numel), "dsts[%d]" % j)
+    sp = (_abi.vp * max(len(srcs), 1))(*[_dptr(t) for t in srcs])
+    dp = (_abi.vp * max(len(dsts), 1))(*[_dptr(t) for t in dsts])
+    check(lib().zero_repartition_tiled(ctypes.byref(from_part), sp, ctypes.byref(to_part), dp,
+                                       _stream(stream)), "zero_repartition_tiled")
+
+
+def zero_state_tile(master, exp_avg, exp_avg_sq, tiled, first: int = 0, n: Optional[int] = None,
+                    stream=None) -> None:
+    """Elements [0, n) of the three separate arrays into elements
+    [first, first + n) of the tiled state (n defaults to master.numel())."""
+    n = master.numel() if n is None else n
+    for t, name in ((master, "master"), (exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq")):
+        _need(t, 4 * n, name)
+    _need(tiled, 4 * tiled_state_numel(first + n), "tiled")
+    check(lib().zero_state_tile(_dptr(master), _dptr(exp_avg), _dptr(exp_avg_sq), n, _dptr(tiled),
+                                first, _stream(stream)), "zero_state_tile")
+
+
+def zero_state_untile(tiled, master, exp_avg, exp_avg_sq, first: int = 0,
+                      n: Optional[int] = None, stream=None) -> None:
+    """Elements [first, first + n) of the tiled state into elements [0, n)
+    of the three separate arrays (n defaults to master.numel())."""
+    n = master.numel() if n is None else n
+    for t, name in ((master, "master"), (exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq")):
+        _need(t, 4 * n, name)
+    _need(tiled, 4 * tiled_state_numel(first + n), "tiled")
+    check(lib().zero_state_untile(_dptr(tiled), first, n, _dptr(master), _dptr(exp_avg),
+                                  _dptr(exp_avg_sq), _stream(stream)), "zero_state_untile")
 
 
 def zero_repartition_plan(from_part: zero_partition_t, to_part: zero_partition_t,

@@ -21,6 +21,9 @@ ZERO_FP16 = 1
 ZERO_BF16 = 2
 ZERO_FP32 = 3
 ZERO_MAX_REPLICAS = 64
+ZERO_STATE_SEPARATE = 0
+ZERO_STATE_TILED = 1
+ZERO_STATE_TILE = 256
 ZERO_NOALLOC_MAX_SHARD = 16777216
 
 i32, i64, f32, f64, vp, sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
@@ -50,7 +53,8 @@ class zero_step_args(ctypes.Structure):
                 ("lr", f64), ("beta1", f64), ("beta2", f64), ("eps", f64),
                 ("weight_decay", f64), ("step", i64), ("loss_scale", f64),
                 ("grad_predivide", f64), ("max_grad_norm", f64), ("param_shard", vp),
-                ("master_out", vp), ("exp_avg_out", vp), ("exp_avg_sq_out", vp)]
+                ("master_out", vp), ("exp_avg_out", vp), ("exp_avg_sq_out", vp),
+                ("state_layout", i32), ("reserved", i32)]
 
 
 class zero_global_t(ctypes.Structure):
@@ -125,6 +129,11 @@ _PROTOTYPES = {
                                              ctypes.POINTER(zero_partition_t), i32,
                                              ctypes.POINTER(zero_repartition_piece_t), i32,
                                              ctypes.POINTER(i32)]),
+    "zero_state_tile": (ctypes.c_int, [vp, vp, vp, i64, vp, i64, vp]),
+    "zero_state_untile": (ctypes.c_int, [vp, i64, i64, vp, vp, vp, vp]),
+    "zero_repartition_tiled": (ctypes.c_int, [ctypes.POINTER(zero_partition_t), ctypes.POINTER(vp),
+                                              ctypes.POINTER(zero_partition_t), ctypes.POINTER(vp),
+                                              vp]),
     "zero_gather_params": (ctypes.c_int, [ctypes.POINTER(zero_partition_t), ctypes.POINTER(vp),
                                           i32, i64, i64, vp, vp]),
     "zero_offload_apply": (ctypes.c_int, [ctypes.POINTER(zero_step_args), vp,

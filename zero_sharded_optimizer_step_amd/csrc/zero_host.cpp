@@ -73,10 +73,18 @@ int validate_step_args(const zero_step_args* a, bool check_workspace) {
     if (check_workspace && !a->workspace) return fail(ZERO_EINVAL, "workspace is NULL");
     if (check_workspace && !aligned16(a->workspace))
         return fail(ZERO_EALIGN, "workspace is not 16-byte aligned");
+    if (a->state_layout != ZERO_STATE_SEPARATE && a->state_layout != ZERO_STATE_TILED)
+        return fail(ZERO_EINVAL, "state_layout %d is not ZERO_STATE_SEPARATE or ZERO_STATE_TILED",
+                    a->state_layout);
+    if (a->reserved != 0) return fail(ZERO_EINVAL, "reserved must be 0");
+    const bool tiled = a->state_layout == ZERO_STATE_TILED;
+    if (tiled && (a->exp_avg || a->exp_avg_sq || a->exp_avg_out || a->exp_avg_sq_out))
+        return fail(ZERO_EINVAL, "a tiled state is `master` (and `master_out`) alone: exp_avg, "
+                                 "exp_avg_sq and their outputs must be NULL");
     // A rank with no real elements reads and writes no element, so its data
     // pointers may be NULL (empty tensors).
     if (a->valid_numel > 0) {
-        if (!a->replica_grad || !a->master || !a->exp_avg || !a->exp_avg_sq ||
+        if (!a->replica_grad || !a->master || (!tiled && (!a->exp_avg || !a->exp_avg_sq)) ||
             (!a->full_params && !a->param_shard))
             return fail(ZERO_EINVAL, "a required pointer is NULL");
         for (int i = 0; i < a->n_replicas; ++i) {
@@ -90,9 +98,16 @@ int validate_step_args(const zero_step_args* a, bool check_workspace) {
     }
     const int n_out = (a->master_out != nullptr) + (a->exp_avg_out != nullptr) +
                       (a->exp_avg_sq_out != nullptr);
-    if (n_out != 0 && n_out != 3)
+    if (tiled) {
+        if (a->master_out && !aligned16(a->master_out))
+            return fail(ZERO_EALIGN, "master_out is not 16-byte aligned");
+        if (a->master_out && a->master_out == a->master)
+            return fail(ZERO_EINVAL, "output state must not be the input state (leave it NULL "
+                                     "to update in place)");
+    } else if (n_out != 0 && n_out != 3) {
         return fail(ZERO_EINVAL, "master_out, exp_avg_out and exp_avg_sq_out are set together");
-    if (n_out == 3) {
+    }
+    if (!tiled && n_out == 3) {
         if (!aligned16(a->master_out) || !aligned16(a->exp_avg_out) || !aligned16(a->exp_avg_sq_out))
             return fail(ZERO_EALIGN, "an output state pointer is not 16-byte aligned");
         if (a->master_out == a->master || a->exp_avg_out == a->exp_avg ||

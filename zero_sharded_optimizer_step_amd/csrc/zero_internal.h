@@ -39,6 +39,12 @@ constexpr int kReduceThreads = 256;        // reduce: 1024 elements per block
 constexpr int kApplyThreads = 64;          // apply: 256 elements per block
 constexpr int kXcds = 8;
 constexpr int kFoldBlocks = 256;           // fixed-size per-rank summary
+constexpr int kStateTile = ZERO_STATE_TILE; // elements per tile of a tiled state
+
+// fp32 values of a rank's tiled state: three per element, whole tiles.
+constexpr size_t tiled_state_floats(int64_t shard_numel) {
+    return 3u * static_cast<size_t>((shard_numel + kStateTile - 1) / kStateTile) * kStateTile;
+}
 
 // One partial sum of squares (fp64) and inf/nan flag.
 struct Partial {

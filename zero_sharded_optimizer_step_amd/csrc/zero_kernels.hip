@@ -324,43 +324,67 @@ __device__ __forceinline__ void adamw1(float g, float& p, float& m, float& v, co
 // buffers into another; the loads are all issued before the stores either
 // way.  Every stream is touched once per step, so loads and stores are all
 // nontemporal.
-template <int PT, bool OOP>
+//
+// TILED: the state is one array of tiles of kStateTile elements, each tile
+// holding master, exp_avg and exp_avg_sq of its elements one after the
+// other (ZERO_STATE_TILED).  A block's 256 elements are exactly one tile,
+// so each wave reads and writes three contiguous 1 KB runs of one 3 KB
+// tile instead of three separate arrays: two state streams instead of six.
+static_assert(kApplyThreads * kQuad == kStateTile, "one apply block is one state tile");
+
+template <int PT, bool OOP, bool TILED>
 __global__ __launch_bounds__(kApplyThreads) void apply_kernel(
     const float* g, const float* p, const float* m, const float* v, float* p2, float* m2, float* v2,
     unsigned short* __restrict__ out, int64_t n_valid, const zero_global_t* __restrict__ glob,
     AdamConsts k, uint32_t group) {
     if (glob->overflow) return;                    // skipped step: touch nothing
-    if constexpr (!OOP) {
+    const int64_t blk = xcd_block(blockIdx.x, group);
+    if constexpr (TILED) {
+        // this block's tile; the quad offsets below are then tile offsets
+        const int64_t tile = blk * (3 * kStateTile);
+        p += tile;
+        m = p + kStateTile;
+        v = p + 2 * kStateTile;
+        if constexpr (OOP) p2 += tile;
+        else p2 = const_cast<float*>(p);
+        m2 = p2 + kStateTile;
+        v2 = p2 + 2 * kStateTile;
+    } else if constexpr (!OOP) {
         p2 = const_cast<float*>(p);
         m2 = const_cast<float*>(m);
         v2 = const_cast<float*>(v);
     }
     const float coef = glob->coef;
-    const int64_t q = xcd_block(blockIdx.x, group) * kApplyThreads + threadIdx.x;
+    const int64_t q = blk * kApplyThreads + threadIdx.x;
     const int64_t full = n_valid / kQuad;
+    // the state's quad index: within the tile, or in the whole array
+    const int64_t sq = TILED ? threadIdx.x : q;
     if (q < full) {
         const f32x4 gq = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g) + q);
-        f32x4 pq = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + q);
-        f32x4 mq = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(m) + q);
-        f32x4 vq = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(v) + q);
+        f32x4 pq = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + sq);
+        f32x4 mq = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(m) + sq);
+        f32x4 vq = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(v) + sq);
         #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float pe = pq[e], me = mq[e], ve = vq[e];
             adamw1(gq[e] * coef, pe, me, ve, k);
             pq[e] = pe; mq[e] = me; vq[e] = ve;
         }
-        __builtin_nontemporal_store(pq, reinterpret_cast<f32x4*>(p2) + q);
-        __builtin_nontemporal_store(mq, reinterpret_cast<f32x4*>(m2) + q);
-        __builtin_nontemporal_store(vq, reinterpret_cast<f32x4*>(v2) + q);
+        __builtin_nontemporal_store(pq, reinterpret_cast<f32x4*>(p2) + sq);
+        __builtin_nontemporal_store(mq, reinterpret_cast<f32x4*>(m2) + sq);
+        __builtin_nontemporal_store(vq, reinterpret_cast<f32x4*>(v2) + sq);
         u32x2 o;
         o.x = pack2<PT>(pq.x, pq.y);
         o.y = pack2<PT>(pq.z, pq.w);
         __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(out) + q);
     } else if (q == full) {
+        // the 1-3 elements after the last complete quad, all in this block's
+        // tile when TILED (a block's quads cover its tile)
         for (int64_t j = q * kQuad; j < n_valid; ++j) {
-            float pj = p[j], mj = m[j], vj = v[j];
+            const int64_t sj = TILED ? j - blk * kStateTile : j;
+            float pj = p[sj], mj = m[sj], vj = v[sj];
             adamw1(g[j] * coef, pj, mj, vj, k);
-            p2[j] = pj; m2[j] = mj; v2[j] = vj;
+            p2[sj] = pj; m2[sj] = mj; v2[sj] = vj;
             out[j] = pack1<PT>(pj);
         }
     }
@@ -486,6 +510,38 @@ __global__ __launch_bounds__(kFlatThreads) void flatten_kernel(FlatBatch b, unsi
     }
 }
 
+// ========================================================= state layouts
+// Moves n elements of a rank's fp32 optimizer state, all three fields,
+// from element src_first of one state to element dst_first of another;
+// either side separate (three arrays) or tiled (ZERO_STATE_TILED), and a
+// NULL source writes zeros.  One thread per element and field: consecutive
+// threads touch consecutive addresses on both sides.  Used for layout
+// conversion and for re-partitioning a tiled state; neither is on the
+// step's path.
+struct StateRef {
+    float* f[3];          // separate: the three arrays; tiled: f[0] is the tiled array
+};
+
+template <bool TILED>
+__device__ __forceinline__ int64_t state_index(int64_t i, int field) {
+    if constexpr (TILED)
+        return (i / kStateTile) * (3 * kStateTile) + field * kStateTile + (i % kStateTile);
+    else
+        return i;
+}
+
+template <bool SRC_TILED, bool DST_TILED>
+__global__ __launch_bounds__(256) void state_move_kernel(StateRef src, int64_t src_first, StateRef dst,
+                                                         int64_t dst_first, int64_t n) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int field = blockIdx.y;
+    if (i >= n) return;
+    const float* sb = SRC_TILED ? src.f[0] : src.f[field];
+    float* db = DST_TILED ? dst.f[0] : dst.f[field];
+    const float x = sb ? sb[state_index<SRC_TILED>(src_first + i, field)] : 0.0f;
+    db[state_index<DST_TILED>(dst_first + i, field)] = x;
+}
+
 // ================================================================ launches
 int launch_error(const char* what) {
     const hipError_t e = hipGetLastError();
@@ -569,19 +625,41 @@ int launch_apply(const zero_step_args* a, const void* global, hipStream_t st) {
     const zero_global_t* gl = static_cast<const zero_global_t*>(global);
     const float* g = static_cast<const float*>(a->workspace);
     const bool oop = a->master_out != nullptr;
+    const bool tiled = a->state_layout == ZERO_STATE_TILED;
     float* p2 = oop ? a->master_out : a->master;
     float* m2 = oop ? a->exp_avg_out : a->exp_avg;
     float* v2 = oop ? a->exp_avg_sq_out : a->exp_avg_sq;
-#define ZERO_APPLY(PT, OOP)                                                                         \
-    hipLaunchKernelGGL((apply_kernel<PT, OOP>), grid, dim3(kApplyThreads), 0, st, g, a->master,      \
-                       a->exp_avg, a->exp_avg_sq, p2, m2, v2, out, a->valid_numel, gl, k, group)
+#define ZERO_APPLY(PT, OOP, TILED)                                                                  \
+    hipLaunchKernelGGL((apply_kernel<PT, OOP, TILED>), grid, dim3(kApplyThreads), 0, st, g,          \
+                       a->master, a->exp_avg, a->exp_avg_sq, p2, m2, v2, out, a->valid_numel, gl, k, \
+                       group)
+#define ZERO_APPLY_LAYOUT(PT, OOP) \
+    do { if (tiled) ZERO_APPLY(PT, OOP, true); else ZERO_APPLY(PT, OOP, false); } while (0)
     if (a->param_dtype == ZERO_BF16) {
-        if (oop) ZERO_APPLY(ZERO_BF16, true); else ZERO_APPLY(ZERO_BF16, false);
+        if (oop) ZERO_APPLY_LAYOUT(ZERO_BF16, true); else ZERO_APPLY_LAYOUT(ZERO_BF16, false);
     } else {
-        if (oop) ZERO_APPLY(ZERO_FP16, true); else ZERO_APPLY(ZERO_FP16, false);
+        if (oop) ZERO_APPLY_LAYOUT(ZERO_FP16, true); else ZERO_APPLY_LAYOUT(ZERO_FP16, false);
     }
+#undef ZERO_APPLY_LAYOUT
 #undef ZERO_APPLY
     return launch_error("apply kernel launch");
+}
+
+// Queue one state move (see state_move_kernel); n >= 0.
+int launch_state_move(const StateRef& src, bool src_tiled, int64_t src_first, const StateRef& dst,
+                      bool dst_tiled, int64_t dst_first, int64_t n, hipStream_t st) {
+    if (n <= 0) return ZERO_OK;
+    if ((n + 255) / 256 > INT32_MAX) return fail(ZERO_EINVAL, "%lld elements in one state move", (long long)n);
+    const dim3 grid(static_cast<unsigned>((n + 255) / 256), 3);
+#define ZERO_MOVE(S, D) \
+    hipLaunchKernelGGL((state_move_kernel<S, D>), grid, dim3(256), 0, st, src, src_first, dst, dst_first, n)
+    if (src_tiled) {
+        if (dst_tiled) ZERO_MOVE(true, true); else ZERO_MOVE(true, false);
+    } else {
+        if (dst_tiled) ZERO_MOVE(false, true); else ZERO_MOVE(false, false);
+    }
+#undef ZERO_MOVE
+    return launch_error("state move kernel launch");
 }
 
 // Copy n ranges of 16-bit values, range t from src(t) to flat elements
@@ -724,7 +802,6 @@ int noalloc_scratch(void** out) {
     return ZERO_OK;
 }
 }  // namespace
-
 
 extern "C" {
 
@@ -947,6 +1024,89 @@ int zero_repartition(const zero_partition_t* from, const float* const* src_dev,
             [&](int32_t q) { return 2 * plan[q].count; },
             reinterpret_cast<unsigned short*>(dst_dev[j]), 2 * s_new, st);
         if (rc) return rc;
+    }
+    return ZERO_OK;
+}
+
+int zero_state_tile(const float* master, const float* exp_avg, const float* exp_avg_sq, int64_t n,
+                    float* tiled, int64_t first, void* stream) {
+    clear_error();
+    if (n < 0 || first < 0) return fail(ZERO_EINVAL, "n %lld or first %lld < 0", (long long)n,
+                                        (long long)first);
+    if (n == 0) return ZERO_OK;
+    if (!master || !exp_avg || !exp_avg_sq || !tiled)
+        return fail(ZERO_EINVAL, "a required pointer is NULL");
+    if (!aligned16(master) || !aligned16(exp_avg) || !aligned16(exp_avg_sq) || !aligned16(tiled))
+        return fail(ZERO_EALIGN, "a pointer is not 16-byte aligned");
+    if (n > (INT64_MAX - first) / 3) return fail(ZERO_EINVAL, "first + n overflows");
+    StateRef src{{const_cast<float*>(master), const_cast<float*>(exp_avg), const_cast<float*>(exp_avg_sq)}};
+    StateRef dst{{tiled, nullptr, nullptr}};
+    return launch_state_move(src, false, 0, dst, true, first, n, static_cast<hipStream_t>(stream));
+}
+
+int zero_state_untile(const float* tiled, int64_t first, int64_t n, float* master, float* exp_avg,
+                      float* exp_avg_sq, void* stream) {
+    clear_error();
+    if (n < 0 || first < 0) return fail(ZERO_EINVAL, "n %lld or first %lld < 0", (long long)n,
+                                        (long long)first);
+    if (n == 0) return ZERO_OK;
+    if (!master || !exp_avg || !exp_avg_sq || !tiled)
+        return fail(ZERO_EINVAL, "a required pointer is NULL");
+    if (!aligned16(master) || !aligned16(exp_avg) || !aligned16(exp_avg_sq) || !aligned16(tiled))
+        return fail(ZERO_EALIGN, "a pointer is not 16-byte aligned");
+    if (n > (INT64_MAX - first) / 3) return fail(ZERO_EINVAL, "first + n overflows");
+    StateRef src{{const_cast<float*>(tiled), nullptr, nullptr}};
+    StateRef dst{{master, exp_avg, exp_avg_sq}};
+    return launch_state_move(src, true, first, dst, false, 0, n, static_cast<hipStream_t>(stream));
+}
+
+int zero_repartition_tiled(const zero_partition_t* from, const float* const* src_dev,
+                           const zero_partition_t* to, float* const* dst_dev, void* stream) {
+    clear_error();
+    if (!from || !to || !src_dev || !dst_dev) return fail(ZERO_EINVAL, "a required pointer is NULL");
+    int rc;
+    if ((rc = check_partition(from, "from"))) return rc;
+    if ((rc = check_partition(to, "to"))) return rc;
+    if (from->numel != to->numel)
+        return fail(ZERO_EINVAL, "partitions cover %lld and %lld elements", (long long)from->numel,
+                    (long long)to->numel);
+    for (int32_t k = 0; k < from->world_size; ++k) {
+        if (zero_partition_valid_numel(from, k) > 0 && !src_dev[k])
+            return fail(ZERO_EINVAL, "src_dev[%d] is NULL", k);
+        if (!aligned16(src_dev[k])) return fail(ZERO_EALIGN, "src_dev[%d] is not 16-byte aligned", k);
+    }
+    for (int32_t j = 0; j < to->world_size; ++j) {
+        if (to->shard_numel > 0 && !dst_dev[j]) return fail(ZERO_EINVAL, "dst_dev[%d] is NULL", j);
+        if (!aligned16(dst_dev[j])) return fail(ZERO_EALIGN, "dst_dev[%d] is not 16-byte aligned", j);
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    std::vector<zero_repartition_piece_t> plan;
+    for (int32_t j = 0; j < to->world_size; ++j) {
+        if (to->shard_numel == 0) break;
+        int32_t n_pieces = 0;
+        rc = zero_repartition_plan(from, to, j, plan.data(), static_cast<int32_t>(plan.size()),
+                                   &n_pieces);
+        if (rc == ZERO_ESIZE) {
+            try {
+                plan.resize(static_cast<size_t>(n_pieces));
+            } catch (...) {
+                return fail(ZERO_ESIZE, "no host memory for a plan of %d pieces", n_pieces);
+            }
+            rc = zero_repartition_plan(from, to, j, plan.data(), n_pieces, &n_pieces);
+        }
+        if (rc) return rc;
+        StateRef dst{{dst_dev[j], nullptr, nullptr}};
+        for (int32_t q = 0; q < n_pieces; ++q) {
+            StateRef src{{const_cast<float*>(src_dev[plan[q].old_rank]), nullptr, nullptr}};
+            if ((rc = launch_state_move(src, true, plan[q].old_offset, dst, true, plan[q].new_offset,
+                                        plan[q].count, st)))
+                return rc;
+        }
+        // the new rank's padding, all three fields, is zeroed
+        const int64_t valid = zero_partition_valid_numel(to, j);
+        StateRef none{{nullptr, nullptr, nullptr}};
+        if ((rc = launch_state_move(none, true, 0, dst, true, valid, to->shard_numel - valid, st)))
+            return rc;
     }
     return ZERO_OK;
 }

@@ -93,6 +93,34 @@ void adamw_range(const HostUpdate& u, int64_t lo, int64_t hi, const float* g, fl
     }
 }
 
+// A rank's host state in either layout (ZERO_STATE_SEPARATE or _TILED).
+struct HostState {
+    float* p;
+    float* m;
+    float* v;
+    bool tiled;       // p is the tiled array; m and v are unused
+};
+
+// Elements [base + lo, base + hi) of the state, with the gradient, and the
+// cast's destination, indexed from base (g[i], out[i] belong to element
+// base + i).  A tiled state is walked one tile at a time, each tile's three
+// fields being three contiguous runs.
+void adamw_span(const HostUpdate& u, int64_t lo, int64_t hi, const float* g, const HostState& s,
+                int64_t base, uint16_t* out) {
+    if (!s.tiled) {
+        adamw_range(u, lo, hi, g, s.p + base, s.m + base, s.v + base, out);
+        return;
+    }
+    for (int64_t i = lo; i < hi;) {
+        const int64_t e = base + i, k = e / kStateTile;
+        const int64_t end = std::min(hi, (k + 1) * kStateTile - base);
+        // p[i] is element e's master: tile k starts at 3 * kStateTile * k
+        float* p = s.p + 2 * kStateTile * k + base;
+        adamw_range(u, i, end, g, p, p + kStateTile, p + 2 * kStateTile, out);
+        i = end;
+    }
+}
+
 // The thread count used when the caller passes 0: OMP_NUM_THREADS when it
 // is set to a positive number, else the CPUs this process may run on, else
 // the hardware's thread count.
@@ -110,16 +138,16 @@ int default_host_threads() {
     return h > 0 ? static_cast<int>(h) : 1;
 }
 
-// Split [0, n) into contiguous ranges of whole 64-byte lines, one per
-// thread, and run them.
-void adamw_parallel(const HostUpdate& u, int64_t n, const float* g, float* p, float* m, float* v,
+// Split elements [base, base + n) into contiguous ranges of whole 64-byte
+// lines, one per thread, and run them; g and out are indexed from base.
+void adamw_parallel(const HostUpdate& u, int64_t n, const float* g, const HostState& s, int64_t base,
                     uint16_t* out, int n_threads) {
     int t = n_threads > 0 ? n_threads : default_host_threads();
     if (t < 1) t = 1;
     const int64_t min_per = int64_t(1) << 16;
     if (static_cast<int64_t>(t) * min_per > n) t = static_cast<int>(std::max<int64_t>(1, n / min_per));
     if (t == 1) {
-        adamw_range(u, 0, n, g, p, m, v, out);
+        adamw_span(u, 0, n, g, s, base, out);
         return;
     }
     const int64_t per = (n + t - 1) / t / 16 * 16 + 16;
@@ -127,7 +155,7 @@ void adamw_parallel(const HostUpdate& u, int64_t n, const float* g, float* p, fl
     pool.reserve(t);
     for (int i = 0; i < t; ++i) {
         const int64_t lo = std::min<int64_t>(n, i * per), hi = std::min<int64_t>(n, lo + per);
-        if (lo < hi) pool.emplace_back(adamw_range, std::cref(u), lo, hi, g, p, m, v, out);
+        if (lo < hi) pool.emplace_back(adamw_span, std::cref(u), lo, hi, g, std::cref(s), base, out);
     }
     for (auto& th : pool) th.join();
 }
@@ -161,8 +189,8 @@ int zero_host_adamw(int64_t n, const float* g, float coef, float* master, float*
         !std::isfinite(weight_decay) || !std::isfinite(coef))
         return fail(ZERO_EINVAL, "a hyper-parameter is out of range");
     HostUpdate u{adam_consts(lr, beta1, beta2, eps, weight_decay, step), coef, param_dtype};
-    adamw_parallel(u, n, g, master, exp_avg, exp_avg_sq, static_cast<uint16_t*>(params_out),
-                   n_threads);
+    const HostState hs{master, exp_avg, exp_avg_sq, false};
+    adamw_parallel(u, n, g, hs, 0, static_cast<uint16_t*>(params_out), n_threads);
     return ZERO_OK;
 }
 
@@ -192,6 +220,7 @@ int zero_offload_apply(const zero_step_args* a, const void* global_dev,
 
     const HostUpdate u{adam_consts(a->lr, a->beta1, a->beta2, a->eps, a->weight_decay, a->step),
                        glob.coef, a->param_dtype};
+    const HostState hs{a->master, a->exp_avg, a->exp_avg_sq, a->state_layout == ZERO_STATE_TILED};
     const int64_t n = a->valid_numel, C = stg->chunk_elems;
     const int64_t n_chunks = (n + C - 1) / C;
     const float* g_dev = static_cast<const float*>(a->workspace);
@@ -231,10 +260,10 @@ int zero_offload_apply(const zero_step_args* a, const void* global_dev,
         if (e != hipSuccess) break;
         const int64_t lo = c * C, len = len_of(c);
         uint16_t* pst = static_cast<uint16_t*>(stg->param_stage[c & 1]);
-        // The host arrays are indexed from the chunk start; the staging
-        // buffers from 0.
-        adamw_parallel(u, len, static_cast<const float*>(stg->grad_stage[c & 1]), a->master + lo,
-                       a->exp_avg + lo, a->exp_avg_sq + lo, pst, stg->n_threads);
+        // The staging buffers hold the chunk's elements from 0; the state
+        // is addressed by element, from the chunk start lo.
+        adamw_parallel(u, len, static_cast<const float*>(stg->grad_stage[c & 1]), hs, lo, pst,
+                       stg->n_threads);
         e = hipMemcpyAsync(out_dev + lo, pst, len * 2, hipMemcpyHostToDevice, up);
         if (e == hipSuccess) e = hipEventRecord(up_done[c & 1], up);
     }

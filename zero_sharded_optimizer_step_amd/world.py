@@ -14,10 +14,12 @@ from typing import Optional, Sequence
 
 import torch
 
-from . import (GLOBAL_BYTES, StepArgs, checkpoint, zero_global_t, zero_partials_bytes,
-               zero_accumulate_local, zero_partition, zero_partition_valid_numel,
-               zero_repartition, zero_shard_accumulate, zero_shard_apply, zero_shard_combine,
-               zero_shard_reduce, zero_shard_workspace_bytes)
+from . import (GLOBAL_BYTES, ZERO_STATE_SEPARATE, ZERO_STATE_TILED, StepArgs, checkpoint,
+               tiled_state_numel, zero_global_t, zero_partials_bytes, zero_accumulate_local,
+               zero_partition, zero_partition_valid_numel, zero_repartition,
+               zero_repartition_tiled, zero_shard_accumulate, zero_shard_apply,
+               zero_shard_combine, zero_shard_reduce, zero_shard_workspace_bytes,
+               zero_state_tile, zero_state_untile)
 
 
 @dataclass
@@ -37,13 +39,15 @@ class SimulatedWorld:
 
     grads[i] holds replica i's flat gradient over the simulated ranks'
     range [lo, hi) of the padded flat space; full_params spans the whole
-    padded space; master/exp_avg/exp_avg_sq[k] are rank ranks[k]'s shard.
+    padded space; master/exp_avg/exp_avg_sq[k] are rank ranks[k]'s shard,
+    or, with state_layout ZERO_STATE_TILED, tiled[k] is its tiled state
+    (and master/exp_avg/exp_avg_sq are None).
     """
 
     def __init__(self, numel: int, world_size: int, n_replicas: Optional[int] = None,
                  alignment: int = 128, grad_dtype=torch.bfloat16, param_dtype=None,
                  device="cuda", ranks: Optional[Sequence[int]] = None,
-                 allocate_grads: bool = True):
+                 allocate_grads: bool = True, state_layout: int = ZERO_STATE_SEPARATE):
         self.part = zero_partition(numel, world_size, alignment)
         self.numel = numel
         self.world_size = world_size
@@ -60,9 +64,17 @@ class SimulatedWorld:
         d = self.device
         self.grads = [torch.zeros(self.hi - self.lo, dtype=grad_dtype, device=d)
                       for _ in range(self.n_replicas)] if allocate_grads else []
-        self.master = [torch.zeros(self.s, dtype=torch.float32, device=d) for _ in self.ranks]
-        self.exp_avg = [torch.zeros(self.s, dtype=torch.float32, device=d) for _ in self.ranks]
-        self.exp_avg_sq = [torch.zeros(self.s, dtype=torch.float32, device=d) for _ in self.ranks]
+        self.state_layout = state_layout
+        if state_layout == ZERO_STATE_TILED:
+            self.tiled = [torch.zeros(tiled_state_numel(self.s), dtype=torch.float32, device=d)
+                          for _ in self.ranks]
+            self.master = self.exp_avg = self.exp_avg_sq = None
+        else:
+            self.tiled = None
+            self.master = [torch.zeros(self.s, dtype=torch.float32, device=d) for _ in self.ranks]
+            self.exp_avg = [torch.zeros(self.s, dtype=torch.float32, device=d) for _ in self.ranks]
+            self.exp_avg_sq = [torch.zeros(self.s, dtype=torch.float32, device=d)
+                               for _ in self.ranks]
         self.full_params = torch.zeros(self.padded, dtype=self.param_dtype, device=d)
         ws = zero_shard_workspace_bytes(self.s)
         self.workspace = [torch.empty(ws, dtype=torch.uint8, device=d) for _ in self.ranks]
@@ -77,16 +89,44 @@ class SimulatedWorld:
 
     def rank_args(self, k: int, hp: Hyper, t: int, accumulate: bool = False) -> StepArgs:
         r = self.ranks[k]
+        tiled = self.state_layout == ZERO_STATE_TILED
         return StepArgs(world_size=self.world_size, rank=r, shard_numel=self.s,
                         valid_numel=self.valid[r],
                         replica_grads=[self.grad_slice(i, r) for i in range(self.n_replicas)],
-                        master=self.master[k], exp_avg=self.exp_avg[k],
-                        exp_avg_sq=self.exp_avg_sq[k], full_params=self.full_params,
+                        master=self.tiled[k] if tiled else self.master[k],
+                        exp_avg=None if tiled else self.exp_avg[k],
+                        exp_avg_sq=None if tiled else self.exp_avg_sq[k],
+                        full_params=self.full_params,
                         workspace=self.workspace[k], lr=hp.lr, beta1=hp.beta1, beta2=hp.beta2,
                         eps=hp.eps, weight_decay=hp.weight_decay, step=t,
                         loss_scale=hp.loss_scale, grad_predivide=hp.grad_predivide,
                         max_grad_norm=hp.max_grad_norm, grad_dtype=self.grad_dtype,
-                        param_dtype=self.param_dtype, accumulate=accumulate)
+                        param_dtype=self.param_dtype, accumulate=accumulate,
+                        state_layout=self.state_layout)
+
+    def separate_state(self, k: int):
+        """Rank ranks[k]'s (master, exp_avg, exp_avg_sq) as three fp32
+        tensors of shard length: the arrays themselves, or, for a tiled
+        state, new tensors the library untiles it into."""
+        if self.state_layout != ZERO_STATE_TILED:
+            return (self.master[k], self.exp_avg[k], self.exp_avg_sq[k])
+        out = tuple(torch.empty(self.s, dtype=torch.float32, device=self.device)
+                    for _ in range(3))
+        zero_state_untile(self.tiled[k], *out, first=0, n=self.s)
+        return out
+
+    def set_state(self, k: int, master, exp_avg=None, exp_avg_sq=None) -> None:
+        """Set rank ranks[k]'s state from fp32 tensors of shard length (the
+        moments default to zero), through the library for a tiled state."""
+        z = lambda: torch.zeros(self.s, dtype=torch.float32, device=self.device)
+        m = exp_avg if exp_avg is not None else z()
+        v = exp_avg_sq if exp_avg_sq is not None else z()
+        if self.state_layout == ZERO_STATE_TILED:
+            zero_state_tile(master, m, v, self.tiled[k], first=0, n=self.s)
+        else:
+            self.master[k].copy_(master)
+            self.exp_avg[k].copy_(m)
+            self.exp_avg_sq[k].copy_(v)
 
     def accumulate(self, hp: Hyper, first: bool, stream=None) -> None:
         """Queue pass 1 only for every simulated rank: a micro-batch before
@@ -132,6 +172,9 @@ class SimulatedWorld:
             raise ValueError("needs every rank of the world")
 
     def state(self, k: int):
+        """Rank ranks[k]'s state as stored: three arrays, or one tiled one."""
+        if self.state_layout == ZERO_STATE_TILED:
+            return (self.tiled[k],)
         return (self.master[k], self.exp_avg[k], self.exp_avg_sq[k])
 
     def save_checkpoint(self, directory: str, step: int, scaler=None) -> None:
@@ -151,9 +194,15 @@ class SimulatedWorld:
 
     def repartition_from(self, other: "SimulatedWorld", stream=None) -> None:
         """Take over the optimizer state of a resident world of the same
-        numel but another partition, on the device."""
+        numel but another partition (and the same state layout), on the
+        device."""
         self._all_ranks()
         other._all_ranks()
+        if self.state_layout != other.state_layout:
+            raise ValueError("both worlds must keep their state in the same layout")
+        if self.state_layout == ZERO_STATE_TILED:
+            zero_repartition_tiled(other.part, other.tiled, self.part, self.tiled, stream)
+            return
         for field in range(3):
             zero_repartition(other.part, [other.state(k)[field] for k in range(other.world_size)],
                              self.part, [self.state(k)[field] for k in range(self.world_size)],
