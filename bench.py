@@ -76,6 +76,10 @@ def parse():
                          "arrays; 'tiled' keeps them in one array of 256-element tiles "
                          "(ZERO_STATE_TILED), so the update pass moves two state streams "
                          "instead of six")
+    ap.add_argument("--flatten-streams", type=int, default=2,
+                    help="ragged: HIP streams the 8 replicas' flatten calls are spread over "
+                         "(replica i on stream i mod S, so one launch's tail overlaps the "
+                         "next one's start); the step waits for all of them")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 29,
                     help="elements of the shard the CPU oracle is timed on")
@@ -521,19 +525,31 @@ def run_ragged(args, torch, Z, W):
             arr = (_abi.zero_tensor_slot_t * len(sl))(*sl)
             parr = (_abi.vp * len(sl))(*ptrs[b.first_tensor:b.first_tensor + b.n_tensors])
             flat_numel = padded if bi == len(buckets) - 1 else b.end
-            calls.append((arr, len(sl), parr, world.grads[i].data_ptr(), flat_numel))
+            calls.append((i, arr, len(sl), parr, world.grads[i].data_ptr(), flat_numel))
     del ref
     for k, r in enumerate(world.ranks):
         W.flat_normal(world.master[k], r * world.s, P, w.master_sigma, W.master_key(w, 0))
     hp = Hyper(lr=w.lr, weight_decay=w.weight_decay, max_grad_norm=w.max_grad_norm)
     L = Z.lib()
     stream = torch.cuda.current_stream()
-    sp = stream.cuda_stream
+    # replica i's calls go to stream i mod S; side streams start after the
+    # main stream's earlier work and the main stream waits for them
+    S = max(1, args.flatten_streams)
+    streams = [stream] + [torch.cuda.Stream() for _ in range(S - 1)]
 
     def flatten_all():
-        for arr, n, parr, dst, fn in calls:
-            Z.check(L.zero_bucket_flatten(arr, n, parr, Z.ZERO_BF16, dst, fn, sp),
-                    "zero_bucket_flatten")
+        if S > 1:
+            start = torch.cuda.Event()
+            start.record(stream)
+            for st in streams[1:]:
+                st.wait_event(start)
+        for i, arr, n, parr, dst, fn in calls:
+            Z.check(L.zero_bucket_flatten(arr, n, parr, Z.ZERO_BF16, dst, fn,
+                                          streams[i % S].cuda_stream), "zero_bucket_flatten")
+        for st in streams[1:]:
+            done = torch.cuda.Event()
+            done.record(st)
+            stream.wait_event(done)
 
     t = 1
     for _ in range(args.warmup):
@@ -574,6 +590,7 @@ def report_ragged(args, r, W, torch):
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": W.RAGGED_2000.name, "params": P, "tensors": 2000,
                    "buckets": r["n_buckets"], "world_size": N, "replicas": N,
+                   "flatten_streams": max(1, args.flatten_streams),
                    "shard_numel": r["s"], "grad_dtype": "bf16", "param_dtype": "bf16"},
         "hbm_gbps": (flat_bytes + step_bytes) / (r["ms"] * 1e-3) / 1e9,
         "hbm_frac": (flat_bytes + step_bytes) / (r["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
