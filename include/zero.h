@@ -563,11 +563,13 @@ int zero_repartition(const zero_partition_t* from, const float* const* src_dev,
  * zero_state_untile: the reverse, element first + i of `tiled` into
  * master[i], exp_avg[i], exp_avg_sq[i].  A rank's whole state is n =
  * shard_numel, first = 0; a chunk at a time is fine (checkpoints do that).
- * Bit copies; device pointers (16-byte aligned), asynchronous on `stream`;
- * the two sides must not overlap.  Tile slots past the last converted
- * element are not touched.  Errors: n < 0, first < 0, a NULL pointer
- * when n > 0 -> ZERO_EINVAL; misalignment -> ZERO_EALIGN; launch ->
- * ZERO_EDEVICE. */
+ * The separate arrays hold n values each; `tiled` holds at least the whole
+ * tiles of elements [0, first + n), 3 * ZERO_STATE_TILE * ceil((first + n)
+ * / ZERO_STATE_TILE) values.  Bit copies; device pointers (16-byte
+ * aligned), asynchronous on `stream`; the two sides must not overlap.
+ * Tile slots of elements outside [first, first + n) are not touched.
+ * Errors: n < 0, first < 0, a NULL pointer when n > 0 -> ZERO_EINVAL;
+ * misalignment -> ZERO_EALIGN; launch -> ZERO_EDEVICE. */
 int zero_state_tile(const float* master, const float* exp_avg, const float* exp_avg_sq, int64_t n,
                     float* tiled, int64_t first, void* stream);
 int zero_state_untile(const float* tiled, int64_t first, int64_t n, float* master, float* exp_avg,
