@@ -173,6 +173,11 @@ int zero_bucket_flatten(const zero_tensor_slot_t* slots, int32_t n_tensors,
 /* ------------------------------------------------------------------------
  * The shard step.
  *
+ * (zero_step_scalars_t, below, may hold the step's scalars in device
+ * memory; declared here so the arguments can point at it.) */
+struct zero_step_scalars;
+
+/*
  * Arguments of one rank's step.  Hyper-parameters follow [P1] §3.1 (AdamW,
  * lr 6e-5, weight_decay 0.01), [P1] §6 (gradient_clipping 1.0) and
  * [P1] §3.3 / §5.1 (fp16 loss scale); the fp32 master weights and two Adam
@@ -234,6 +239,16 @@ typedef struct {
      * zero_state_untile convert between the layouts. */
     int32_t state_layout;
     int32_t reserved;         /* 0 */
+    /* Optional device copy of the step's scalars (zero_step_scalars_t,
+     * 16-byte aligned), for HIP graphs replayed across steps.  NULL: the
+     * kernels take the scalars above as launch arguments, fixed when a
+     * graph is captured.  Set: the reduce reads its unscale multiplier, the
+     * AdamW pass its constants and zero_shard_step's combine its clip
+     * threshold and peer values from this buffer when they run, so a
+     * captured step replays with whatever the caller last wrote there
+     * (zero_step_scalars fills it on the host).  The fields above are still
+     * checked.  zero_offload_apply does not read it. */
+    const struct zero_step_scalars* scalars;
 } zero_step_args;
 
 /* Result of the cross-rank combine, 32 bytes in device memory. */
@@ -312,7 +327,8 @@ int zero_accumulate_local(const void* grad, int32_t grad_dtype, float* acc, int6
  * zero_global_t at global_dev (device): the global sum of squares and norm,
  * the overflow flag (any slot flagged, or a non-finite sum), and the clip
  * factor max_grad_norm / (norm + 1e-6), applied only when below 1 and
- * max_grad_norm > 0 ([P1] §6 gradient_clipping). */
+ * max_grad_norm > 0 ([P1] §6 gradient_clipping).  max_grad_norm is a
+ * launch argument (fixed under graph capture). */
 int zero_shard_combine(const void* partials_dev, int32_t n_slots,
                        double max_grad_norm, void* global_dev, void* stream);
 
@@ -342,14 +358,48 @@ int zero_shard_apply(const zero_step_args* a, const void* global_dev,
  * ZERO_ESIZE; a HIP failure -> ZERO_EDEVICE.  When valid_numel is 0 the
  * rank touches no element and only the workspace must be given.
  * Graph capture: without info the call queues four kernels and nothing
- * else, so it can be captured in a HIP graph.  The step's scalars (t, lr,
- * betas, eps, weight decay, loss scale, predivide, max_grad_norm,
- * peer_sumsq, peer_overflow) travel as kernel arguments and are fixed at
- * capture: every replay uses the captured values.  Since t changes after
- * every applied step and the loss scale after scaler events, re-capture
- * when any of them changes, or capture only where they stay fixed. */
+ * else, so it can be captured in a HIP graph.  By default the step's
+ * scalars (t, lr, betas, eps, weight decay, loss scale, predivide,
+ * max_grad_norm, peer_sumsq, peer_overflow) travel as kernel arguments and
+ * are fixed at capture: every replay uses the captured values.  With
+ * a->scalars set, the kernels read them from that device buffer instead
+ * (see zero_step_scalars), and one capture serves every step. */
 int zero_shard_step(const zero_step_args* a, double peer_sumsq,
                     int32_t peer_overflow, zero_step_info* info, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Step scalars in device memory.  Every per-step constant the kernels use,
+ * computed on the host exactly as the kernels' launch arguments are (each
+ * in fp64 from the step's hyper-parameters and rounded once to fp32), so a
+ * step that reads them from device memory gives the same bits as one that
+ * takes them as arguments.  A caller that captures the step in a HIP graph
+ * points zero_step_args.scalars at a device copy, and before each replay
+ * fills a host copy with zero_step_scalars (t, the learning rate and the
+ * loss scale may all change) and copies it to the device.  64 bytes.
+ * ([P1] §3.1 AdamW hyper-parameters, §3.3 / §5.1 loss scale, §6 clipping.)
+ */
+typedef struct zero_step_scalars {
+    float   inv_scale;        /* fp32(1 / (loss_scale * grad_predivide))     */
+    float   decay;            /* fp32(1 - lr * weight_decay)                 */
+    float   beta1;            /* fp32(beta1)                                 */
+    float   one_minus_beta1;  /* fp32(1 - beta1)                             */
+    float   beta2;            /* fp32(beta2)                                 */
+    float   one_minus_beta2;  /* fp32(1 - beta2)                             */
+    float   step_size;        /* fp32(lr / (1 - beta1^t))                    */
+    float   inv_sqrt_bc2;     /* fp32(1 / sqrt(1 - beta2^t))                 */
+    float   eps;              /* fp32(eps)                                   */
+    int32_t peer_overflow;    /* the peers' OR'd flag (zero_shard_step)      */
+    int32_t reserved[2];      /* 0                                           */
+    double  max_grad_norm;    /* <= 0 disables clipping                      */
+    double  peer_sumsq;       /* the peers' sum of squares (zero_shard_step) */
+} zero_step_scalars_t;
+
+/* Fill *out from a's hyper-parameters (lr, betas, eps, weight_decay, step,
+ * loss_scale, grad_predivide, max_grad_norm) and the peers' contribution.
+ * Errors: any of them out of range (as zero_shard_step checks them), a
+ * negative or NaN peer_sumsq, NULL arguments -> ZERO_EINVAL.  Host only. */
+int zero_step_scalars(const zero_step_args* a, double peer_sumsq, int32_t peer_overflow,
+                      zero_step_scalars_t* out);
 
 /* ------------------------------------------------------------------------
  * The step without any allocation, for callers that cannot allocate device

@@ -584,3 +584,38 @@ def test_layout_conversions_reject_bad_arguments_before_any_work():
     mis = (_abi.vp * 4)(0x100000, 0x200004, 0x300000, 0x400000)
     assert L.zero_repartition_tiled(ctypes.byref(good), mis, ctypes.byref(good), ptrs,
                                     None) == Z.ZERO_EALIGN
+
+
+# ------------------------------------------------------ step scalars on the device
+@pytest.mark.parametrize("hp", [dict(), dict(lr=1e-3, beta1=0.8, beta2=0.95, eps=1e-6, weight_decay=0.1,
+                                          step=7, loss_scale=2.0**12, grad_predivide=3.0),
+                                dict(lr=0.0, beta1=0.0, step=123456, loss_scale=0.5,
+                                     max_grad_norm=0.0)])
+def test_step_scalars_are_the_step_constants(hp):
+    # Each field is the hyper-parameter expression evaluated in fp64 and
+    # rounded once to fp32, as the kernels' launch arguments are.
+    a = good_args(**hp)
+    sc = Z.zero_step_scalars(a, peer_sumsq=2.5, peer_overflow=True)
+    f = np.float32
+    t = a.step
+    assert sc.inv_scale == f(1.0 / (a.loss_scale * a.grad_predivide))
+    assert sc.decay == f(1.0 - a.lr * a.weight_decay)
+    assert (sc.beta1, sc.one_minus_beta1) == (f(a.beta1), f(1.0 - a.beta1))
+    assert (sc.beta2, sc.one_minus_beta2) == (f(a.beta2), f(1.0 - a.beta2))
+    assert sc.step_size == f(a.lr / (1.0 - a.beta1 ** t))
+    assert sc.inv_sqrt_bc2 == f(1.0 / np.sqrt(1.0 - a.beta2 ** t))
+    assert sc.eps == f(a.eps)
+    assert (sc.max_grad_norm, sc.peer_sumsq, sc.peer_overflow) == (a.max_grad_norm, 2.5, 1)
+    assert list(sc.reserved) == [0, 0]
+
+
+def test_step_scalars_checks():
+    with pytest.raises(Z.ZeroError):
+        Z.zero_step_scalars(good_args(step=0))
+    with pytest.raises(Z.ZeroError):
+        Z.zero_step_scalars(good_args(), peer_sumsq=float("nan"))
+    with pytest.raises(Z.ZeroError) as e:       # a misaligned device copy is refused by the step
+        Z.zero_shard_step(good_args(scalars=FakeTensor(0x900008, 64)), stream=0)
+    assert e.value.code == Z.ZERO_EALIGN and "scalars" in Z.zero_last_error()
+    with pytest.raises(ValueError):             # and a short one by the binding
+        good_args(scalars=FakeTensor(0x900000, 32)).c_args()

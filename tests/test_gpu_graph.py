@@ -11,9 +11,11 @@ scalars (t, lr, loss scale, ...) are kernel arguments fixed at capture, so
 every replay here is a step at t = 1 and is compared with an eager step at
 t = 1; a caller whose t or scale changes re-captures.
 """
+import numpy as np
 import pytest
 import torch
 
+import oracle
 import parity
 import zero_sharded_optimizer_step_amd as Z
 from zero_sharded_optimizer_step_amd import workloads as W
@@ -130,3 +132,100 @@ def test_captured_accumulation_window_replays_equal_eager(mode):
                                   parity.f32(eager.state(0)[f][:numel]))
         parity.assert_bitwise("%s replay %d params" % (mode, rep), parity.u16(graph_w.full_params),
                               parity.u16(eager.full_params))
+
+
+def _scalars_bytes(sc):
+    return torch.frombuffer(bytearray(bytes(sc)), dtype=torch.uint8)
+
+
+@pytest.mark.parametrize("entry", ["step", "noalloc"])
+def test_captured_step_with_device_scalars_serves_every_step(entry):
+    # One capture of a step whose scalars live in a device buffer
+    # (zero_step_args.scalars), replayed for 6 consecutive training steps:
+    # before each replay the host refills the buffer with zero_step_scalars
+    # for that step's t (advanced only after applied steps), learning rate
+    # (a decaying schedule) and fp16 loss scale (driven by the dynamic
+    # scaler; one replay is poisoned and must skip and halve it).  Every
+    # replay must equal an eager step with the same scalars as launch
+    # arguments, bit for bit, and the eager run must match the oracle.
+    numel, R = 400_009, 4
+    print("graph capture with device scalars (%s)" % entry, flush=True)
+    eager = SimulatedWorld(numel, 1, n_replicas=R, alignment=128, grad_dtype=torch.float16)
+    graph_w = SimulatedWorld(numel, 1, n_replicas=R, alignment=128, grad_dtype=torch.float16)
+    scal_dev = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    sc_lib = Z.zero_loss_scaler_init(12, 2, 1, 1.0)
+    o_sc = oracle.LossScaler(12, 2, 1, 1.0)
+
+    def hyper(t, scale):
+        return Hyper(lr=1e-3 * 0.8 ** (t - 1), loss_scale=scale)
+
+    def graph_args(t, scale):
+        a = graph_w.rank_args(0, hyper(t, scale), t)
+        a.scalars = scal_dev
+        if entry == "noalloc":
+            a.workspace = None
+        return a
+
+    def call(a, stream=None):
+        if entry == "noalloc":
+            Z.zero_shard_step_noalloc(a, stream=stream)
+        else:
+            Z.zero_shard_step(a, stream=stream)
+
+    def reset():
+        for w in (eager, graph_w):
+            W.flat_normal(w.master[0], 0, numel, 0.02, ("graph-sc-m",))
+            w.exp_avg[0].zero_()
+            w.exp_avg_sq[0].zero_()
+            w.full_params.zero_()
+
+    scal_dev.copy_(_scalars_bytes(Z.zero_step_scalars(graph_args(1, sc_lib.scale))))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                   # warm the library on the side stream
+        call(graph_args(1, sc_lib.scale), stream=s)
+    torch.cuda.synchronize()
+    reset()
+    o_p = parity.f32(eager.master[0])[:numel].copy()
+    o_m = np.zeros(numel, np.float32)
+    o_v = np.zeros(numel, np.float32)
+    o_full = np.zeros(numel, np.uint16)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):                    # captured once, with t = 1's launch arguments
+        call(graph_args(1, sc_lib.scale))
+    t = 1
+    skipped = 0
+    for rep in range(6):
+        scale = sc_lib.scale
+        for i in range(R):
+            W.flat_normal(eager.grads[i], 0, numel, 1e-3, ("graph-sc", rep, i), scale=scale)
+        if rep == 3:
+            W.plant(eager.grads[2], W.Poison(rep, 2, numel // 5, 2))
+        for i in range(R):
+            graph_w.grads[i].copy_(eager.grads[i])
+        reps = [parity.u16(x)[:numel] for x in eager.grads]
+        # this step's scalars into the captured buffer, then the replay
+        scal_dev.copy_(_scalars_bytes(Z.zero_step_scalars(graph_args(t, scale))))
+        g.replay()
+        eager.step(hyper(t, scale), t)
+        res = eager.result()
+        _ = torch.ones(1000, device="cuda").sum().item()      # eager work and a sync between
+        info = oracle.step(reps, oracle.FP16, numel, 1, 1, [o_p], [o_m], [o_v], o_full,
+                           oracle.Hyper(lr=hyper(t, scale).lr, loss_scale=scale), t)
+        assert bool(res.overflow) == info.overflow == (rep == 3)
+        for f, name in enumerate(("master", "exp_avg", "exp_avg_sq")):
+            got = parity.f32(graph_w.state(0)[f][:numel])
+            parity.assert_bitwise("replay %d %s vs eager" % (rep, name), got,
+                                  parity.f32(eager.state(0)[f][:numel]))
+            parity.assert_rel("replay %d %s vs oracle" % (rep, name), got, (o_p, o_m, o_v)[f],
+                              parity.RTOL_STATE)
+        parity.assert_bitwise("replay %d params" % rep, parity.u16(graph_w.full_params),
+                              parity.u16(eager.full_params))
+        skip = Z.zero_loss_scaler_update(sc_lib, bool(res.overflow))
+        assert skip == o_sc.update(info.overflow) and sc_lib.scale == o_sc.scale
+        if skip:
+            skipped += 1
+        else:
+            t += 1
+    assert skipped == 1 and t == 6 and sc_lib.scale != 2.0**12   # the scale moved

@@ -20,7 +20,7 @@ from ._abi import (ZERO_BF16, ZERO_CKPT_MAGIC, ZERO_CKPT_VERSION, ZERO_EALIGN, Z
                    check, lib, zero_bucket_t, zero_ckpt_header_t, zero_global_t,
                    zero_loss_scaler_t, zero_offload_staging_t, zero_partition_t,
                    zero_repartition_piece_t, zero_step_args, zero_step_info,
-                   zero_tensor_slot_t)
+                   zero_step_scalars_t, zero_tensor_slot_t)
 
 __all__ = [
     "ZERO_OK", "ZERO_EINVAL", "ZERO_EALIGN", "ZERO_ESIZE", "ZERO_EDEVICE",
@@ -31,7 +31,8 @@ __all__ = [
     "zero_bucket_plan", "zero_bucket_flatten", "zero_shard_workspace_bytes",
     "zero_partials_bytes", "zero_shard_reduce", "zero_shard_accumulate",
     "zero_accumulate_local", "zero_shard_combine",
-    "zero_shard_apply", "zero_shard_step", "zero_shard_step_noalloc", "zero_loss_scaler_init",
+    "zero_shard_apply", "zero_shard_step", "zero_shard_step_noalloc", "zero_step_scalars",
+    "zero_loss_scaler_init",
     "zero_loss_scaler_update", "zero_ckpt_header_make", "zero_ckpt_header_check",
     "zero_repartition", "zero_repartition_plan", "zero_repartition_tiled", "zero_state_tile",
     "zero_state_untile", "zero_gather_params", "zero_offload_apply",
@@ -210,6 +211,9 @@ class StepArgs:
     # ZERO_STATE_TILED: `master` (and `master_out`) hold the tiled state and
     # exp_avg, exp_avg_sq (and their outputs) are None
     state_layout: int = ZERO_STATE_SEPARATE
+    # device buffer (>= 64 bytes) holding a zero_step_scalars_t the kernels
+    # read at run time instead of taking the scalars as launch arguments
+    scalars: object = None
 
     def check_sizes(self, gsize: int) -> None:
         """Every buffer must hold what the step touches in it: valid_numel
@@ -265,6 +269,8 @@ class StepArgs:
         a.grad_predivide = self.grad_predivide
         a.max_grad_norm = self.max_grad_norm
         a.state_layout = self.state_layout
+        a.scalars = _dptr(self.scalars)
+        _need(self.scalars, ctypes.sizeof(zero_step_scalars_t), "scalars")
         self.check_sizes(4 if a.grad_dtype == ZERO_FP32 else 2)
         self._c = a
         return a
@@ -323,6 +329,16 @@ def zero_shard_step(args, peer_sumsq: float = 0.0, peer_overflow: bool = False,
                                 ctypes.byref(info) if info is not None else None,
                                 _stream(stream)), "zero_shard_step")
     return info
+
+
+def zero_step_scalars(args, peer_sumsq: float = 0.0, peer_overflow: bool = False
+                      ) -> zero_step_scalars_t:
+    """The step's scalars, computed on the host, for a device copy that
+    args.scalars points at (see zero.h)."""
+    out = zero_step_scalars_t()
+    check(lib().zero_step_scalars(ctypes.byref(_args(args)), peer_sumsq, 1 if peer_overflow else 0,
+                                  ctypes.byref(out)), "zero_step_scalars")
+    return out
 
 
 def zero_shard_step_noalloc(args, peer_sumsq: float = 0.0, peer_overflow: bool = False,

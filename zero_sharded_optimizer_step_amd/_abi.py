@@ -54,7 +54,17 @@ class zero_step_args(ctypes.Structure):
                 ("weight_decay", f64), ("step", i64), ("loss_scale", f64),
                 ("grad_predivide", f64), ("max_grad_norm", f64), ("param_shard", vp),
                 ("master_out", vp), ("exp_avg_out", vp), ("exp_avg_sq_out", vp),
-                ("state_layout", i32), ("reserved", i32)]
+                ("state_layout", i32), ("reserved", i32), ("scalars", vp)]
+
+
+class zero_step_scalars_t(ctypes.Structure):
+    _fields_ = [("inv_scale", f32), ("decay", f32), ("beta1", f32), ("one_minus_beta1", f32),
+                ("beta2", f32), ("one_minus_beta2", f32), ("step_size", f32),
+                ("inv_sqrt_bc2", f32), ("eps", f32), ("peer_overflow", i32),
+                ("reserved", i32 * 2), ("max_grad_norm", f64), ("peer_sumsq", f64)]
+
+
+assert ctypes.sizeof(zero_step_scalars_t) == 64
 
 
 class zero_global_t(ctypes.Structure):
@@ -112,6 +122,8 @@ _PROTOTYPES = {
     "zero_shard_apply": (ctypes.c_int, [ctypes.POINTER(zero_step_args), vp, vp]),
     "zero_shard_step": (ctypes.c_int, [ctypes.POINTER(zero_step_args), f64, i32,
                                        ctypes.POINTER(zero_step_info), vp]),
+    "zero_step_scalars": (ctypes.c_int, [ctypes.POINTER(zero_step_args), f64, i32,
+                                         ctypes.POINTER(zero_step_scalars_t)]),
     "zero_shard_step_noalloc": (ctypes.c_int, [ctypes.POINTER(zero_step_args), f64, i32,
                                                ctypes.POINTER(zero_step_info), vp]),
     "zero_loss_scaler_init": (ctypes.c_int, [i32, i32, i32, f64,

@@ -115,6 +115,7 @@ int validate_step_args(const zero_step_args* a, bool check_workspace) {
             return fail(ZERO_EINVAL, "output state must not be the input state (leave it NULL "
                                      "to update in place)");
     }
+    if (!aligned16(a->scalars)) return fail(ZERO_EALIGN, "scalars is not 16-byte aligned");
     // Start of this rank's slice of the full buffer: shard_numel is a
     // multiple of 8, so 2-byte elements keep 16-byte alignment.
     if (check_workspace && a->workspace_bytes < zero_shard_workspace_bytes(a->shard_numel))
@@ -349,6 +350,33 @@ int zero_ckpt_header_check(const zero_ckpt_header_t* h, uint64_t file_bytes,
                     (unsigned long long)file_bytes,
                     (unsigned long long)(sizeof(zero_ckpt_header_t) + payload));
     if (part) *part = p;
+    return ZERO_OK;
+}
+
+static_assert(sizeof(zero_step_scalars_t) == 64, "step scalars are 64 bytes");
+
+int zero_step_scalars(const zero_step_args* a, double peer_sumsq, int32_t peer_overflow,
+                      zero_step_scalars_t* out) {
+    clear_error();
+    if (!out) return fail(ZERO_EINVAL, "out is NULL");
+    int rc = validate_step_args(a, false);
+    if (rc) return rc;
+    if (!(peer_sumsq >= 0.0)) return fail(ZERO_EINVAL, "peer_sumsq must be >= 0 (got NaN or negative)");
+    // the same constants, rounded the same way, as the launch arguments
+    const AdamConsts k = adam_consts(a->lr, a->beta1, a->beta2, a->eps, a->weight_decay, a->step);
+    std::memset(out, 0, sizeof *out);
+    out->inv_scale = unscale_factor(a);
+    out->decay = k.decay;
+    out->beta1 = k.b1;
+    out->one_minus_beta1 = k.c1;
+    out->beta2 = k.b2;
+    out->one_minus_beta2 = k.c2;
+    out->step_size = k.step_size;
+    out->inv_sqrt_bc2 = k.inv_sqrt_bc2;
+    out->eps = k.eps;
+    out->peer_overflow = peer_overflow ? 1 : 0;
+    out->max_grad_norm = a->max_grad_norm;
+    out->peer_sumsq = peer_sumsq;
     return ZERO_OK;
 }
 

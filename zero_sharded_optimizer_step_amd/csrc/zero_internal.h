@@ -152,4 +152,9 @@ struct AdamConsts {
 AdamConsts adam_consts(double lr, double beta1, double beta2, double eps, double weight_decay,
                        int64_t step);
 
+// The unscale multiplier fp32(1 / (loss_scale * grad_predivide)) of a step.
+inline float unscale_factor(const zero_step_args* a) {
+    return static_cast<float>(1.0 / (a->loss_scale * a->grad_predivide));
+}
+
 }  // namespace zero

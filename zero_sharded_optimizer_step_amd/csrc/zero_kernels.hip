@@ -161,8 +161,10 @@ __device__ __forceinline__ void sum_quad(const ReplicaPtrs& reps, int nrep, int6
 // accumulation over micro-batches; [P1] §3.1 gradient_accumulation_steps).
 template <int DT, int NR, bool ACC>
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(
-    ReplicaPtrs reps, int nrep, int64_t n_valid, float inv_scale, float* __restrict__ g,
-    Partial* __restrict__ partials, uint32_t group) {
+    ReplicaPtrs reps, int nrep, int64_t n_valid, float inv_scale,
+    const zero_step_scalars_t* __restrict__ sc, float* __restrict__ g, Partial* __restrict__ partials,
+    uint32_t group) {
+    if (sc) inv_scale = sc->inv_scale;            // the step's scalars in device memory
     const int64_t blk = xcd_block(blockIdx.x, group);
     const int64_t q = blk * kReduceThreads + threadIdx.x;
     const int64_t full = n_valid / kQuad;              // complete quads
@@ -273,7 +275,7 @@ constexpr int kCombineThreads = 256;
 
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const unsigned char* __restrict__ partials, int n_slots, double peer_sumsq, int peer_overflow,
-    double max_norm, zero_global_t* __restrict__ out) {
+    double max_norm, const zero_step_scalars_t* __restrict__ sc, zero_global_t* __restrict__ out) {
     double ss = 0.0;
     int bad = 0;
     for (int s = 0; s < n_slots; ++s) {
@@ -288,6 +290,11 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     }
     block_reduce<kCombineThreads>(ss, bad);
     if (threadIdx.x == 0) {
+        if (sc) {                                 // the step's scalars in device memory
+            peer_sumsq = sc->peer_sumsq;
+            peer_overflow = sc->peer_overflow;
+            max_norm = sc->max_grad_norm;
+        }
         ss += peer_sumsq;
         bad |= peer_overflow;
         const double norm = sqrt(ss);
@@ -336,8 +343,18 @@ template <int PT, bool OOP, bool TILED>
 __global__ __launch_bounds__(kApplyThreads) void apply_kernel(
     const float* g, const float* p, const float* m, const float* v, float* p2, float* m2, float* v2,
     unsigned short* __restrict__ out, int64_t n_valid, const zero_global_t* __restrict__ glob,
-    AdamConsts k, uint32_t group) {
+    AdamConsts k, const zero_step_scalars_t* __restrict__ sc, uint32_t group) {
     if (glob->overflow) return;                    // skipped step: touch nothing
+    if (sc) {                                      // the step's scalars in device memory
+        k.decay = sc->decay;
+        k.b1 = sc->beta1;
+        k.c1 = sc->one_minus_beta1;
+        k.b2 = sc->beta2;
+        k.c2 = sc->one_minus_beta2;
+        k.step_size = sc->step_size;
+        k.inv_sqrt_bc2 = sc->inv_sqrt_bc2;
+        k.eps = sc->eps;
+    }
     const int64_t blk = xcd_block(blockIdx.x, group);
     if constexpr (TILED) {
         // this block's tile; the quad offsets below are then tile offsets
@@ -550,22 +567,22 @@ int launch_error(const char* what) {
 }
 
 template <int DT, bool ACC>
-void launch_reduce_dt(const ReplicaPtrs& reps, int nrep, int64_t n_valid, float inv, float* g,
-                      Partial* parts, hipStream_t st) {
+void launch_reduce_dt(const ReplicaPtrs& reps, int nrep, int64_t n_valid, float inv,
+                      const zero_step_scalars_t* sc, float* g, Partial* parts, hipStream_t st) {
     const Grid gr = grid_for(n_valid, kReduceThreads);
     const dim3 grid(static_cast<unsigned>(gr.blocks));
     const uint32_t group = static_cast<uint32_t>(gr.group);
 #define ZERO_REDUCE_CASE(NR)                                                                   \
     case NR:                                                                                   \
         hipLaunchKernelGGL((reduce_kernel<DT, NR, ACC>), grid, dim3(kReduceThreads), 0, st, reps, \
-                           nrep, n_valid, inv, g, parts, group);                               \
+                           nrep, n_valid, inv, sc, g, parts, group);                           \
         break;
     switch (nrep) {
         ZERO_REDUCE_CASE(1) ZERO_REDUCE_CASE(2) ZERO_REDUCE_CASE(3) ZERO_REDUCE_CASE(4)
         ZERO_REDUCE_CASE(5) ZERO_REDUCE_CASE(6) ZERO_REDUCE_CASE(7) ZERO_REDUCE_CASE(8)
         default:
             hipLaunchKernelGGL((reduce_kernel<DT, 0, ACC>), grid, dim3(kReduceThreads), 0, st, reps,
-                               nrep, n_valid, inv, g, parts, group);
+                               nrep, n_valid, inv, sc, g, parts, group);
     }
 #undef ZERO_REDUCE_CASE
 }
@@ -577,16 +594,17 @@ int launch_pass1(const zero_step_args* a, hipStream_t st) {
     ReplicaPtrs reps;
     for (int r = 0; r < ZERO_MAX_REPLICAS; ++r)
         reps.p[r] = (a->replica_grad && r < a->n_replicas) ? a->replica_grad[r] : nullptr;
-    const float inv = static_cast<float>(1.0 / (a->loss_scale * a->grad_predivide));
+    const float inv = unscale_factor(a);
+    const zero_step_scalars_t* sc = a->scalars;
     unsigned char* ws = static_cast<unsigned char*>(a->workspace);
     float* g = reinterpret_cast<float*>(ws);
     Partial* parts = reinterpret_cast<Partial*>(ws + ws_blocks_offset(a->shard_numel));
 #define ZERO_PASS1(DT)                                                                          \
     do {                                                                                        \
         if (a->accumulate)                                                                      \
-            launch_reduce_dt<DT, true>(reps, a->n_replicas, a->valid_numel, inv, g, parts, st);  \
+            launch_reduce_dt<DT, true>(reps, a->n_replicas, a->valid_numel, inv, sc, g, parts, st); \
         else                                                                                    \
-            launch_reduce_dt<DT, false>(reps, a->n_replicas, a->valid_numel, inv, g, parts, st); \
+            launch_reduce_dt<DT, false>(reps, a->n_replicas, a->valid_numel, inv, sc, g, parts, st); \
     } while (0)
     switch (a->grad_dtype) {
         case ZERO_BF16: ZERO_PASS1(ZERO_BF16); break;
@@ -609,10 +627,10 @@ int launch_reduce(const zero_step_args* a, unsigned char* slot, hipStream_t st) 
 }
 
 int launch_combine(const void* partials, int n_slots, double peer_ss, int peer_of, double max_norm,
-                   void* global, hipStream_t st) {
+                   const zero_step_scalars_t* sc, void* global, hipStream_t st) {
     hipLaunchKernelGGL(combine_kernel, dim3(1), dim3(kCombineThreads), 0, st,
                        static_cast<const unsigned char*>(partials), n_slots, peer_ss, peer_of, max_norm,
-                       static_cast<zero_global_t*>(global));
+                       sc, static_cast<zero_global_t*>(global));
     return launch_error("combine kernel launch");
 }
 
@@ -632,7 +650,7 @@ int launch_apply(const zero_step_args* a, const void* global, hipStream_t st) {
 #define ZERO_APPLY(PT, OOP, TILED)                                                                  \
     hipLaunchKernelGGL((apply_kernel<PT, OOP, TILED>), grid, dim3(kApplyThreads), 0, st, g,          \
                        a->master, a->exp_avg, a->exp_avg_sq, p2, m2, v2, out, a->valid_numel, gl, k, \
-                       group)
+                       a->scalars, group)
 #define ZERO_APPLY_LAYOUT(PT, OOP) \
     do { if (tiled) ZERO_APPLY(PT, OOP, true); else ZERO_APPLY(PT, OOP, false); } while (0)
     if (a->param_dtype == ZERO_BF16) {
@@ -750,7 +768,8 @@ int run_step(const zero_step_args* a, double peer_sumsq, int32_t peer_overflow, 
     void* global = ws + ws_global_offset(a->shard_numel);
     int rc;
     if ((rc = launch_reduce(a, slot, st))) return rc;
-    if ((rc = launch_combine(slot, 1, peer_sumsq, peer_overflow ? 1 : 0, a->max_grad_norm, global, st)))
+    if ((rc = launch_combine(slot, 1, peer_sumsq, peer_overflow ? 1 : 0, a->max_grad_norm, a->scalars,
+                             global, st)))
         return rc;
     if ((rc = launch_apply(a, global, st))) return rc;
     if (info) {
@@ -871,7 +890,7 @@ int zero_shard_combine(const void* partials_dev, int32_t n_slots, double max_gra
     if (std::isnan(max_grad_norm)) return fail(ZERO_EINVAL, "max_grad_norm is NaN");
     if (!aligned16(partials_dev) || !aligned16(global_dev))
         return fail(ZERO_EALIGN, "partials_dev or global_dev is not 16-byte aligned");
-    return launch_combine(partials_dev, n_slots, 0.0, 0, max_grad_norm, global_dev,
+    return launch_combine(partials_dev, n_slots, 0.0, 0, max_grad_norm, nullptr, global_dev,
                           static_cast<hipStream_t>(stream));
 }
 
