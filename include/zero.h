@@ -24,16 +24,20 @@
  *     then describes the failure (per calling thread).  Arguments are
  *     checked before any work is queued: a call that fails has queued
  *     nothing and touched no memory.
- *   - The caller owns every buffer.  The library allocates no device
- *     memory.  "device" pointers are HIP device addresses on the current
- *     device; "host" pointers are ordinary process memory.
+ *   - The caller owns every buffer.  No call allocates device memory.
+ *     The one device array the library holds itself is the scratch
+ *     workspace of zero_shard_step_noalloc (67,375,616 bytes per GPU,
+ *     created with the library's code).  "device" pointers are HIP device
+ *     addresses on the current device; "host" pointers are ordinary
+ *     process memory.
  *   - `stream` is a hipStream_t passed as void* (NULL: the null stream).
  *     Device work is queued on it and the call returns without waiting,
  *     unless a call says otherwise.
  *   - Device pointers must be 16-byte aligned (ZERO_EALIGN otherwise).
  *   - Element counts are 64-bit; shards beyond 2^32 elements are fine.
- *   - Calls keep no state between them; concurrent calls on different
- *     buffers are safe.  Calls that write the same buffers race.
+ *   - Calls keep no state between them, except the scratch array of
+ *     zero_shard_step_noalloc; concurrent calls on different buffers are
+ *     safe.  Calls that write the same buffers race.
  *   - A call's inputs and outputs must not overlap, unless the call says
  *     that it updates a buffer in place.
  */
