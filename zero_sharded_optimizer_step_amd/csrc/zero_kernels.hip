@@ -409,7 +409,8 @@ __global__ __launch_bounds__(kApplyThreads) void apply_kernel(
 
 // ================================================================ flatten
 // contiguous_gradients ([P1] §5.2): one replica's tensors are copied end to
-// end into its flat buffer, then the padding is zeroed.  Each thread writes
+// end into its flat buffer, then any gap between them and the padding are
+// zeroed (as table entries without a source).  Each thread writes
 // one aligned 16-byte vector of 8 destination elements.  The source side is
 // read as aligned 16-byte vectors and shifted into place, so a tensor's
 // arbitrary offset costs no unaligned accesses (the second vector of a
