@@ -72,24 +72,31 @@ struct HostUpdate {
 };
 
 // One contiguous range; the loop body is the GPU pass's per-element update.
+// The cast to the parameter dtype follows each block of kCastBlock
+// elements while that block's masters are still in the core's L1 cache,
+// rather than in a second pass that reads every master from memory again.
+constexpr int64_t kCastBlock = 1024;
+
 void adamw_range(const HostUpdate& u, int64_t lo, int64_t hi, const float* g, float* p, float* m,
                  float* v, uint16_t* out) {
     const AdamConsts& k = u.k;
-    for (int64_t i = lo; i < hi; ++i) {
-        const float gi = g[i] * u.coef;
-        const float m1 = k.b1 * m[i] + k.c1 * gi;
-        const float v1 = k.b2 * v[i] + k.c2 * (gi * gi);
-        const float d = std::sqrt(v1) * k.inv_sqrt_bc2 + k.eps;
-        const float p1 = p[i] * k.decay - k.step_size * (m1 / d);
-        m[i] = m1;
-        v[i] = v1;
-        p[i] = p1;
-    }
-    if (out) {
+    for (int64_t b = lo; b < hi; b += kCastBlock) {
+        const int64_t e = std::min(hi, b + kCastBlock);
+        for (int64_t i = b; i < e; ++i) {
+            const float gi = g[i] * u.coef;
+            const float m1 = k.b1 * m[i] + k.c1 * gi;
+            const float v1 = k.b2 * v[i] + k.c2 * (gi * gi);
+            const float d = std::sqrt(v1) * k.inv_sqrt_bc2 + k.eps;
+            const float p1 = p[i] * k.decay - k.step_size * (m1 / d);
+            m[i] = m1;
+            v[i] = v1;
+            p[i] = p1;
+        }
+        if (!out) continue;
         if (u.dtype == ZERO_BF16)
-            for (int64_t i = lo; i < hi; ++i) out[i] = to_bf16(p[i]);
+            for (int64_t i = b; i < e; ++i) out[i] = to_bf16(p[i]);
         else
-            for (int64_t i = lo; i < hi; ++i) out[i] = to_f16(p[i]);
+            for (int64_t i = b; i < e; ++i) out[i] = to_f16(p[i]);
     }
 }
 
