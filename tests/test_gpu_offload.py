@@ -107,3 +107,62 @@ def test_offloaded_step_skips_on_overflow():
         for x, y in zip(st, b):
             assert torch.equal(x, y)
     assert bool((host.full_params.view(torch.int16) == parity.CANARY).all())
+
+
+def _random_offload_case(case):
+    rng = np.random.default_rng(5000 + case)
+    numel = int(np.exp(rng.uniform(np.log(1e3), np.log(3e6))))
+    N = int(rng.integers(1, 7))
+    align = int(rng.choice([8, 64, 128]))
+    gdt = torch.bfloat16 if rng.random() < 0.5 else torch.float16
+    # every fourth case casts into the other format
+    pdt = gdt if case % 4 != 3 else (torch.float16 if gdt == torch.bfloat16 else torch.bfloat16)
+    scale = 1.0 if gdt == torch.bfloat16 else float(2.0 ** int(rng.integers(0, 13)))
+    hp = Hyper(lr=float(10 ** rng.uniform(-5, -2)), beta1=float(rng.choice([0.0, 0.9])),
+               beta2=float(rng.choice([0.95, 0.999])), eps=float(rng.choice([1e-8, 1e-6])),
+               weight_decay=float(rng.choice([0.0, 0.01, 0.1])),
+               max_grad_norm=float(rng.choice([0.0, 0.5, 1.0])), loss_scale=scale)
+    chunk = int(rng.choice([8, 64, 1000, 4096, 65536, 1 << 20]))
+    # at most about 2000 chunks per rank and step, so a case stays short
+    chunk = max(chunk, -(-(numel // 2000) // 8) * 8)
+    threads = int(rng.choice([0, 1, 3]))
+    return numel, N, align, gdt, pdt, hp, chunk, threads
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_offloaded_steps_equal_gpu_pass(case):
+    """Seeded random worlds, hyper-parameters, chunk sizes and host thread
+    counts: two offloaded steps equal the GPU pass bit for bit, state and
+    cast."""
+    numel, N, align, gdt, pdt, hp, chunk, threads = _random_offload_case(case)
+    say("offload case %d: P %d N %d A %d %s/%s chunk %d threads %d lr %.1e b1 %g b2 %g wd %g "
+        "clip %g scale %g" % (case, numel, N, align, str(gdt)[6:], str(pdt)[6:], chunk, threads,
+                              hp.lr, hp.beta1, hp.beta2, hp.weight_decay, hp.max_grad_norm,
+                              hp.loss_scale))
+    gpu = SimulatedWorld(numel, N, alignment=align, grad_dtype=gdt, param_dtype=pdt)
+    host = SimulatedWorld(numel, N, alignment=align, grad_dtype=gdt, param_dtype=pdt)
+    for w in (gpu, host):
+        for k in range(N):
+            W.flat_normal(w.master[k], k * w.s, numel, 0.02, ("off-random", case))
+    state = _pinned_state(host)
+    staging = Z.OffloadStaging(chunk, n_threads=threads)
+    for t in (1, 2):
+        for w in (gpu, host):
+            for i in range(w.n_replicas):
+                W.flat_normal(w.grads[i], 0, numel, 1e-3, ("off-random", case, t, i),
+                              scale=hp.loss_scale)
+        gpu.step(hp, t)
+        args = [host.rank_args(k, hp, t) for k in range(N)]
+        for k, a in enumerate(args):
+            Z.zero_shard_reduce(a, k, host.partials)
+        Z.zero_shard_combine(host.partials, N, hp.max_grad_norm, host.global_buf)
+        for k, a in enumerate(args):
+            a.master, a.exp_avg, a.exp_avg_sq = state[k]
+            info = Z.zero_offload_apply(a, host.global_buf, staging, want_info=True)
+            assert info.overflow == gpu.result().overflow
+    for k in range(N):
+        for f, name in enumerate(("master", "exp_avg", "exp_avg_sq")):
+            parity.assert_bitwise("rank %d %s: host vs GPU pass" % (k, name), state[k][f].numpy(),
+                                  parity.f32(gpu.state(k)[f]))
+    parity.assert_bitwise("params: host vs GPU pass", parity.u16(host.full_params),
+                          parity.u16(gpu.full_params))
