@@ -91,14 +91,14 @@ CASES = _cases()
 
 def _describe(s):
     return ("P%d N%d R%d A%d %s/%s K%d%s%s %s steps%d lr%.1e b1 %g b2 %g eps %g wd %g "
-            "clip %g scale %g%s D %g%s" % (
+            "clip %g scale %g%s D %g" % (
                 s.numel, s.world_size, s.n_replicas, s.alignment, str(s.grad_dtype)[6:],
                 str(s.param_dtype)[6:], s.micro_batches, " local" if s.local_accumulation else "",
                 " poison@%d" % next(i for i, p in enumerate(s.poison) if p) if s.poison else "",
                 "tiled" if s.state_layout == Z.ZERO_STATE_TILED else "separate", s.steps,
                 s.hp.lr, s.hp.beta1, s.hp.beta2, s.hp.eps, s.hp.weight_decay,
                 s.hp.max_grad_norm, s.hp.loss_scale, " dynamic" if s.dynamic_scale else "",
-                s.hp.grad_predivide, ""))
+                s.hp.grad_predivide))
 
 
 def test_draws_cover_every_axis():
