@@ -179,7 +179,7 @@ int zero_bucket_flatten(const zero_tensor_slot_t* slots, int32_t n_tensors,
  *
  * (zero_step_scalars_t, below, may hold the step's scalars in device
  * memory; declared here so the arguments can point at it.) */
-struct zero_step_scalars;
+struct zero_step_scalars_s;
 
 /*
  * Arguments of one rank's step.  Hyper-parameters follow [P1] §3.1 (AdamW,
@@ -252,7 +252,7 @@ typedef struct {
      * captured step replays with whatever the caller last wrote there
      * (zero_step_scalars fills it on the host).  The fields above are still
      * checked.  zero_offload_apply does not read it. */
-    const struct zero_step_scalars* scalars;
+    const struct zero_step_scalars_s* scalars;
 } zero_step_args;
 
 /* Result of the cross-rank combine, 32 bytes in device memory. */
@@ -382,7 +382,7 @@ int zero_shard_step(const zero_step_args* a, double peer_sumsq,
  * loss scale may all change) and copies it to the device.  64 bytes.
  * ([P1] §3.1 AdamW hyper-parameters, §3.3 / §5.1 loss scale, §6 clipping.)
  */
-typedef struct zero_step_scalars {
+typedef struct zero_step_scalars_s {
     float   inv_scale;        /* fp32(1 / (loss_scale * grad_predivide))     */
     float   decay;            /* fp32(1 - lr * weight_decay)                 */
     float   beta1;            /* fp32(beta1)                                 */

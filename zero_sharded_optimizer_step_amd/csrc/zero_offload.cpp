@@ -159,7 +159,7 @@ void adamw_parallel(const HostUpdate& u, int64_t n, const float* g, const HostSt
     }
     const int64_t per = (n + t - 1) / t / 16 * 16 + 16;
     std::vector<std::thread> pool;
-    pool.reserve(t);
+    pool.reserve(static_cast<size_t>(t));
     for (int i = 0; i < t; ++i) {
         const int64_t lo = std::min<int64_t>(n, i * per), hi = std::min<int64_t>(n, lo + per);
         if (lo < hi) pool.emplace_back(adamw_span, std::cref(u), lo, hi, g, std::cref(s), base, out);
@@ -254,7 +254,8 @@ int zero_offload_apply(const zero_step_args* a, const void* global_dev,
     }
     auto len_of = [&](int64_t c) { return std::min(C, n - c * C); };
     auto fetch = [&](int64_t c) -> hipError_t {
-        hipError_t r = hipMemcpyAsync(stg->grad_stage[c & 1], g_dev + c * C, len_of(c) * 4,
+        hipError_t r = hipMemcpyAsync(stg->grad_stage[c & 1], g_dev + c * C,
+                                      static_cast<size_t>(len_of(c)) * 4,
                                       hipMemcpyDeviceToHost, st);
         if (r == hipSuccess) r = hipEventRecord(down_done[c & 1], st);
         return r;
@@ -271,7 +272,8 @@ int zero_offload_apply(const zero_step_args* a, const void* global_dev,
         // is addressed by element, from the chunk start lo.
         adamw_parallel(u, len, static_cast<const float*>(stg->grad_stage[c & 1]), hs, lo, pst,
                        stg->n_threads);
-        e = hipMemcpyAsync(out_dev + lo, pst, len * 2, hipMemcpyHostToDevice, up);
+        e = hipMemcpyAsync(out_dev + lo, pst, static_cast<size_t>(len) * 2, hipMemcpyHostToDevice,
+                           up);
         if (e == hipSuccess) e = hipEventRecord(up_done[c & 1], up);
     }
     // Wait for both streams whatever happened above: after an error some
