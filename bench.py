@@ -36,6 +36,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "ZeRO shard step: params updated/s + achieved HBM GB/s (% of 8 TB/s peak)"
+# stage3_max_live_parameters of the pages' ZeRO-3 configuration
+# ("ZeRO技术解析：大模型分布式训练的革命性突破" §3.1)
+MAX_LIVE_PARAMETERS = int(1e9)
 
 
 def parse():
@@ -751,8 +754,9 @@ def run_zero3(args, torch, Z, W):
     """ZeRO-3 forward-pass gathering on the 13B/8 model: its bf16 parameters
     sit as 8 rank shards (one 26 GB buffer); one step walks 40 equal layers
     in order, each gathered from the shards on a side stream, prefetched
-    within a live bound of two layers.  Bytes: every parameter read from its
-    shard and written to its layer buffer, 4 B."""
+    within the live bound of the pages' configuration
+    (stage3_max_live_parameters = 1e9 elements, three layers).  Bytes: every
+    parameter read from its shard and written to its layer buffer, 4 B."""
     from zero_sharded_optimizer_step_amd.zero3 import LayerGatherer
     w = W.SHARD_13B_OF_8
     part = Z.zero_partition(w.numel, w.world_size, w.alignment)
@@ -763,7 +767,7 @@ def run_zero3(args, torch, Z, W):
     L = 40
     sizes = [w.numel // L] * L
     sizes[-1] += w.numel - sum(sizes)
-    g = LayerGatherer(part, shards, sizes, int(2e8), 2 * max(sizes))
+    g = LayerGatherer(part, shards, sizes, int(2e8), MAX_LIVE_PARAMETERS)
     stream = torch.cuda.current_stream()
 
     def walk():
@@ -789,8 +793,8 @@ def run_zero3(args, torch, Z, W):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "13B bf16 parameters as 8 rank shards, gathered as 40 layers with "
-                               "prefetch (live bound: 2 layers)", "params": w.numel,
-                   "layers": L},
+                               "prefetch (live bound: 1e9 parameters)", "params": w.numel,
+                   "layers": L, "max_live_parameters": MAX_LIVE_PARAMETERS},
         "hbm_gbps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS, "bytes_per_step": nbytes,
         "roofline": {"bound": "hbm", "kernel": "flatten_kernel (range copies of zero_gather_params, "
                                                 "all launches of one walk)",

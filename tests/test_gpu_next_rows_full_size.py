@@ -131,7 +131,7 @@ def test_zero3_gather_13b_in_bench_configuration():
     L = 40
     sizes = [w.numel // L] * L
     sizes[-1] += w.numel - sum(sizes)
-    g = LayerGatherer(part, shards, sizes, int(2e8), 2 * max(sizes))
+    g = LayerGatherer(part, shards, sizes, int(2e8), int(1e9))    # the bench's live bound
     rng = np.random.default_rng(9)
     edges = np.concatenate([np.cumsum(sizes)[:-1], np.arange(1, w.world_size) * s])
     sample = np.unique(np.concatenate([rng.integers(0, w.numel, 1 << 16, dtype=np.int64),

@@ -119,3 +119,38 @@ def test_layer_walk_with_a_slow_caller_keeps_every_layer():
     for t, c in enumerate(copies):
         parity.assert_bitwise("layer %d" % t, parity.u16(c),
                               oracle.gather(host, L * n, 4, 128, t * n, (t + 1) * n))
+
+
+def test_walks_queued_ahead_stay_within_the_live_bound():
+    """The host queues three whole walks before the device has run them,
+    behind a caller that sleeps on its stream before copying each layer
+    out.  The walks allocate nothing but the gatherer's arena of max_live
+    elements, and every layer of every walk equals its range."""
+    L, n = 24, 1 << 16
+    sizes = [n + 8 * (t % 3) for t in range(L)]       # unequal layers, one per bucket
+    P = sum(sizes)
+    offs = np.concatenate([[0], np.cumsum(sizes)])
+    part = Z.zero_partition(P, 4, 128)
+    s = part.shard_numel
+    shards = [torch.randint(-32768, 32767, (s,), dtype=torch.int16, device="cuda")
+              .view(torch.bfloat16) for _ in range(4)]
+    host = [parity.u16(x) for x in shards]
+    max_live = 3 * max(sizes) + 5
+    say("queued walks: %d layers, max live %d" % (L, max_live))
+    g = LayerGatherer(part, shards, sizes, n, max_live)
+    outs = [torch.empty(P, dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    for out in outs:
+        for t, params in g.forward():
+            torch.cuda._sleep(200_000)
+            out[offs[t]:offs[t + 1]].copy_(params)
+    torch.cuda.synchronize()
+    grown = torch.cuda.max_memory_allocated() - base
+    assert grown <= 2 * max_live + (2 << 20), "the walks held %d bytes" % grown
+    for w, out in enumerate(outs):
+        got = parity.u16(out)
+        for t in range(L):
+            parity.assert_bitwise("walk %d layer %d" % (w, t), got[offs[t]:offs[t + 1]],
+                                  oracle.gather(host, P, 4, 128, int(offs[t]), int(offs[t + 1])))

@@ -1,0 +1,53 @@
+"""CPU checks of the ZeRO-3 walk's arena placement (zero3.ring_place).
+
+The walk gathers buckets into one arena of max_live elements, in bucket
+order, and a gather may only take space that no bucket the caller still
+holds occupies.  Here random sequences of placements (sizes from zero to
+the whole arena) and releases (oldest first) are simulated: every placed
+bucket must lie inside the arena and overlap no held bucket, and an empty
+arena must take any bucket that fits it.
+"""
+import numpy as np
+import pytest
+
+from zero_sharded_optimizer_step_amd.zero3 import ring_place
+
+
+def _overlap(a, b):
+    return a[0] < b[1] and b[0] < a[1]
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_ring_place_never_overlaps_a_held_bucket(seed):
+    rng = np.random.default_rng(seed)
+    cap = int(rng.integers(1, 200))
+    held = []
+    placed = 0
+    for _ in range(3000):
+        if held and rng.random() < 0.45:
+            held.pop(0)                                   # the caller leaves the oldest
+            continue
+        size = int(rng.integers(0, cap + 1)) if rng.random() < 0.3 else \
+            int(rng.integers(0, max(1, cap // 3) + 1))
+        start = ring_place(held, size, cap)
+        if not held:
+            assert start == 0
+        if start is None:
+            continue
+        new = (start, start + size)
+        assert 0 <= new[0] and new[1] <= cap, (held, size, cap, new)
+        for h in held:
+            assert not _overlap(new, h), (held, size, cap, new)
+        held.append(new)
+        placed += 1
+    assert placed > 100
+
+
+def test_ring_place_examples():
+    assert ring_place([], 10, 10) == 0
+    assert ring_place([(0, 4)], 4, 10) == 4
+    assert ring_place([(0, 4), (4, 8)], 3, 10) is None       # 2 left at the end, none at the start
+    assert ring_place([(4, 8)], 3, 10) == 0                   # wraps to the freed start
+    assert ring_place([(4, 8), (0, 3)], 1, 10) == 3           # wrapped: [3, 4) is free
+    assert ring_place([(4, 8), (0, 3)], 2, 10) is None
+    assert ring_place([(5, 5)], 3, 10) == 5                   # an empty bucket takes no room
