@@ -154,3 +154,29 @@ def test_walks_queued_ahead_stay_within_the_live_bound():
         for t in range(L):
             parity.assert_bitwise("walk %d layer %d" % (w, t), got[offs[t]:offs[t + 1]],
                                   oracle.gather(host, P, 4, 128, int(offs[t]), int(offs[t + 1])))
+
+
+def test_walks_on_different_caller_streams():
+    """Consecutive walks from different caller streams: the second walk's
+    gathers wait for the first stream's pending reads of the arena."""
+    L, n = 12, 1 << 16
+    sizes = [n] * L
+    part = Z.zero_partition(L * n, 4, 128)
+    s = part.shard_numel
+    shards = [torch.randint(-32768, 32767, (s,), dtype=torch.int16, device="cuda")
+              .view(torch.bfloat16) for _ in range(4)]
+    host = [parity.u16(x) for x in shards]
+    say("walks on two caller streams")
+    g = LayerGatherer(part, shards, sizes, n, 2 * n)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]      # default priority
+    outs = [torch.empty(L * n, dtype=torch.bfloat16, device="cuda") for _ in streams]
+    torch.cuda.synchronize()
+    for st, out in zip(streams, outs):
+        with torch.cuda.stream(st):
+            for t, params in g.forward(st):
+                torch.cuda._sleep(200_000)
+                out[t * n:(t + 1) * n].copy_(params)
+    torch.cuda.synchronize()
+    ref = oracle.gather(host, L * n, 4, 128, 0, L * n)
+    for w, out in enumerate(outs):
+        parity.assert_bitwise("walk %d" % w, parity.u16(out), ref)

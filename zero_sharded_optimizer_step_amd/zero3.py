@@ -70,6 +70,7 @@ class LayerGatherer:
         self.max_live = max_live
         self.side = torch.cuda.Stream()              # default priority
         self.arena = None                            # max_live elements, from the first walk
+        self.last_stream = None                      # the caller's stream of the last walk
 
     def forward(self, stream=None) -> Iterator[Tuple[int, torch.Tensor]]:
         """Yield (layer index, its gathered parameters) in order; each view is
@@ -81,8 +82,12 @@ class LayerGatherer:
                                      device=self.shards[0].device)
             self.arena.record_stream(self.side)      # kept until the side stream is done
         # The side stream follows all the caller has queued so far: the
-        # shards' last writes and an earlier walk's last reads of the arena.
+        # shards' last writes and an earlier walk's last reads of the arena,
+        # also when that walk ran on another stream.
         self.side.wait_stream(main)
+        if self.last_stream is not None and self.last_stream != main:
+            self.side.wait_stream(self.last_stream)
+        self.last_stream = main
         pending = deque()       # gathered, not yet left by the caller: (bucket, start, end, event)
         released = []           # left by the caller, maybe still read on its stream: (start, end, event)
         nxt = 0
