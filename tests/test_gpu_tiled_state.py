@@ -261,3 +261,33 @@ def test_tiled_13b_shard_every_element():
     for a0 in range(s, part.padded_numel, 1 << 30):
         assert bool((full[a0:min(part.padded_numel, a0 + (1 << 30))] == parity.CANARY).all())
     say("tiled 13B/8 matches the oracle over all %d elements" % n)
+
+
+def test_noalloc_step_over_tiled_state_equals_step_with_workspace():
+    """The allocation-free step (the library's scratch array as workspace)
+    on a tiled state equals zero_shard_step with a caller-owned workspace,
+    bit for bit, over two steps of rank 1 of a 3-rank world."""
+    P, N, k = 200_003, 3, 1
+    say("noalloc over a tiled state")
+    worlds = [SimulatedWorld(P, N, n_replicas=4, alignment=8, grad_dtype=FP16,
+                             state_layout=TILED) for _ in range(2)]
+    for w in worlds:
+        m0 = torch.empty(w.s, dtype=torch.float32, device="cuda")
+        W.flat_normal(m0, k * w.s, P, 0.02, ("tiled-noalloc",))
+        w.set_state(k, m0)
+        w.full_params.view(torch.int16).fill_(parity.CANARY)
+    assert worlds[0].s <= Z.ZERO_NOALLOC_MAX_SHARD
+    hp = Hyper(loss_scale=2.0**10, max_grad_norm=0.5)
+    for t in (1, 2):
+        for w in worlds:
+            for i in range(4):
+                W.flat_normal(w.grads[i], 0, P, 1e-3, ("tiled-noalloc", t, i), scale=hp.loss_scale)
+        ia = Z.zero_shard_step(worlds[0].rank_args(k, hp, t), want_info=True)
+        b = worlds[1].rank_args(k, hp, t)
+        b.workspace = None
+        ib = Z.zero_shard_step_noalloc(b, want_info=True)
+        for f in ("sumsq", "norm", "coef", "overflow", "clipped"):
+            assert getattr(ia, f) == getattr(ib, f), (t, f)
+        assert torch.equal(worlds[0].tiled[k].view(torch.int32), worlds[1].tiled[k].view(torch.int32))
+        assert torch.equal(worlds[0].full_params.view(torch.int16),
+                           worlds[1].full_params.view(torch.int16))
