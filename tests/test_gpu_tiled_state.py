@@ -8,8 +8,9 @@ not what it holds: a tiled world's step must match the oracle element by
 element (untiled by the library's own conversion), exactly as a separate
 world's does.  Also covered: the conversion itself (tile, untile), the
 out-of-place tiled step, re-partitioning a tiled state, a checkpoint round
-trip between the layouts, the offloaded step over a tiled host state, and
-the 13B/8 shard at full size against the oracle, every element.
+trip between the layouts, the offloaded step over a tiled host state, the
+allocation-free step, and the 13B/8 shard at full size against the oracle,
+every element.
 """
 import numpy as np
 import pytest
