@@ -166,3 +166,49 @@ def test_random_offloaded_steps_equal_gpu_pass(case):
                                   parity.f32(gpu.state(k)[f]))
     parity.assert_bitwise("params: host vs GPU pass", parity.u16(host.full_params),
                           parity.u16(gpu.full_params))
+
+
+@pytest.mark.parametrize("local", [False, True])
+def test_offloaded_step_after_an_accumulation_window(local):
+    """A window of 3 micro-batches, accumulated per micro-batch into the
+    ranks' slices or before the reduce (fp32 window sums), then the
+    offloaded update: bitwise equal to the GPU pass after the same window."""
+    numel, N, K = 250_007, 3, 3
+    say("offload after a window of %d, %s accumulation" % (K, "local" if local else "reduced"))
+    gdt = torch.float32 if local else torch.bfloat16
+    gpu = SimulatedWorld(numel, N, alignment=8, grad_dtype=gdt, param_dtype=torch.bfloat16)
+    host = SimulatedWorld(numel, N, alignment=8, grad_dtype=gdt, param_dtype=torch.bfloat16)
+    for w in (gpu, host):
+        for k in range(N):
+            W.flat_normal(w.master[k], k * w.s, numel, 0.02, ("off-window",))
+    state = _pinned_state(host)
+    staging = Z.OffloadStaging(10_000, n_threads=3)
+    micro = [torch.empty(gpu.grads[0].numel(), dtype=torch.bfloat16, device="cuda")
+             for _ in range(N)]
+    hp = Hyper(max_grad_norm=0.5)
+    for t in (1, 2):
+        for j in range(K):
+            for w in (gpu, host):
+                for i in range(N):
+                    target = micro[i] if local else w.grads[i]
+                    W.flat_normal(target, 0, numel, 1e-3, ("off-window", t, j, i))
+                if local:
+                    w.accumulate_local(micro, first=j == 0)
+                elif j < K - 1:
+                    w.accumulate(hp, first=j == 0)
+        acc = K > 1 and not local
+        gpu.step(hp, t, accumulate=acc)
+        args = [host.rank_args(k, hp, t, accumulate=acc) for k in range(N)]
+        for k, a in enumerate(args):
+            Z.zero_shard_reduce(a, k, host.partials)
+        Z.zero_shard_combine(host.partials, N, hp.max_grad_norm, host.global_buf)
+        for k, a in enumerate(args):
+            a.master, a.exp_avg, a.exp_avg_sq = state[k]
+            info = Z.zero_offload_apply(a, host.global_buf, staging, want_info=True)
+            assert info.overflow == 0 and info.coef == gpu.result().coef
+    for k in range(N):
+        for f, name in enumerate(("master", "exp_avg", "exp_avg_sq")):
+            parity.assert_bitwise("rank %d %s: host vs GPU pass" % (k, name), state[k][f].numpy(),
+                                  parity.f32(gpu.state(k)[f]))
+    parity.assert_bitwise("params: host vs GPU pass", parity.u16(host.full_params),
+                          parity.u16(gpu.full_params))
