@@ -138,8 +138,10 @@ def _scalars_bytes(sc):
     return torch.frombuffer(bytearray(bytes(sc)), dtype=torch.uint8)
 
 
-@pytest.mark.parametrize("entry", ["step", "noalloc"])
-def test_captured_step_with_device_scalars_serves_every_step(entry):
+@pytest.mark.parametrize("entry,layout", [("step", Z.ZERO_STATE_SEPARATE),
+                                          ("noalloc", Z.ZERO_STATE_SEPARATE),
+                                          ("step", Z.ZERO_STATE_TILED)])
+def test_captured_step_with_device_scalars_serves_every_step(entry, layout):
     # One capture of a step whose scalars live in a device buffer
     # (zero_step_args.scalars), replayed for 6 consecutive training steps:
     # before each replay the host refills the buffer with zero_step_scalars
@@ -149,9 +151,11 @@ def test_captured_step_with_device_scalars_serves_every_step(entry):
     # replay must equal an eager step with the same scalars as launch
     # arguments, bit for bit, and the eager run must match the oracle.
     numel, R = 400_009, 4
-    print("graph capture with device scalars (%s)" % entry, flush=True)
-    eager = SimulatedWorld(numel, 1, n_replicas=R, alignment=128, grad_dtype=torch.float16)
-    graph_w = SimulatedWorld(numel, 1, n_replicas=R, alignment=128, grad_dtype=torch.float16)
+    print("graph capture with device scalars (%s, layout %d)" % (entry, layout), flush=True)
+    eager = SimulatedWorld(numel, 1, n_replicas=R, alignment=128, grad_dtype=torch.float16,
+                           state_layout=layout)
+    graph_w = SimulatedWorld(numel, 1, n_replicas=R, alignment=128, grad_dtype=torch.float16,
+                             state_layout=layout)
     scal_dev = torch.zeros(64, dtype=torch.uint8, device="cuda")
     sc_lib = Z.zero_loss_scaler_init(12, 2, 1, 1.0)
     o_sc = oracle.LossScaler(12, 2, 1, 1.0)
@@ -174,9 +178,9 @@ def test_captured_step_with_device_scalars_serves_every_step(entry):
 
     def reset():
         for w in (eager, graph_w):
-            W.flat_normal(w.master[0], 0, numel, 0.02, ("graph-sc-m",))
-            w.exp_avg[0].zero_()
-            w.exp_avg_sq[0].zero_()
+            m0 = torch.empty(w.s, dtype=torch.float32, device="cuda")
+            W.flat_normal(m0, 0, numel, 0.02, ("graph-sc-m",))
+            w.set_state(0, m0)                   # zero moments
             w.full_params.zero_()
 
     scal_dev.copy_(_scalars_bytes(Z.zero_step_scalars(graph_args(1, sc_lib.scale))))
@@ -186,7 +190,7 @@ def test_captured_step_with_device_scalars_serves_every_step(entry):
         call(graph_args(1, sc_lib.scale), stream=s)
     torch.cuda.synchronize()
     reset()
-    o_p = parity.f32(eager.master[0])[:numel].copy()
+    o_p = parity.f32(eager.separate_state(0)[0])[:numel].copy()
     o_m = np.zeros(numel, np.float32)
     o_v = np.zeros(numel, np.float32)
     o_full = np.zeros(numel, np.uint16)
@@ -215,9 +219,9 @@ def test_captured_step_with_device_scalars_serves_every_step(entry):
                            oracle.Hyper(lr=hyper(t, scale).lr, loss_scale=scale), t)
         assert bool(res.overflow) == info.overflow == (rep == 3)
         for f, name in enumerate(("master", "exp_avg", "exp_avg_sq")):
-            got = parity.f32(graph_w.state(0)[f][:numel])
+            got = parity.f32(graph_w.separate_state(0)[f][:numel])
             parity.assert_bitwise("replay %d %s vs eager" % (rep, name), got,
-                                  parity.f32(eager.state(0)[f][:numel]))
+                                  parity.f32(eager.separate_state(0)[f][:numel]))
             parity.assert_rel("replay %d %s vs oracle" % (rep, name), got, (o_p, o_m, o_v)[f],
                               parity.RTOL_STATE)
         parity.assert_bitwise("replay %d params" % rep, parity.u16(graph_w.full_params),
