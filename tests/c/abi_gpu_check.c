@@ -11,6 +11,9 @@
  * masters (rank r's shard at r * shard_numel).
  * Output, per step: zero_global_t, then padded_numel fp32 master, exp_avg,
  * exp_avg_sq, then padded_numel 16-bit full parameters.
+ * With a third argument `noalloc` (a world of one rank only), each step is
+ * one zero_shard_step_noalloc call instead, and no workspace is allocated:
+ * the library's own scratch memory serves.
  * Exit status 0 on success; a failing call prints its error. */
 #include <stdio.h>
 #include <stdlib.h>
@@ -54,10 +57,11 @@
 enum { MAX_RANKS = 64 };
 
 int main(int argc, char** argv) {
-    if (argc != 3) {
-        fprintf(stderr, "usage: %s input output\n", argv[0]);
+    if (argc != 3 && !(argc == 4 && strcmp(argv[3], "noalloc") == 0)) {
+        fprintf(stderr, "usage: %s input output [noalloc]\n", argv[0]);
         return 1;
     }
+    const int noalloc = argc == 4;
     FILE* in = fopen(argv[1], "rb");
     if (!in) return 1;
     int64_t hdr[6];
@@ -68,6 +72,7 @@ int main(int argc, char** argv) {
     const int32_t world = (int32_t)hdr[1], align = (int32_t)hdr[2], nrep = (int32_t)hdr[3];
     const int32_t dtype = (int32_t)hdr[4], steps = (int32_t)hdr[5];
     if (world < 1 || world > MAX_RANKS || nrep < 1 || nrep > ZERO_MAX_REPLICAS) return 1;
+    if (noalloc && world != 1) return 1;
     zero_partition_t part;
     ZCHECK(zero_partition(numel, world, align, &part));
     const int64_t s = part.shard_numel, padded = part.padded_numel;
@@ -98,7 +103,10 @@ int main(int argc, char** argv) {
     HIPCHECK(hipMemset(d_v, 0, (size_t)padded * 4));
     HIPCHECK(hipMalloc(&d_full, (size_t)padded * 2));
     HIPCHECK(hipMemset(d_full, 0, (size_t)padded * 2));
-    for (int r = 0; r < world; ++r) HIPCHECK(hipMalloc(&d_ws[r], ws_bytes));
+    for (int r = 0; r < world; ++r) {
+        d_ws[r] = NULL;
+        if (!noalloc) HIPCHECK(hipMalloc(&d_ws[r], ws_bytes));
+    }
     HIPCHECK(hipMalloc(&d_partials, zero_partials_bytes(world)));
     HIPCHECK(hipMalloc(&d_global, 256));
     hipStream_t st;
@@ -126,7 +134,7 @@ int main(int argc, char** argv) {
             a[r].exp_avg_sq = d_v + (size_t)r * s;
             a[r].full_params = d_full;
             a[r].workspace = d_ws[r];
-            a[r].workspace_bytes = ws_bytes;
+            a[r].workspace_bytes = noalloc ? 0 : ws_bytes;
             a[r].lr = 6e-5;
             a[r].beta1 = 0.9;
             a[r].beta2 = 0.999;
@@ -136,13 +144,18 @@ int main(int argc, char** argv) {
             a[r].loss_scale = hp[0];
             a[r].grad_predivide = 1.0;
             a[r].max_grad_norm = hp[1];
-            ZCHECK(zero_shard_reduce(&a[r], r, d_partials, st));
+            if (!noalloc) ZCHECK(zero_shard_reduce(&a[r], r, d_partials, st));
         }
-        ZCHECK(zero_shard_combine(d_partials, world, hp[1], d_global, st));
-        for (int r = 0; r < world; ++r) ZCHECK(zero_shard_apply(&a[r], d_global, st));
-        HIPCHECK(hipStreamSynchronize(st));
         zero_global_t g;
-        HIPCHECK(hipMemcpy(&g, d_global, sizeof g, hipMemcpyDeviceToHost));
+        if (noalloc) {
+            /* the whole step of the one rank; info waits for the stream */
+            ZCHECK(zero_shard_step_noalloc(&a[0], 0.0, 0, &g, st));
+        } else {
+            ZCHECK(zero_shard_combine(d_partials, world, hp[1], d_global, st));
+            for (int r = 0; r < world; ++r) ZCHECK(zero_shard_apply(&a[r], d_global, st));
+            HIPCHECK(hipStreamSynchronize(st));
+            HIPCHECK(hipMemcpy(&g, d_global, sizeof g, hipMemcpyDeviceToHost));
+        }
         WRITE(&g, sizeof g);
         float* fields[3] = {d_master, d_m, d_v};
         for (int f = 0; f < 3; ++f) {
@@ -154,7 +167,8 @@ int main(int argc, char** argv) {
     }
     fclose(out);
     for (int i = 0; i < nrep; ++i) HIPCHECK(hipFree(d_reps[i]));
-    for (int r = 0; r < world; ++r) HIPCHECK(hipFree(d_ws[r]));
+    for (int r = 0; r < world; ++r)
+        if (d_ws[r]) HIPCHECK(hipFree(d_ws[r]));
     HIPCHECK(hipFree(d_master));
     HIPCHECK(hipFree(d_m));
     HIPCHECK(hipFree(d_v));

@@ -1,7 +1,9 @@
 """The device entry points from plain C: tests/c/abi_gpu_check (built by
 __graft_entry__.build() with gcc against include/zero.h and the HIP runtime)
 allocates with hipMalloc, runs every rank's reduce, the combine and every
-rank's apply for two steps on one stream, and writes the results to a file.
+rank's apply for two steps on one stream (or, for a world of one rank,
+zero_shard_step_noalloc with no workspace at all), and writes the results to
+a file.
 No Python or torch takes part in those calls.  The results are compared
 with the oracle's world step on the same inputs."""
 import os
@@ -21,15 +23,19 @@ GLOBAL = np.dtype([("sumsq", "<f8"), ("norm", "<f8"), ("coef", "<f4"), ("overflo
                    ("clipped", "<i4"), ("reserved", "<i4")])
 
 
-@pytest.mark.parametrize("P,N,A,R,dtype,scale,clip", [
-    (100_003, 4, 128, 4, oracle.BF16, 1.0, 1.0),
-    (30_011, 3, 8, 5, oracle.FP16, 2.0**12, 1.0),
-    (5, 4, 8, 2, oracle.BF16, 1.0, 0.0),            # three empty ranks, clipping off
+@pytest.mark.parametrize("P,N,A,R,dtype,scale,clip,mode", [
+    (100_003, 4, 128, 4, oracle.BF16, 1.0, 1.0, None),
+    (30_011, 3, 8, 5, oracle.FP16, 2.0**12, 1.0, None),
+    (5, 4, 8, 2, oracle.BF16, 1.0, 0.0, None),      # three empty ranks, clipping off
+    # one rank's whole step through zero_shard_step_noalloc, no workspace
+    (50_021, 1, 128, 3, oracle.FP16, 2.0**10, 1.0, "noalloc"),
+    (5, 1, 8, 2, oracle.BF16, 1.0, 0.0, "noalloc"),
 ])
-def test_plain_c_world_step_matches_oracle(tmp_path, P, N, A, R, dtype, scale, clip):
+def test_plain_c_world_step_matches_oracle(tmp_path, P, N, A, R, dtype, scale, clip, mode):
     if not os.path.exists(EXE):
         pytest.fail("tests/c/abi_gpu_check is not built: run __graft_entry__.build()")
-    print("plain C caller: P=%d N=%d R=%d dtype=%d" % (P, N, R, dtype), flush=True)
+    print("plain C caller: P=%d N=%d R=%d dtype=%d %s" % (P, N, R, dtype, mode or ""),
+          flush=True)
     s, padded, valid = oracle.partition(P, N, A)
     rng = np.random.default_rng(P)
     enc = oracle.f32_to_f16 if dtype == oracle.FP16 else oracle.f32_to_bf16
@@ -48,7 +54,8 @@ def test_plain_c_world_step_matches_oracle(tmp_path, P, N, A, R, dtype, scale, c
         for x in reps:
             x.tofile(f)
         masters.tofile(f)
-    r = subprocess.run([EXE, src, dst], capture_output=True, text=True, timeout=120)
+    r = subprocess.run([EXE, src, dst] + ([mode] if mode else []), capture_output=True,
+                       text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     raw = np.fromfile(dst, np.uint8)
     per_step = GLOBAL.itemsize + 3 * 4 * padded + 2 * padded
