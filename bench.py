@@ -501,7 +501,6 @@ def run_ragged(args, torch, Z, W):
     offsets of one pool) flattened bucket by bucket into its flat buffer,
     then the step of all 8 ranks (reduce per rank, one combine, AdamW +
     cast per rank).  One step = both; HIP events split them."""
-    import ctypes
     from zero_sharded_optimizer_step_amd import _abi
     from zero_sharded_optimizer_step_amd.world import Hyper, SimulatedWorld
     w = W.RAGGED_2000

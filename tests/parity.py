@@ -17,7 +17,6 @@ records how many elements are.
 """
 from __future__ import annotations
 
-import math
 import os
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field

@@ -8,7 +8,6 @@ predivide 4).  Each result must equal the existing entry point's bit for
 bit: the combine's result, master, both moments and the full buffer, whose
 elements outside the rank's slice must keep their canary.
 """
-import numpy as np
 import pytest
 import torch
 
