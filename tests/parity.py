@@ -272,8 +272,8 @@ def _compare(world, info, o_master, o_m, o_v, o_full, odt, step, rep):
 # At the workloads' full sizes the oracle cannot hold every input at once.
 # It regenerates each input chunk by chunk from the seeded generator (never
 # from anything the HIP path wrote), runs its reduce over every element to
-# get the norm and overflow flag, and evaluates AdamW on a sample of
-# elements; every other element is covered by whole-buffer properties.
+# get the norm and overflow flag, then its AdamW and cast over every
+# element, a chunk at a time (check_every_element below).
 
 def gen_chunks(lo: int, hi: int, total: int, sigma: float, key, dtype, scale: float = 1.0):
     """Yield (a, b, codes) for consecutive ranges [a, b) covering [lo, hi):
@@ -287,36 +287,6 @@ def gen_chunks(lo: int, hi: int, total: int, sigma: float, key, dtype, scale: fl
         W.flat_normal(t, a, total, sigma, key, scale)
         yield a, b, u16(t)
         a = b
-
-
-@dataclass
-class OracleNorm:
-    sumsq: float
-    overflow: int
-    codes: List[np.ndarray]          # per replica, codes at the sampled indices
-
-
-def oracle_norm_and_sample(n_replicas: int, lo: int, hi: int, total: int, sigma: float,
-                           key_of, dtype, sample: np.ndarray, inv: float,
-                           log: Optional[Callable[[str], None]] = None) -> OracleNorm:
-    """The oracle's reduce over flat [lo, hi) of every replica, in index
-    order (the order its one-pass step takes), regenerated chunk by chunk;
-    also picks out each replica's codes at the sorted flat indices
-    `sample` (all inside [lo, hi))."""
-    odt = oracle_dtype(dtype)
-    ss, of = 0.0, 0
-    codes = [np.empty(sample.size, np.uint16) for _ in range(n_replicas)]
-    gens = [gen_chunks(lo, hi, total, sigma, key_of(i), dtype) for i in range(n_replicas)]
-    for k, parts in enumerate(zip(*gens)):
-        a, b = parts[0][0], parts[0][1]
-        reps = [p[2] for p in parts]
-        _, ss, of = oracle.reduce(reps, odt, inv, ss, of)
-        sel = (sample >= a) & (sample < b)
-        for i in range(n_replicas):
-            codes[i][sel] = reps[i][sample[sel] - a]
-        if log and k % 8 == 0:
-            log("  oracle reduce: [%d, %d) done" % (a, b))
-    return OracleNorm(ss, of, codes)
 
 
 def gather_generated(idx: np.ndarray, lo: int, total: int, sigma: float, key, dtype,
@@ -528,8 +498,7 @@ def shard13b_reference(log: Optional[Callable[[str], None]] = None) -> dict:
     inv = oracle.inv_scale(1.0)
     fr = oracle_reduce_full(w.world_size, 0, n, w.numel, w.grad_sigma, gkey, torch.bfloat16, inv,
                             log=log)
-    on = OracleNorm(fr.sumsq, fr.overflow, [])
-    applies, onorm, ocoef = oracle.clip(on.sumsq, w.max_grad_norm)
+    applies, onorm, ocoef = oracle.clip(fr.sumsq, w.max_grad_norm)
     o_g = fr.g[sample].copy()
     p = gather_generated(sample, 0, w.numel, w.master_sigma, W.master_key(w, 0), torch.float32,
                          n).copy()
@@ -541,7 +510,7 @@ def shard13b_reference(log: Optional[Callable[[str], None]] = None) -> dict:
         oracle.adamw(o_g, p, m, v, ocoef, hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, t)
         states.append((p.copy(), m.copy(), v.copy()))
     _SHARD13B = dict(w=w, part=part, s=part.shard_numel, n=n, gkey=gkey, sample=sample, inv=inv,
-                     overflow=on.overflow, sumsq=on.sumsq, applies=applies, norm=onorm,
+                     overflow=fr.overflow, sumsq=fr.sumsq, applies=applies, norm=onorm,
                      coef=ocoef, g=o_g, g_full=fr.g, states=states, hp=hp,
                      init_master=lambda a, b: gen_host(a, b, w.numel, w.master_sigma,
                                                        W.master_key(w, 0)))
