@@ -101,7 +101,7 @@ def test_13b_shard_in_bench_configuration():
                           grad_dtype=torch.bfloat16, param_dtype=torch.bfloat16)
 
     # the oracle's norm over every element, from regenerated inputs, and
-    # its AdamW on a sample
+    # its AdamW on a sample as a quick pre-check (every element follows)
     oref = parity.shard13b_reference(log=say)
     sample, inv = oref["sample"], oref["inv"]
     assert oref["overflow"] == 0
