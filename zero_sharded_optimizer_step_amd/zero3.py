@@ -81,6 +81,7 @@ class LayerGatherer:
             self.arena = torch.empty(self.max_live, dtype=self.dtype,
                                      device=self.shards[0].device)
             self.arena.record_stream(self.side)      # kept until the side stream is done
+        self.arena.record_stream(main)               # and every caller stream that read it
         # The side stream follows all the caller has queued so far: the
         # shards' last writes and an earlier walk's last reads of the arena,
         # also when that walk ran on another stream.
