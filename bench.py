@@ -26,9 +26,11 @@ same inputs on one host core.
 from __future__ import annotations
 
 import argparse
+import contextlib
 import json
 import os
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -348,16 +350,43 @@ def run_shard13b_local(args, torch, Z, W):
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
-        out["cpu_baseline"] = cpu_baseline_local(args, torch, W, own, peers, K)
+        with one_host_core():
+            out["cpu_baseline"] = cpu_baseline_local(args, torch, W, own, peers, K)
     print(json.dumps(out), flush=True)
+
+
+@contextlib.contextmanager
+def one_host_core():
+    """Run the block with the calling thread pinned to one CPU of the
+    process's set (the oracle is single-threaded; pinning keeps the timing
+    off thread migrations), and restore the thread's CPUs after."""
+    global _HOST_CPUS
+    tid = threading.get_native_id()
+    before = os.sched_getaffinity(tid)
+    _HOST_CPUS = len(before)
+    try:
+        os.sched_setaffinity(tid, {min(before)})
+        pinned = True
+    except OSError:
+        pinned = False
+    try:
+        yield
+    finally:
+        if pinned:
+            os.sched_setaffinity(tid, before)
+
+
+_HOST_CPUS = None      # the CPUs the thread could use before one_host_core pinned it
 
 
 def cpu_record(n, dt, sample, total):
     """A `cpu_baseline` entry: the oracle's rate over a sample of n of the
     workload's `total` params (the timed region covers those n only)."""
+    mine = os.sched_getaffinity(threading.get_native_id())
+    where = "pinned to CPU %d" % min(mine) if len(mine) == 1 else "unpinned"
     return dict(value=n / dt, unit="params/s", cores=1, kind="oracle",
-                sample="%s; one host thread of %s (%d CPUs available), %.1f s"
-                       % (sample, host_cpu(), len(os.sched_getaffinity(0)), dt),
+                sample="%s; one host thread of %s (%d CPUs available, %s), %.1f s"
+                       % (sample, host_cpu(), _HOST_CPUS or len(mine), where, dt),
                 sample_elements=int(n), workload_elements=int(total),
                 sample_fraction=float(n) / float(total) if total else 1.0, seconds=dt)
 
@@ -606,7 +635,8 @@ def report_ragged(args, r, W, torch):
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
-        out["cpu_baseline"] = cpu_baseline_ragged(args, torch, W, r)
+        with one_host_core():
+            out["cpu_baseline"] = cpu_baseline_ragged(args, torch, W, r)
     print(json.dumps(out), flush=True)
 
 
@@ -674,7 +704,8 @@ def run_repartition(args, torch, Z, W):
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
-        out["cpu_baseline"] = cpu_baseline_repartition(args, torch, src)
+        with one_host_core():
+            out["cpu_baseline"] = cpu_baseline_repartition(args, torch, src)
     print(json.dumps(out), flush=True)
 
 
@@ -745,7 +776,8 @@ def run_offload(args, torch, Z, W):
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
-        out["cpu_baseline"] = cpu_baseline_shard13b(args, torch, W, grads)
+        with one_host_core():
+            out["cpu_baseline"] = cpu_baseline_shard13b(args, torch, W, grads)
     print(json.dumps(out), flush=True)
 
 
@@ -802,7 +834,8 @@ def run_zero3(args, torch, Z, W):
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
-        out["cpu_baseline"] = cpu_baseline_zero3(args, torch, shards)
+        with one_host_core():
+            out["cpu_baseline"] = cpu_baseline_zero3(args, torch, shards)
     print(json.dumps(out), flush=True)
 
 
@@ -932,8 +965,9 @@ def main():
     out["copy_ceiling"] = cc
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
-        out["cpu_baseline"] = cpu_baseline_shard13b(args, torch, W, r["st"]["grads"],
-                                                    args.micro_batches)
+        with one_host_core():
+            out["cpu_baseline"] = cpu_baseline_shard13b(args, torch, W, r["st"]["grads"],
+                                                        args.micro_batches)
     print(json.dumps(out), flush=True)
 
 
