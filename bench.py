@@ -922,12 +922,14 @@ def main():
                     "achieved": add_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": add_gbps / HBM_PEAK_GBPS, "traffic": measured_traffic("shard13b_accum")}
     else:
-        # counted on the in-place apply (one state set); the ping-pong
-        # variant is another kernel instantiation, whose counters were not taken
+        # counted on the in-place apply over separate arrays (one state set);
+        # the ping-pong and tiled variants are other kernel instantiations,
+        # whose counters were not taken
+        counted = args.state_buffers == 1 and args.state_layout == "separate"
         roofline = {"bound": "hbm", "kernel": "apply_kernel (AdamW + cast)",
                     "achieved": app_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": app_gbps / HBM_PEAK_GBPS,
-                    "traffic": measured_traffic("shard13b") if args.state_buffers == 1 else None}
+                    "traffic": measured_traffic("shard13b") if counted else None}
     out = {
         "metric": METRIC,
         "value": r["valid"] / (r["ms"] * 1e-3),
