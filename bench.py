@@ -542,14 +542,18 @@ def run_ragged(args, torch, Z, W):
                                                                            len(buckets)))
     pools, calls = [], []
     ref = torch.empty(padded, dtype=torch.bfloat16, device="cuda")
+    # tensor k sits at pool offset (its flat offset) + k + 1, so sources
+    # start at odd element offsets; the pool is filled a generator chunk at
+    # a time, each flat element j going to j + k(j) + 1
+    starts = torch.tensor([x.offset for x in slots], dtype=torch.int64, device="cuda")
     for i in range(N):
         W.flat_normal(ref, 0, P, w.grad_sigma, W.grad_key(w, 0, 0, i))
         pool = torch.empty(P + len(sizes) + 8, dtype=torch.bfloat16, device="cuda")
-        ptrs = []
-        for k, x in enumerate(slots):
-            src = pool[x.offset + k + 1:x.offset + k + 1 + x.numel]
-            src.copy_(ref[x.offset:x.offset + x.numel])
-            ptrs.append(src.data_ptr())
+        for a in range(0, P, W.CHUNK):
+            j = torch.arange(a, min(P, a + W.CHUNK), dtype=torch.int64, device="cuda")
+            pool[j + torch.searchsorted(starts, j, right=True)] = ref[a:a + j.numel()]
+            del j
+        ptrs = [pool[x.offset + k + 1:].data_ptr() for k, x in enumerate(slots)]
         pools.append(pool)
         for bi, b in enumerate(buckets):
             sl = slots[b.first_tensor:b.first_tensor + b.n_tensors]
@@ -630,7 +634,7 @@ def report_ragged(args, r, W, torch):
         "step_gbps": step_bytes / (r["step_ms"] * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "kernel": "flatten_kernel (all launches of one step)",
                      "achieved": flat_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": flat_gbps / HBM_PEAK_GBPS, "traffic": None},
+                     "frac": flat_gbps / HBM_PEAK_GBPS, "traffic": measured_traffic("ragged")},
         "step_check": {"norm": r["norm"], "clipped": r["clipped"], "overflow": r["overflow"]},
     }
     if not args.no_cpu_baseline:

@@ -53,4 +53,7 @@ def algorithmic_bytes(rec):
     if rec["workload"] == "repartition":     # 3 fp32 arrays: read once, new padded written
         P = W.RAGGED_2000.numel
         return 3 * (4 * P + 4 * Z.zero_partition(P, 3, 128).padded_numel)
+    if rec["workload"] == "ragged":          # 8 replicas: each real element read, padded written
+        P = W.RAGGED_2000.numel
+        return 8 * (2 * P + 2 * Z.zero_partition(P, 8, 128).padded_numel)
     raise AssertionError("no algorithmic figure for " + rec["workload"])
