@@ -1,4 +1,5 @@
-"""Shared pytest setup: the `gpu` marker and import paths."""
+"""Shared pytest setup: the `gpu` marker, import paths, and a build of a
+fresh checkout."""
 import os
 import sys
 
@@ -10,6 +11,21 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line(
         "markers", "gpu: needs an MI355X (gfx950) GPU; parity against the CPU oracle")
+    _build_if_missing()
+
+
+def _build_if_missing():
+    """The tests load what is built.  Only when the HIP library, the CPU
+    oracle or the plain-C test driver has not been built at all (a fresh
+    checkout) is the build run first; an existing build is used as is, so
+    a changed source must be built again before testing."""
+    needed = [os.path.join(ROOT, "zero_sharded_optimizer_step_amd", "libzero_mi355x.so"),
+              os.path.join(ROOT, "oracle", "liboracle.so"),
+              os.path.join(ROOT, "tests", "c", "abi_gpu_check")]
+    if all(os.path.exists(p) for p in needed):
+        return
+    import __graft_entry__
+    __graft_entry__.build()
 
 
 def pytest_runtest_teardown(item, nextitem):
