@@ -892,6 +892,8 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    import __graft_entry__
+    __graft_entry__.ensure_built()             # only a fresh checkout is built here
     import zero_sharded_optimizer_step_amd as Z
     from zero_sharded_optimizer_step_amd import workloads as W
     Z.lib()

@@ -11,21 +11,8 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line(
         "markers", "gpu: needs an MI355X (gfx950) GPU; parity against the CPU oracle")
-    _build_if_missing()
-
-
-def _build_if_missing():
-    """The tests load what is built.  Only when the HIP library, the CPU
-    oracle or the plain-C test driver has not been built at all (a fresh
-    checkout) is the build run first; an existing build is used as is, so
-    a changed source must be built again before testing."""
-    needed = [os.path.join(ROOT, "zero_sharded_optimizer_step_amd", "libzero_mi355x.so"),
-              os.path.join(ROOT, "oracle", "liboracle.so"),
-              os.path.join(ROOT, "tests", "c", "abi_gpu_check")]
-    if all(os.path.exists(p) for p in needed):
-        return
     import __graft_entry__
-    __graft_entry__.build()
+    __graft_entry__.ensure_built()       # a fresh checkout is built first
 
 
 def pytest_runtest_teardown(item, nextitem):
