@@ -133,3 +133,19 @@ def test_encode_against_exact_rational():
         assert (np.isinf(h[i]) and r is None) or Fraction(float(h[i])) == r
         r = exact_rne(x, 7, -126, bfmax)
         assert (np.isinf(b[i]) and r is None) or Fraction(float(b[i])) == r
+
+
+def test_to_low_precision_follows_the_requested_format():
+    """The step's cast picks its encoder by the parameter format: fp16 codes
+    for FP16 and bfloat16 codes for BF16, each against torch's own
+    round-to-nearest-even cast, on values where the two formats differ
+    (bfloat16's range and fp16's finer fraction)."""
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.standard_normal(4096).astype(np.float32) * 100,
+                        np.float32([1e5, -3e38, 1.0009765625, 2.0 ** -20, 65520.0])])
+    f16 = oracle.to_low_precision(x, oracle.FP16)
+    bf16 = oracle.to_low_precision(x, oracle.BF16)
+    t = torch.from_numpy(x)
+    assert np.array_equal(f16, t.to(torch.float16).view(torch.int16).numpy().view(np.uint16))
+    assert np.array_equal(bf16, t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    assert not np.array_equal(f16, bf16)
