@@ -87,6 +87,8 @@ PY_MUTANTS = {
     "gather_one_past_the_end": ("return flat[lo:hi].copy()", "return flat[lo:hi + 1].copy()"),
     "flatten_one_element_late": ("flat[int(off):int(off) + t.size] = t",
                                  "flat[int(off) + 1:int(off) + 1 + t.size] = t"),
+    "cast_format_swapped": ("return f32_to_f16(p) if dtype == FP16 else f32_to_bf16(p)",
+                            "return f32_to_bf16(p) if dtype == FP16 else f32_to_f16(p)"),
 }
 
 
