@@ -928,14 +928,13 @@ def main():
                     "achieved": add_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": add_gbps / HBM_PEAK_GBPS, "traffic": measured_traffic("shard13b_accum")}
     else:
-        # counted on the in-place apply over separate arrays (one state set);
-        # the ping-pong and tiled variants are other kernel instantiations,
-        # whose counters were not taken
-        counted = args.state_buffers == 1 and args.state_layout == "separate"
+        # each state layout and state-set count runs its own instantiation
+        # of the kernel, counted under its own record
+        variant = "shard13b" + ("_tiled" if args.state_layout == "tiled" else "") + \
+            ("_pingpong" if args.state_buffers == 2 else "")
         roofline = {"bound": "hbm", "kernel": "apply_kernel (AdamW + cast)",
                     "achieved": app_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": app_gbps / HBM_PEAK_GBPS,
-                    "traffic": measured_traffic("shard13b") if counted else None}
+                    "frac": app_gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(variant)}
     out = {
         "metric": METRIC,
         "value": r["valid"] / (r["ms"] * 1e-3),

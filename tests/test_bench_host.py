@@ -39,15 +39,22 @@ def test_traffic_record_matches_the_built_library(path):
 
 def algorithmic_bytes(rec):
     """The bytes the roofline kernel must move per unit the record counts,
-    from the workloads' sizes."""
+    derived here from the workloads' sizes (not taken from the record)."""
     import zero_sharded_optimizer_step_amd as Z
     from zero_sharded_optimizer_step_amd import workloads as W
-    if "algorithmic_bytes_per_launch" in rec:
-        return rec["algorithmic_bytes_per_launch"]
     w = W.SHARD_13B_OF_8
-    if rec["workload"] == "shard13b":        # AdamW + cast: 16 B read, 14 B written
-        part = Z.zero_partition(w.numel, w.world_size, w.alignment)
-        return 30 * Z.zero_partition_valid_numel(part, 0)
+    part = Z.zero_partition(w.numel, w.world_size, w.alignment)
+    s = Z.zero_partition_valid_numel(part, 0)
+    if rec["workload"] in ("shard13b", "shard13b_tiled", "shard13b_pingpong",
+                           "shard13b_tiled_pingpong"):    # AdamW + cast: 16 B read, 14 B written
+        return 30 * s
+    if rec["workload"] == "shard13b_accum":  # adding pass: 8 bf16 replicas and the fp32 sum
+        # plus one 16-byte partial per reduce block: 1024 elements a block,
+        # the grid rounded up to a multiple of 2048 blocks
+        blocks = -(-(-(-s // 1024)) // 2048) * 2048
+        return (2 * w.world_size + 8) * s + 16 * blocks
+    if rec["workload"] == "shard13b_local":  # adding window pass over the rank's full gradient
+        return 10 * part.padded_numel
     if rec["workload"] == "zero3":           # every parameter read and written once
         return 4 * w.numel
     if rec["workload"] == "repartition":     # 3 fp32 arrays: read once, new padded written
