@@ -64,3 +64,24 @@ def algorithmic_bytes(rec):
         P = W.RAGGED_2000.numel
         return 8 * (2 * P + 2 * Z.zero_partition(P, 8, 128).padded_numel)
     raise AssertionError("no algorithmic figure for " + rec["workload"])
+
+
+def test_one_host_core_pins_and_restores_the_thread():
+    """The oracle's timing runs on one CPU of the thread's set; the set is
+    restored afterwards, also when the timed block raises."""
+    import threading
+    import bench
+    tid = threading.get_native_id()
+    before = os.sched_getaffinity(tid)
+    with bench.one_host_core():
+        inside = os.sched_getaffinity(tid)
+        rec = bench.cpu_record(10, 1.0, "sample", 100)
+    assert inside == {min(before)} and "pinned to CPU %d" % min(before) in rec["sample"]
+    assert "%d CPUs available" % len(before) in rec["sample"] and rec["cores"] == 1
+    assert os.sched_getaffinity(tid) == before
+    try:
+        with bench.one_host_core():
+            raise RuntimeError("inside")
+    except RuntimeError:
+        pass
+    assert os.sched_getaffinity(tid) == before
