@@ -51,3 +51,19 @@ def test_ring_place_examples():
     assert ring_place([(4, 8), (0, 3)], 1, 10) == 3           # wrapped: [3, 4) is free
     assert ring_place([(4, 8), (0, 3)], 2, 10) is None
     assert ring_place([(5, 5)], 3, 10) == 5                   # an empty bucket takes no room
+
+
+def test_layer_gatherer_refuses_bad_layouts_before_touching_the_device():
+    """The checks run before any stream exists: layers that do not cover
+    the flat parameter space, and a live bound below the largest bucket."""
+    import torch
+    import zero_sharded_optimizer_step_amd as Z
+    from zero_sharded_optimizer_step_amd.zero3 import LayerGatherer
+    part = Z.zero_partition(1000, 4, 8)
+    shards = [torch.zeros(part.shard_numel, dtype=torch.bfloat16) for _ in range(4)]
+    with pytest.raises(ValueError, match="cover"):
+        LayerGatherer(part, shards, [400, 500], 1000, 1000)
+    with pytest.raises(ValueError, match="largest bucket"):
+        LayerGatherer(part, shards, [600, 400], 1000, 999)     # one bucket of 1000
+    with pytest.raises(ValueError, match="largest bucket"):
+        LayerGatherer(part, shards, [600, 400], 100, 599)      # buckets of 600 and 400
