@@ -49,3 +49,21 @@ def test_hip_library_does_not_link_or_call_the_oracle():
     undefined = subprocess.run(["nm", "-D", "--undefined-only", lib], capture_output=True, text=True,
                                check=True).stdout
     assert "oracle" not in undefined
+
+
+def test_oracle_does_not_use_the_library():
+    """The other direction: the oracle's Python layer imports nothing of the
+    package, and its C library refers to none of the HIP library's symbols."""
+    tree = ast.parse(open(os.path.join(ROOT, "oracle", "__init__.py")).read())
+    for node in ast.walk(tree):
+        if isinstance(node, ast.Import):
+            assert all(not a.name.startswith("zero_sharded_optimizer_step_amd") for a in node.names)
+        elif isinstance(node, ast.ImportFrom):
+            assert not (node.module or "").startswith("zero_sharded_optimizer_step_amd")
+    import oracle
+    lib = oracle.build(force=False)
+    undefined = subprocess.run(["nm", "-D", "--undefined-only", lib], capture_output=True, text=True,
+                               check=True).stdout
+    assert "zero_" not in undefined
+    needed = subprocess.run(["readelf", "-d", lib], capture_output=True, text=True, check=True).stdout
+    assert "zero_mi355x" not in needed
